@@ -1,0 +1,122 @@
+"""Seeded synthetic workloads for the frame-wise GDN forward recurrence.
+
+This module only draws random numbers and fixes shapes: it holds none of the
+method's arithmetic, so both the oracle side and the HIP side of every test
+can take their inputs from it.
+
+Shapes follow the SANA-WM pages: a 60 s 720p clip is 961 latent frames
+("NVIDIA Apresenta SANA-WM ...", section "1. Atencao Linear Hibrida com Gated
+DeltaNet (GDN)"); a frame holds S spatial tokens of a latent grid (22 x 40 =
+880 for 720p-shaped inputs, 45 x 80 = 3600 for the stress shape) and each head
+carries a D x D state.  No dataset is used: Q, K, V are Gaussian, gamma and
+beta uniform, drawn per (tensor, head) so that any single head can be
+regenerated on its own.
+
+Draw recipe (fixed; changing it changes every stored expectation):
+  * one torch.Generator per (tensor, head), seeded with
+      seed * 1_000_003 + stream_id,
+    stream_id = tensor_index * B*H + b*H + h, tensor_index Q=0 K=1 V=2 gamma=3 beta=4;
+  * Q, K, V: fp32 ``randn`` of shape [T, S, D] times the tensor's std, then
+    rounded to nearest-even bf16 when the I/O dtype is bf16;
+  * gamma, beta: fp32 ``rand`` of shape [T], mapped affinely onto [lo, hi].
+CPU and GPU generators give different streams: a test draws on one device and
+hands the same values to both sides.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Iterable, Optional, Tuple
+
+import torch
+
+TENSORS = ("q", "k", "v", "gamma", "beta")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    S: int
+    D: int
+    dtype: str = "bf16"                 # I/O dtype of q, k, v, o: "bf16" or "f32"
+    gamma: Tuple[float, float] = (0.9, 1.0)
+    beta: Tuple[float, float] = (0.0, 1.0)
+    q_std: float = 1.0
+    k_std: float = 1.0
+    v_std: float = 1.0
+    beta_mode: str = "erase"
+    chunk: int = 0                      # >0: frames per gdn_frame_step call
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.T * self.S
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the benchmark suite.
+TINY = Workload("tiny-fp32 B1 H2 T8 S16 D16", 1, 2, 8, 16, 16, dtype="f32",
+                gamma=(0.8, 1.0), beta=(0.0, 1.0))
+SHORT = Workload("short-clip B1 H16 T81 S880 D64", 1, 16, 81, 880, 64,
+                 gamma=(0.9, 1.0), beta=(0.2, 1.0))
+MINUTE_720P = Workload("minute-720p B1 H20 T961 S880 D112", 1, 20, 961, 880, 112,
+                       gamma=(0.95, 1.0), beta=(0.1, 1.0))
+CHUNKED = SHORT.with_(name="chunked-rollout B1 H16 T81 S880 D64 chunk4", chunk=4)
+STRESS = Workload("stress B2 H20 T961 S3600 D128", 2, 20, 961, 3600, 128,
+                  gamma=(0.5, 1.0), beta=(1.0, 1.0), k_std=2.0)
+
+ALL = (TINY, SHORT, MINUTE_720P, CHUNKED, STRESS)
+
+
+def _gen(device, seed: int, stream_id: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1_000_003 + stream_id)
+    return g
+
+
+def head_tensors(w: Workload, b: int, h: int, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of one head: q, k, v [T, S, D] (I/O dtype), gamma, beta [T] fp32."""
+    BH = w.B * w.H
+    sid = lambda ti: ti * BH + b * w.H + h
+    out = {}
+    for ti, (name, std) in enumerate((("q", w.q_std), ("k", w.k_std), ("v", w.v_std))):
+        x = torch.randn((w.T, w.S, w.D), generator=_gen(device, seed, sid(ti)),
+                        device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        out[name] = x.to(w.torch_dtype)
+    for ti, name, (lo, hi) in ((3, "gamma", w.gamma), (4, "beta", w.beta)):
+        u = torch.rand((w.T,), generator=_gen(device, seed, sid(ti)), device=device,
+                       dtype=torch.float32)
+        out[name] = (u * (hi - lo) + lo) if hi != lo else torch.full_like(u, lo)
+    return out
+
+
+def generate(w: Workload, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """All heads: q, k, v [B, H, T, S, D]; gamma, beta [B, H, T] (fp32)."""
+    q = torch.empty((w.B, w.H, w.T, w.S, w.D), dtype=w.torch_dtype, device=device)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    gamma = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=device)
+    beta = torch.empty_like(gamma)
+    for b in range(w.B):
+        for h in range(w.H):
+            t = head_tensors(w, b, h, device, seed)
+            q[b, h], k[b, h], v[b, h] = t["q"], t["k"], t["v"]
+            gamma[b, h], beta[b, h] = t["gamma"], t["beta"]
+    return {"q": q, "k": k, "v": v, "gamma": gamma, "beta": beta}
+
+
+def to_numpy_io(x: torch.Tensor):
+    """Host copy in the oracle's input convention: float32, or uint16 bf16 bits."""
+    x = x.detach().to("cpu").contiguous()
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).numpy().view("uint16")
+    return x.numpy()

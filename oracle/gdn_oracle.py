@@ -1,0 +1,128 @@
+"""Python front end of the double-precision oracle (test infrastructure only).
+
+Only the tests, the package's smoke check and the CPU-baseline leg of the
+benchmark may import this module.  It loads ``liboracle_gdn.so`` built from
+``gdn_oracle.c`` with the host C compiler and never touches the HIP library.
+
+Arrays are numpy.  bf16 tensors travel as ``uint16`` bit patterns; fp32 as
+``float32``.  Layouts: q, k, v, o are [B, H, T, S, D]; gamma, beta [B, H, T];
+states [B, H, D, D] indexed [key][value].
+
+The recurrence itself is documented in ``gdn_oracle.c`` (source: the SANA-WM
+news article "NVIDIA Apresenta SANA-WM ...", section "1. Atencao Linear
+Hibrida com Gated DeltaNet (GDN)").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gdn_oracle.c")
+LIB = os.path.join(HERE, "liboracle_gdn.so")
+
+ERASE, WRITE = 0, 1
+_MODES = {"erase": ERASE, "write": WRITE, ERASE: ERASE, WRITE: WRITE}
+
+
+def build(out: str = LIB, mutant: int = 0, quiet: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math). Returns the path."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off",
+           f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True, capture_output=quiet)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_libs: dict = {}
+
+
+def load(path: str = LIB) -> ctypes.CDLL:
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
+        if path != LIB:
+            raise FileNotFoundError(path)
+        build(path)
+    lib = ctypes.CDLL(path)
+    lib.oracle_gdn_head.restype = ctypes.c_int
+    lib.oracle_gdn_head.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int]
+    _libs[path] = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def head(q, k, v, gamma, beta, state_in=None, beta_mode="erase", want_out=True,
+         want_norms=False, threads: int = 0, lib_path: str = LIB):
+    """One head: q, k, v [T, S, D] (float32 or uint16 bf16 bits), gamma/beta [T].
+
+    Returns (out [T,S,D] float64 or None, state_out [D,D] float64, norms [T] or None).
+    """
+    lib = load(lib_path)
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    if not (q.shape == k.shape == v.shape and q.ndim == 3):
+        raise ValueError("q, k, v must share shape [T, S, D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share dtype")
+    if q.dtype == np.float32:
+        io = 0
+    elif q.dtype == np.uint16:
+        io = 1
+    else:
+        raise TypeError("inputs must be float32 or uint16 (bf16 bit patterns)")
+    T, S, D = q.shape
+    g = np.ascontiguousarray(gamma, dtype=np.float32).reshape(T)
+    b = np.ascontiguousarray(beta, dtype=np.float32).reshape(T)
+    sin = None if state_in is None else np.ascontiguousarray(state_in, dtype=np.float64).reshape(D, D)
+    out = np.empty((T, S, D), np.float64) if want_out else None
+    sout = np.empty((D, D), np.float64)
+    norms = np.empty((T,), np.float64) if want_norms else None
+    rc = lib.oracle_gdn_head(T, S, D, io, _MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(g), _ptr(b), _ptr(sin), _ptr(out), _ptr(sout), _ptr(norms),
+                             int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gdn_head failed with code {rc}")
+    return out, sout, norms
+
+
+def forward(q, k, v, gamma, beta, state_in=None, beta_mode="erase", want_out=True,
+            want_norms=False, threads: int = 0, lib_path: str = LIB):
+    """All heads: q, k, v [B, H, T, S, D]; gamma/beta [B, H, T]; state_in [B, H, D, D] or None.
+
+    Returns (out [B,H,T,S,D] float64 or None, state_out [B,H,D,D], norms [B,H,T] or None).
+    """
+    B, H, T, S, D = q.shape
+    out = np.empty((B, H, T, S, D), np.float64) if want_out else None
+    sout = np.empty((B, H, D, D), np.float64)
+    norms = np.empty((B, H, T), np.float64) if want_norms else None
+    for bi in range(B):
+        for hi in range(H):
+            o, s, n = head(q[bi, hi], k[bi, hi], v[bi, hi], gamma[bi, hi], beta[bi, hi],
+                           None if state_in is None else state_in[bi, hi], beta_mode,
+                           want_out, want_norms, threads, lib_path)
+            if want_out:
+                out[bi, hi] = o
+            sout[bi, hi] = s
+            if want_norms:
+                norms[bi, hi] = n
+    return out, sout, norms
+
+
+def bf16_bits_to_f64(x: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
