@@ -1,0 +1,165 @@
+#!/usr/bin/env python3
+"""Benchmark of the frame-wise GDN forward path on one MI355X.
+
+One step = one gdn_frame_forward call over the whole minute-scale 720p-shaped
+workload (B1 H20 T961 S880 D112, bf16 I/O, fp32 state, ERASE mode), inputs
+already resident in HBM.  Prints ONE JSON line with tokens/s (B*H*T*S per
+second), the roofline of the dominant kernel, the whole-path roofline and the
+oracle's CPU rate on a bounded sample.
+
+Roofline bookkeeping (algorithmic bytes only; the per-frame state snapshots
+and the re-reads of keys by the column tiles are overhead, not algorithm):
+  whole path   8*D bytes per token-head (Q, K, V read; O written, bf16)
+  recurrence   4*D bytes per token-head (K, V read) + 8 per frame-head (gamma, beta)
+  readout      4*D bytes per token-head (Q read, O written) + 4 per frame-head if norms
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFS = 2500.0    # dense bf16 MFMA, TFLOP/s
+KERNEL_SRC = os.path.join(ROOT, "frame_wise_gated_gdn_amd", "csrc", "gdn_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_minute720p.json")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def pmc_traffic(kernel: str):
+    """HBM traffic per launch from a stored rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    if it was taken on the current kernel source; else None."""
+    try:
+        s = json.load(open(PMC_SUMMARY))
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    k = s.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, heads: int):
+    """Oracle (as it stands) on `heads` whole heads of the same workload."""
+    import numpy as np
+    from oracle import gdn_oracle
+    from frame_wise_gated_gdn_amd import workloads as wl
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    gdn_oracle.load()
+    tok = 0
+    t0 = time.perf_counter()
+    for h in range(heads):
+        q, k, v = (wl.to_numpy_io(inp[n][0, h]) for n in ("q", "k", "v"))
+        g = inp["gamma"][0, h].cpu().numpy()
+        b = inp["beta"][0, h].cpu().numpy()
+        gdn_oracle.head(q, k, v, g, b, beta_mode=w.beta_mode, want_out=True, threads=threads)
+        tok += w.T * w.S
+    dt = time.perf_counter() - t0
+    return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} whole head(s) (b=0, h=0..{heads - 1}) of {w.name}: {tok} tokens, "
+                      f"{dt:.1f} s wall, fp64, OpenMP {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=3, help="oracle heads timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (for rocprofv3 counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the path shards "
+              "by (batch, head) with no communication, so N GPUs would each run their own heads.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import frame_wise_gated_gdn_amd as gdn
+    from frame_wise_gated_gdn_amd import workloads as wl
+
+    w = wl.MINUTE_720P
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.generate(w, device=dev)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode)
+    ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["q"])
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    call = lambda timed: gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
+                                           beta_mode=w.beta_mode, out=out, state_out=st, workspace=ws,
+                                           time_kernels=timed)
+    for _ in range(args.warmup):
+        call(False)
+    torch.cuda.synchronize()
+    gdn.kernel_times(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    (ms_rec, ms_read), (n_rec, n_read) = gdn.kernel_times(reset=True)
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_step = dt * 1e3 / args.steps
+    tokens = w.tokens
+    value = tokens / (ms_step * 1e-3)
+    D, BH, T, S = w.D, w.B * w.H, w.T, w.S
+    per_launch_frames = T                       # the workspace holds all frames: one launch each
+    rec_bytes = BH * T * S * 4 * D + BH * T * 8
+    read_bytes = BH * T * S * 4 * D
+    avg_rec = ms_rec / max(n_rec, 1)
+    avg_read = ms_read / max(n_read, 1)
+    dom = "recurrence" if avg_rec >= avg_read else "readout"
+    dom_bytes, dom_ms = (rec_bytes, avg_rec) if dom == "recurrence" else (read_bytes, avg_read)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    path_bytes = BH * T * S * 8 * D
+    path_flops = BH * T * S * 6 * D * D
+    path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": "GDN frame-wise fwd tokens/s (B·H·T·S) at 1 GPU; % of HBM/MFMA roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q/K/V, uniform gamma/beta; no dataset)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "S": w.S, "D": w.D,
+                   "io_dtype": w.dtype, "state_dtype": "f32", "beta_mode": w.beta_mode,
+                   "calls_per_step": 1, "frames_per_launch": per_launch_frames},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": pmc_traffic(dom),
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
+        "path_roofline": {"bound": "hbm", "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes,
+                          "mfma_frac": path_flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
+        "kernels_ms_per_step": {"recurrence": avg_rec, "readout": avg_read},
+    }
+    if args.cpu_heads > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,13 @@
+"""MI355X-native frame-wise Gated DeltaNet (SANA-WM) forward path.
+
+The recurrence runs in hand-written gfx950 HIP kernels behind the C ABI of
+``libgdn.so`` (include/gdn.h); this package holds that library's sources, the
+ctypes binding and the seeded synthetic workloads.  PyTorch only provides
+device memory and streams.
+"""
+from .binding import (ABI_VERSION, BF16, ERASE, F32, WRITE, Desc, GDNError, check_args,  # noqa: F401
+                      frame_forward, frame_step, kernel_times, lib, make_desc, workspace_min_size,
+                      workspace_size)
+
+__all__ = ["frame_forward", "frame_step", "GDNError", "workspace_size", "workspace_min_size",
+           "kernel_times", "check_args", "make_desc", "lib"]

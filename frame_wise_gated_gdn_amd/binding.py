@@ -1,0 +1,195 @@
+"""Thin ctypes binding of ``libgdn.so`` (the C ABI declared in include/gdn.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the stream.
+If the library is missing the calls raise; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+
+ABI_VERSION = 1
+F32, BF16 = 0, 1
+ERASE, WRITE = 0, 1
+FLAG_TIME_KERNELS = 0x1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
+          5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_ABI", 8: "GDN_ERR_WORKSPACE",
+          9: "GDN_ERR_HIP"}
+# Every symbol include/gdn.h declares.
+EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
+           "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
+           "gdn_kernel_times")
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("beta_mode", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(hipcc, gfx950); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int
+    pdesc = ctypes.POINTER(Desc)
+    L.gdn_abi_version.restype = ctypes.c_int
+    L.gdn_status_string.restype = ctypes.c_char_p
+    L.gdn_status_string.argtypes = [ctypes.c_int]
+    L.gdn_last_error.restype = ctypes.c_char_p
+    L.gdn_workspace_size.restype = sz
+    L.gdn_workspace_size.argtypes = [pdesc]
+    L.gdn_workspace_min_size.restype = sz
+    L.gdn_workspace_min_size.argtypes = [pdesc]
+    L.gdn_check_args.restype = ctypes.c_int
+    L.gdn_check_args.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int]
+    for name in ("gdn_frame_forward", "gdn_frame_step"):
+        fn = getattr(L, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_kernel_times.restype = ctypes.c_int
+    L.gdn_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+    if L.gdn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libgdn.so ABI {L.gdn_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = L
+    return L
+
+
+def make_desc(B, H, T, S, D, io_dtype, beta_mode="erase", flags=0, abi_version=ABI_VERSION) -> Desc:
+    mode = {"erase": ERASE, "write": WRITE}.get(beta_mode, beta_mode)
+    dt = {"bf16": BF16, "f32": F32}.get(io_dtype, io_dtype)
+    return Desc(abi_version, B, H, T, S, D, dt, mode, flags)
+
+
+def _raise(status: int):
+    if status != 0:
+        raise GDNError(status, lib().gdn_last_error().decode())
+
+
+def workspace_size(desc: Desc) -> int:
+    return int(lib().gdn_workspace_size(ctypes.byref(desc)))
+
+
+def workspace_min_size(desc: Desc) -> int:
+    return int(lib().gdn_workspace_min_size(ctypes.byref(desc)))
+
+
+def check_args(desc: Desc, q=0, k=0, v=0, gamma=0, beta=0, state_in=0, o=0, state_out=0, norms=0,
+               workspace=0, workspace_bytes=0, state_in_required=False) -> int:
+    """Host-only argument check on raw addresses (no device access)."""
+    p = lambda x: ctypes.c_void_p(x or None)
+    return int(lib().gdn_check_args(ctypes.byref(desc), p(q), p(k), p(v), p(gamma), p(beta), p(state_in),
+                                    p(o), p(state_out), p(norms), p(workspace), workspace_bytes,
+                                    int(bool(state_in_required))))
+
+
+def kernel_times(reset: bool = True) -> Tuple[Tuple[float, float], Tuple[int, int]]:
+    """(ms_recurrence, ms_readout), (launches_recurrence, launches_readout) recorded so far."""
+    ms = (ctypes.c_double * 2)()
+    n = (ctypes.c_int64 * 2)()
+    _raise(lib().gdn_kernel_times(ms, n, int(reset)))
+    return (ms[0], ms[1]), (int(n[0]), int(n[1]))
+
+
+def _addr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out, norms, workspace,
+          stream, time_kernels: bool):
+    import torch
+    if q.dim() != 5:
+        raise ValueError("q, k, v must be [B, H, T, S, D]")
+    B, H, T, S, D = q.shape
+    if q.dtype == torch.bfloat16:
+        io = BF16
+    elif q.dtype == torch.float32:
+        io = F32
+    else:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("beta", beta)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    if gamma.shape != (B, H, T) or beta.shape != (B, H, T) or gamma.dtype != torch.float32 \
+            or beta.dtype != torch.float32:
+        raise ValueError("gamma and beta must be float32 [B, H, T]")
+    desc = make_desc(B, H, T, S, D, io, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = workspace_size(desc)
+        if n == 0:
+            _raise(lib().gdn_check_args(ctypes.byref(desc), *([None] * 10), 0, 0))
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = getattr(lib(), entry)
+    st = fn(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma), _addr(beta), _addr(state_in),
+            _addr(out), _addr(state_out), _addr(norms), _addr(workspace), workspace.numel(),
+            ctypes.c_void_p(stream))
+    _raise(st)
+    return out
+
+
+def frame_forward(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None, state_out=None,
+                  norms=None, want_state=True, want_norms=False, workspace=None, stream=None,
+                  time_kernels=False):
+    """Whole-sequence forward.  q, k, v [B,H,T,S,D] (bf16 or fp32), gamma/beta [B,H,T] fp32,
+    state [B,H,D,D] fp32 or None (zeros).  Returns (o, state_out, norms)."""
+    import torch
+    B, H, T, S, D = q.shape
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    if norms is None and want_norms:
+        norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    out = _call("gdn_frame_forward", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
+                workspace, stream, time_kernels)
+    return out, state_out, norms
+
+
+def frame_step(q, k, v, gamma, beta, state, beta_mode="erase", out=None, state_out=None, norms=None,
+               commit="new", workspace=None, stream=None, time_kernels=False):
+    """One chunk of a chunk-causal rollout; `state` [B,H,D,D] fp32 is required.
+
+    commit: "new" -> the updated state goes to a new tensor (or `state_out`);
+            "inplace" -> `state` is updated in place; "peek" -> the state is not written.
+    Returns (o, state_after, norms) where state_after is None for "peek".
+    """
+    import torch
+    if state is None:
+        raise ValueError("frame_step requires a state")
+    B, H, T, S, D = q.shape
+    if commit == "inplace":
+        state_out = state
+    elif commit == "peek":
+        state_out = None
+    elif state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    out = _call("gdn_frame_step", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
+                workspace, stream, time_kernels)
+    return out, state_out, norms

@@ -1,0 +1,281 @@
+// C ABI of the frame-wise GDN forward path: argument checks, workspace
+// planning, kernel dispatch on the caller's stream, status strings and the
+// optional per-kernel timing record.  See include/gdn.h for the contract.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxFramesPerLaunch = 1024;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  size_t bh, esz, nb;
+  size_t io_bytes, gb_bytes, state_bytes;
+  size_t carrier, snap_frame, norm_frame;
+};
+
+// Shapes already validated.
+Plan make_plan(const gdn_desc* d) {
+  Plan p;
+  p.bh = (size_t)d->B * (size_t)d->H;
+  p.esz = d->io_dtype == GDN_BF16 ? 2 : 4;
+  p.nb = (size_t)d->D / 16;
+  p.io_bytes = p.bh * (size_t)d->T * (size_t)d->S * (size_t)d->D * p.esz;
+  p.gb_bytes = p.bh * (size_t)d->T * 4;
+  p.state_bytes = p.bh * (size_t)d->D * (size_t)d->D * 4;
+  p.carrier = round_up(p.state_bytes);
+  p.snap_frame = p.bh * (size_t)d->D * (size_t)d->D * p.esz;
+  p.norm_frame = p.bh * p.nb * 4;
+  return p;
+}
+
+size_t ws_bytes_for(const Plan& p, size_t frames) {
+  return p.carrier + round_up(frames * p.snap_frame) + round_up(frames * p.norm_frame);
+}
+
+gdn_status check_desc(const gdn_desc* d) {
+  if (!d) return fail(GDN_ERR_NULL, "desc is NULL");
+  if (d->abi_version != GDN_ABI_VERSION)
+    return fail(GDN_ERR_ABI, "desc.abi_version %d != library ABI %d", d->abi_version, GDN_ABI_VERSION);
+  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "io_dtype %d is not GDN_F32 or GDN_BF16", d->io_dtype);
+  if (d->beta_mode != GDN_BETA_ERASE && d->beta_mode != GDN_BETA_WRITE)
+    return fail(GDN_ERR_DTYPE, "beta_mode %d is not GDN_BETA_ERASE or GDN_BETA_WRITE", d->beta_mode);
+  if (d->flags & ~GDN_FLAG_TIME_KERNELS) return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->S < 1 || d->D < 1)
+    return fail(GDN_ERR_SHAPE, "B=%d H=%d T=%d S=%d D=%d: every size must be >= 1", d->B, d->H, d->T, d->S, d->D);
+  if (d->D % 16 != 0 || d->D > 128)
+    return fail(GDN_ERR_UNSUPPORTED, "D=%d: supported head dims are 16, 32, ..., 128", d->D);
+  const long double per_head = (long double)d->T * d->S * d->D;
+  if (per_head >= 2147483648.0L)
+    return fail(GDN_ERR_SHAPE, "T*S*D = %.0Lf exceeds the per-head 32-bit limit", per_head);
+  const long double bh = (long double)d->B * d->H;
+  if (bh * d->T >= 2147483648.0L || bh * d->D * d->D >= 2147483648.0L * 8)
+    return fail(GDN_ERR_SHAPE, "B*H too large for these T and D");
+  if (bh * per_head * 4 >= (long double)SIZE_MAX / 4)
+    return fail(GDN_ERR_SHAPE, "tensor sizes overflow size_t");
+  return GDN_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool misaligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
+
+struct TimedLaunch {
+  hipEvent_t ev[3];
+};
+std::mutex g_time_mu;
+std::vector<TimedLaunch> g_timed;
+double g_time_ms[2] = {0.0, 0.0};
+int64_t g_time_n[2] = {0, 0};
+
+gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+               const float* beta, const float* state_in, void* o, float* state_out, float* norms,
+               void* workspace, size_t workspace_bytes, void* stream, int is_step) {
+  gdn_status st = gdn_check_args(d, q, k, v, gamma, beta, state_in, o, state_out, norms, workspace,
+                                 workspace_bytes, is_step);
+  if (st != GDN_OK) return st;
+  const Plan p = make_plan(d);
+  const bool bf16 = d->io_dtype == GDN_BF16;
+  const size_t per_frame = p.snap_frame + p.norm_frame;
+  size_t frames = 1;  // the minimum-size check guarantees that one frame fits
+  if (workspace_bytes > p.carrier + 2 * kAlign) frames = std::max<size_t>(1, (workspace_bytes - p.carrier - 2 * kAlign) / per_frame);
+  while (frames > 1 && ws_bytes_for(p, frames) > workspace_bytes) --frames;
+  if (frames > (size_t)d->T) frames = (size_t)d->T;
+  if (frames > (size_t)kMaxFramesPerLaunch) frames = kMaxFramesPerLaunch;
+
+  unsigned char* ws = (unsigned char*)workspace;
+  float* carrier = (float*)ws;
+  void* snap = ws + p.carrier;
+  float* norm_part = (float*)(ws + p.carrier + round_up(frames * p.snap_frame));
+
+  // The state travels between launches through state_out when the caller gave
+  // one (in-place per workgroup tile), else through the workspace carrier.
+  float* hand = state_out ? state_out : carrier;
+  const float kscale = (float)(1.0 / std::sqrt((double)d->D * (double)d->S));
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  hipStream_t s = (hipStream_t)stream;
+
+  for (int t0 = 0; t0 < d->T; t0 += (int)frames) {
+    const int tc = (int)std::min<size_t>(frames, (size_t)(d->T - t0));
+    const bool last = t0 + tc >= d->T;
+    gdn::RecurArgs ra;
+    ra.k = k; ra.v = v; ra.gamma = gamma; ra.beta = beta;
+    ra.state_src = (t0 == 0) ? state_in : hand;
+    ra.state_dst = last ? state_out : hand;
+    ra.snap = snap;
+    ra.norm_part = norms ? norm_part : nullptr;
+    ra.units = (int)(p.bh * p.nb);
+    ra.T = d->T; ra.S = d->S; ra.t0 = t0; ra.Tc = tc;
+    ra.beta_mode = d->beta_mode;
+    ra.kscale = kscale;
+    gdn::ReadoutArgs ro;
+    ro.q = q; ro.o = o; ro.snap = snap; ro.norm_part = ra.norm_part; ro.norms = norms;
+    ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
+
+    TimedLaunch tl;
+    if (timed) {
+      for (int i = 0; i < 3; ++i) {
+        hipError_t e = hipEventCreate(&tl.ev[i]);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+      }
+    }
+    hipError_t e = gdn::launch_chunk(d->D, bf16, ra, ro, s, timed ? tl.ev : nullptr);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1,
+                                     hipGetErrorString(e));
+    if (timed) {
+      std::lock_guard<std::mutex> lk(g_time_mu);
+      g_timed.push_back(tl);
+    }
+  }
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: a size is out of range";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown io_dtype or beta_mode";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is misaligned";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: forbidden buffer overlap";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: head dim or flags not supported";
+    case GDN_ERR_ABI: return "GDN_ERR_ABI: ABI version mismatch";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP runtime error";
+  }
+  return "unknown gdn_status";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+size_t gdn_workspace_min_size(const gdn_desc* d) {
+  if (check_desc(d) != GDN_OK) return 0;
+  return ws_bytes_for(make_plan(d), 1);
+}
+
+size_t gdn_workspace_size(const gdn_desc* d) {
+  if (check_desc(d) != GDN_OK) return 0;
+  const size_t frames = std::min<size_t>((size_t)d->T, (size_t)kMaxFramesPerLaunch);
+  return ws_bytes_for(make_plan(d), frames);
+}
+
+gdn_status gdn_check_args(const gdn_desc* d, const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta, const float* state_in,
+                          const void* o, const float* state_out, const float* state_norms,
+                          const void* workspace, size_t workspace_bytes, int state_in_required) {
+  g_last_error.clear();
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v) return fail(GDN_ERR_NULL, "q, k and v are required");
+  if (!gamma || !beta) return fail(GDN_ERR_NULL, "gamma and beta are required");
+  if (!o) return fail(GDN_ERR_NULL, "o is required");
+  if (state_in_required && !state_in) return fail(GDN_ERR_NULL, "gdn_frame_step requires state_in");
+  if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is required (gdn_workspace_size)");
+  const Plan p = make_plan(d);
+  if (workspace_bytes < ws_bytes_for(p, 1))
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, ws_bytes_for(p, 1));
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (misaligned(gamma, 4) || misaligned(beta, 4) || misaligned(state_in, 4) || misaligned(state_out, 4) ||
+      misaligned(state_norms, 4))
+    return fail(GDN_ERR_ALIGN, "gamma, beta, states and norms must be 4-byte aligned");
+  if (misaligned(workspace, kAlign)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  struct Buf { const void* p; size_t n; const char* name; };
+  const Buf ins[] = {{q, p.io_bytes, "q"}, {k, p.io_bytes, "k"}, {v, p.io_bytes, "v"},
+                     {gamma, p.gb_bytes, "gamma"}, {beta, p.gb_bytes, "beta"},
+                     {state_in, p.state_bytes, "state_in"}};
+  const Buf outs[] = {{o, p.io_bytes, "o"}, {state_out, p.state_bytes, "state_out"},
+                      {state_norms, p.gb_bytes, "state_norms"}, {workspace, workspace_bytes, "workspace"}};
+  for (const Buf& x : outs) {
+    if (!x.p) continue;
+    for (const Buf& y : ins) {
+      if (x.p == state_out && y.p == state_in && state_out == state_in) continue;  // in place
+      if (overlap(x.p, x.n, y.p, y.n)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
+    }
+    for (const Buf& y : outs)
+      if (&y != &x && y.p && overlap(x.p, x.n, y.p, y.n))
+        return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_frame_forward(const gdn_desc* d, const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* state_in,
+                             void* o, float* state_out, float* state_norms,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return run(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, workspace, workspace_bytes,
+             stream, 0);
+}
+
+gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta, const float* state_in,
+                          void* o, float* state_out, float* state_norms,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return run(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, workspace, workspace_bytes,
+             stream, 1);
+}
+
+gdn_status gdn_kernel_times(double ms_out[2], int64_t launches_out[2], int reset) {
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  gdn_status st = GDN_OK;
+  for (TimedLaunch& tl : g_timed) {
+    float a = 0.f, b = 0.f;
+    hipError_t e = hipEventSynchronize(tl.ev[2]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&a, tl.ev[0], tl.ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&b, tl.ev[1], tl.ev[2]);
+    if (e != hipSuccess) {
+      st = fail(GDN_ERR_HIP, "kernel timing: %s", hipGetErrorString(e));
+    } else {
+      g_time_ms[0] += a; g_time_ms[1] += b;
+      g_time_n[0] += 1; g_time_n[1] += 1;
+    }
+    for (int i = 0; i < 3; ++i) (void)hipEventDestroy(tl.ev[i]);
+  }
+  g_timed.clear();
+  if (ms_out) { ms_out[0] = g_time_ms[0]; ms_out[1] = g_time_ms[1]; }
+  if (launches_out) { launches_out[0] = g_time_n[0]; launches_out[1] = g_time_n[1]; }
+  if (reset) { g_time_ms[0] = g_time_ms[1] = 0.0; g_time_n[0] = g_time_n[1] = 0; }
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,494 @@
+// Frame-wise Gated DeltaNet forward: CDNA4 (gfx950) kernels.
+//
+// The recurrence (SANA-WM news article "NVIDIA Apresenta SANA-WM ...", section
+// "1. Atencao Linear Hibrida com Gated DeltaNet (GDN)"): per head a D x D state
+// M[key][value] is carried across frames; frame t of S tokens does
+//   Md = g_t M;  P = Kf Md;  R = V - b_t P (ERASE) or b_t (V - P) (WRITE);
+//   M = Md + Kf^T R;  O_t = Qf M,   Kf = ReLU(K)/sqrt(D*S), Qf = ReLU(Q).
+//
+// Work split (one GPU):
+//   * gdn_recur: one workgroup per (head, 16-wide value-column tile of M).
+//     Columns of M evolve independently (each column only meets the same
+//     column of V, R and O), so the tile's state lives in registers for the
+//     whole frame loop.  The 8 waves of the workgroup split the frame's tokens
+//     into 32-token chunks; per chunk a wave runs the prediction (MFMA with the
+//     bf16 copy of M as B operand), the residual in fp32, and the write
+//     Kf^T R (MFMA, the residual split into a bf16 hi+lo pair so that the
+//     write keeps ~16 bits).  The waves' partial writes are reduced through LDS
+//     in fixed order (deterministic), the owning wave updates its 16-key block
+//     of M in fp32, and the bf16 copy of the new M is published to LDS for the
+//     next frame and to a per-frame snapshot in HBM.
+//   * gdn_readout: O_t = Qf M_t for every frame in parallel from the snapshots
+//     (fully parallel, HBM-bound), plus the optional state norms.
+// Workgroups of one head are placed on the same XCD (workgroups are dealt to
+// the 8 XCDs round-robin by id), so the re-reads of a frame's keys by the
+// head's column tiles hit that XCD's L2.
+//
+// MFMA lane layouts used (gfx950, wave64; l = lane, g = l/16):
+//   v_mfma_f32_16x16x32_bf16: A lane holds row l%16, k = 8g..8g+7;
+//                             B lane holds col l%16, k = 8g..8g+7;
+//                             C lane holds col l%16, rows 4g..4g+3.
+//   v_mfma_f32_16x16x4_f32:   A row l%16, k = g; B col l%16, k = g; C as above.
+//   ds_read_b64_tr_b16: in each 16-lane group, lane j supplies the address of
+//   4 consecutive 16-bit values (row j/4, columns 4(j%4)..+3 of a 4 x 16 block);
+//   lane i receives column i (rows 0..3).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 8;          // waves per recurrence workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kReadWaves = 4;      // waves per readout workgroup
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ReLU on two packed bf16: a negative bf16 has its sign bit set, i.e. it is a
+// negative int16, so an int16 max with 0 zeroes it and keeps the rest.
+__device__ __forceinline__ uint32_t relu2(uint32_t x) {
+  i16x2 v = __builtin_bit_cast(i16x2, x);
+  i16x2 z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, z));
+}
+__device__ __forceinline__ u32x4 relu8(u32x4 x) {
+  return u32x4{relu2(x[0]), relu2(x[1]), relu2(x[2]), relu2(x[3])};
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 8-byte transposed LDS read (see header comment for the lane mapping).
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Wave-local LDS ordering: LDS operations of one wave complete in order; the
+// fence stops the compiler from moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Pack two floats into two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// XCD-aware unit for this workgroup: units are split into 8 contiguous ranges,
+// range x is served by the workgroups that land on XCD x (ids = x mod 8).
+__device__ __forceinline__ int xcd_unit(int units) {
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int start = (int)(((long long)x * units) >> 3);
+  const int end = (int)(((long long)(x + 1) * units) >> 3);
+  return (start + slot < end) ? start + slot : -1;
+}
+
+// ----------------------------------------------------------------------------
+// Recurrence kernel.
+// ----------------------------------------------------------------------------
+template <int D, bool BF16>
+struct RecurShape {
+  static constexpr int NB = D / 16;                      // key blocks == value tiles
+  static constexpr int NKC = BF16 ? (D + 31) / 32 : 0;   // bf16 k-chunks of 32 keys
+  static constexpr int TOK = BF16 ? 32 : 16;             // tokens per wave chunk
+  // per-wave staging of the chunk's ReLU(K) rows: row stride in elements
+  static constexpr int KS = BF16 ? (D + 8) : (D + 4);
+  static constexpr int MBS = BF16 ? (32 * ((D + 31) / 32) + 8) : (D + 4);  // mbT row stride
+  static constexpr int ESZ = BF16 ? 2 : 4;
+  static constexpr size_t kst_bytes = (size_t)kWaves * TOK * KS * ESZ;
+  static constexpr size_t vst_bytes = BF16 ? (size_t)kWaves * 32 * 16 * 2 : 0;
+  static constexpr size_t red_bytes = (size_t)kWaves * NB * 64 * 16;
+  static constexpr size_t mbt_bytes = (size_t)16 * MBS * ESZ;
+  static constexpr size_t lds_bytes = kst_bytes + vst_bytes + red_bytes + mbt_bytes + 64;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads, 1) void gdn_recur_kernel(RecurArgs a) {
+  using Sh = RecurShape<D, BF16>;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, TOK = Sh::TOK, KS = Sh::KS, MBS = Sh::MBS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* kst_base = smem;
+  uint16_t* vst_base = (uint16_t*)(smem + Sh::kst_bytes);
+  f32x4* red = (f32x4*)(smem + Sh::kst_bytes + Sh::vst_bytes);
+  unsigned char* mbt = smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes;
+  float* normp = (float*)(mbt + Sh::mbt_bytes);
+
+  const int unit = xcd_unit(a.units);
+  if (unit < 0) return;                       // whole workgroup leaves together
+  const int bh = unit / NB, jt = unit % NB, j0 = jt * 16;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), g = l >> 4, n = l & 15;
+  const int S = a.S, T = a.T;
+  const size_t head_off = (size_t)bh * T * S * D;     // element offset of this head
+  const float c = a.kscale;
+  const bool erase = a.beta_mode == 0;
+
+  // ---- initial state: wave w < NB owns key rows 16w..16w+15 of the tile (C layout)
+  f32x4 Mown = {0.f, 0.f, 0.f, 0.f};
+  if (w < NB && a.state_src) {
+    const float* src = a.state_src + (size_t)bh * D * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Mown[i] = src[(size_t)(16 * w + 4 * g + i) * D + j0 + n];
+  }
+  // zero mbT (including the k padding beyond D), then publish bf16(M0)
+  for (int x = tid; x < (int)(Sh::mbt_bytes / 4); x += kThreads) ((uint32_t*)mbt)[x] = 0u;
+  __syncthreads();
+  if (w < NB) {
+    if constexpr (BF16) {
+      uint16_t* mb = (uint16_t*)mbt;
+      u32x2 pk = {pack_bf16(Mown[0], Mown[1]), pack_bf16(Mown[2], Mown[3])};
+      *(u32x2*)(mb + n * MBS + 16 * w + 4 * g) = pk;
+    } else {
+      float* mb = (float*)mbt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mb[n * MBS + 16 * w + 4 * g + i] = Mown[i];
+    }
+  }
+  __syncthreads();
+
+  // B operand of the prediction: value column n, keys of chunk kc (bf16) /
+  // keys g*(D/4)+kc (fp32) -- loaded from mbT after every frame.
+  u32x4 MB[BF16 ? NKC : 1];
+  float MBf[BF16 ? 1 : D / 4];
+  auto load_mb = [&]() {
+    if constexpr (BF16) {
+      const uint16_t* mb = (const uint16_t*)mbt;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) MB[kc] = *(const u32x4*)(mb + n * MBS + 32 * kc + 8 * g);
+    } else {
+      const float* mb = (const float*)mbt;
+#pragma unroll
+      for (int kc = 0; kc < D / 4; ++kc) MBf[kc] = mb[n * MBS + g * (D / 4) + kc];
+    }
+  };
+  load_mb();
+
+  const int nchunks = (S + TOK - 1) / TOK;
+  const uint16_t* kb16 = (const uint16_t*)a.k + head_off;
+  const uint16_t* vb16 = (const uint16_t*)a.v + head_off;
+  const float* kf32 = (const float*)a.k + head_off;
+  const float* vf32 = (const float*)a.v + head_off;
+
+  for (int tl = 0; tl < a.Tc; ++tl) {
+    const int t = a.t0 + tl;
+    const float gam = a.gamma[(size_t)bh * T + t];
+    const float bet = a.beta[(size_t)bh * T + t];
+    const float s_pred = bet * c * gam;        // R = av*V - s_pred * (phi(K) bf16(M))
+    const float av = erase ? 1.0f : bet;
+    const size_t fo = (size_t)t * S * D;       // frame offset inside the head
+
+    f32x4 Wacc[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) Wacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ch = w; ch < nchunks; ch += kWaves) {
+      const int tb = ch * TOK;
+      if constexpr (BF16) {
+        uint16_t* kst = (uint16_t*)kst_base + (size_t)w * TOK * KS;
+        uint16_t* vst = vst_base + w * 32 * 16;
+        // -- loads: ReLU(K) rows as prediction A operands, V tile rows
+        u32x4 KA[2][NKC];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int tok = tb + 16 * r + n;
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            const int key = 32 * kc + 8 * g;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (tok < S && key < D) x = *(const u32x4*)(kb16 + fo + (size_t)tok * D + key);
+            KA[r][kc] = relu8(x);
+          }
+        }
+        {
+          const int tok = tb + (l >> 1);
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (tok < S) x = *(const u32x4*)(vb16 + fo + (size_t)tok * D + j0 + 8 * (l & 1));
+          *(u32x4*)(vst + (l >> 1) * 16 + 8 * (l & 1)) = x;
+        }
+        // -- stage ReLU(K) for the transposed reads of the write
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            const int key = 32 * kc + 8 * g;
+            if (key < D) *(u32x4*)(kst + (16 * r + n) * KS + key) = KA[r][kc];
+          }
+        // -- prediction P = phi(K) bf16(M) for the two 16-token row tiles
+        f32x4 P[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          P[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) P[r] = mfma_bf16(KA[r][kc], MB[kc], P[r]);
+        }
+        wave_lds_sync();
+        // -- V in the C layout (value column n, tokens 4g..4g+3 of each row tile)
+        u32x4 RBhi, RBlo;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const u32x2 vv = lds_tr16(vst + (16 * r + 4 * g + (n >> 2)) * 16 + 4 * (n & 3));
+          float R[4];
+          R[0] = av * bf16_lo_f32(vv[0]) - s_pred * P[r][0];
+          R[1] = av * bf16_hi_f32(vv[0]) - s_pred * P[r][1];
+          R[2] = av * bf16_lo_f32(vv[1]) - s_pred * P[r][2];
+          R[3] = av * bf16_hi_f32(vv[1]) - s_pred * P[r][3];
+          const uint32_t h01 = pack_bf16(R[0], R[1]), h23 = pack_bf16(R[2], R[3]);
+          const uint32_t l01 = pack_bf16(R[0] - bf16_lo_f32(h01), R[1] - bf16_hi_f32(h01));
+          const uint32_t l23 = pack_bf16(R[2] - bf16_lo_f32(h23), R[3] - bf16_hi_f32(h23));
+          RBhi[2 * r] = h01; RBhi[2 * r + 1] = h23;
+          RBlo[2 * r] = l01; RBlo[2 * r + 1] = l23;
+        }
+        // -- write: Wacc[kb] += phi(K)^T R over the chunk's 32 tokens
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          const uint16_t* p0 = kst + (4 * g + (n >> 2)) * KS + 16 * kb + 4 * (n & 3);
+          const u32x2 a0 = lds_tr16(p0);
+          const u32x2 a1 = lds_tr16(p0 + 16 * KS);
+          const u32x4 A = {a0[0], a0[1], a1[0], a1[1]};
+          Wacc[kb] = mfma_bf16(A, RBhi, Wacc[kb]);
+          Wacc[kb] = mfma_bf16(A, RBlo, Wacc[kb]);
+        }
+        wave_lds_sync();
+      } else {
+        float* kst = (float*)kst_base + (size_t)w * TOK * KS;
+        // -- loads: ReLU(K) rows, lane (token n, keys g*(D/4) .. +D/4-1)
+        const int tok = tb + n;
+        float KAf[D / 4];
+#pragma unroll
+        for (int kc = 0; kc < D / 4; ++kc) {
+          const float x = (tok < S) ? kf32[fo + (size_t)tok * D + g * (D / 4) + kc] : 0.f;
+          KAf[kc] = x > 0.f ? x : 0.f;
+        }
+#pragma unroll
+        for (int kc = 0; kc < D / 4; ++kc) kst[n * KS + g * (D / 4) + kc] = KAf[kc];
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < D / 4; ++kc) P = mfma_f32(KAf[kc], MBf[kc], P);
+        wave_lds_sync();
+        float R[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = tb + 4 * g + i;
+          const float vv = (tk < S) ? vf32[fo + (size_t)tk * D + j0 + n] : 0.f;
+          R[i] = av * vv - s_pred * P[i];
+        }
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Wacc[kb] = mfma_f32(kst[(4 * g + i) * KS + 16 * kb + n], R[i], Wacc[kb]);
+        wave_lds_sync();
+      }
+    }
+
+    // ---- reduce the waves' partial writes (fixed order), update the owned block
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) red[(w * NB + kb) * 64 + l] = Wacc[kb];
+    __syncthreads();
+    if (w < NB) {
+      f32x4 s = red[w * 64 + l];
+      for (int ww = 1; ww < kWaves; ++ww) {
+        const f32x4 x = red[(ww * NB + w) * 64 + l];
+        s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Mown[i] = gam * Mown[i] + c * s[i];
+      // publish bf16(M) / fp32 M to mbT and to the frame snapshot (transposed:
+      // row = value column, contiguous keys)
+      const size_t snap_off = ((size_t)bh * a.Tc + tl) * D * D + (size_t)(j0 + n) * D + 16 * w + 4 * g;
+      if constexpr (BF16) {
+        const u32x2 pk = {pack_bf16(Mown[0], Mown[1]), pack_bf16(Mown[2], Mown[3])};
+        *(u32x2*)((uint16_t*)mbt + n * MBS + 16 * w + 4 * g) = pk;
+        *(u32x2*)((uint16_t*)a.snap + snap_off) = pk;
+      } else {
+        float* mb = (float*)mbt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mb[n * MBS + 16 * w + 4 * g + i] = Mown[i];
+        *(f32x4*)((float*)a.snap + snap_off) = Mown;
+      }
+      if (a.norm_part) {
+        float sq = Mown[0] * Mown[0] + Mown[1] * Mown[1] + Mown[2] * Mown[2] + Mown[3] * Mown[3];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+        if (l == 0) normp[w] = sq;
+      }
+    }
+    __syncthreads();
+    load_mb();
+    if (a.norm_part && tid == 0) {
+      float sq = 0.f;
+      for (int kb = 0; kb < NB; ++kb) sq += normp[kb];
+      a.norm_part[((size_t)bh * a.Tc + tl) * NB + jt] = sq;
+    }
+  }
+
+  if (w < NB && a.state_dst) {
+    float* dst = a.state_dst + (size_t)bh * D * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(size_t)(16 * w + 4 * g + i) * D + j0 + n] = Mown[i];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Readout kernel: O_t = Qf M_t, computed as O^T = M^T Qf^T so that the Q rows
+// are natural B operands (16 contiguous bytes per lane) and each lane stores
+// 4 consecutive output columns of one token.
+// ----------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kReadWaves * 64) void gdn_readout_kernel(ReadoutArgs a) {
+  constexpr int NB = D / 16, NKC = (D + 31) / 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int frame = blockIdx.x;                    // over BH * Tc
+  const int bh = frame / a.Tc, tl = frame % a.Tc, t = a.t0 + tl;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), g = l >> 4, n = l & 15;
+  const int S = a.S, T = a.T;
+  const size_t fo = ((size_t)bh * T + t) * S * D;
+  const size_t so = ((size_t)bh * a.Tc + tl) * D * D;
+  const int ntile = (S + 15) / 16;
+
+  if (a.norms && tid == 0) {
+    float sq = 0.f;
+    for (int j = 0; j < NB; ++j) sq += a.norm_part[((size_t)bh * a.Tc + tl) * NB + j];
+    a.norms[(size_t)bh * T + t] = sqrtf(sq);
+  }
+
+  if constexpr (BF16) {
+    const uint16_t* snap = (const uint16_t*)a.snap + so;
+    const uint16_t* q = (const uint16_t*)a.q + fo;
+    uint16_t* o = (uint16_t*)a.o + fo;
+    // A operands: M^T rows (value column 16jb + n), keys 32kc + 8g .. +7
+    u32x4 A[NB][NKC];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int key = 32 * kc + 8 * g;
+        A[jb][kc] = (key < D) ? *(const u32x4*)(snap + (size_t)(16 * jb + n) * D + key) : u32x4{0u, 0u, 0u, 0u};
+      }
+    for (int tile = w; tile < ntile; tile += kReadWaves) {
+      const int tok = tile * 16 + n;
+      u32x4 B[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int key = 32 * kc + 8 * g;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (tok < S && key < D) x = *(const u32x4*)(q + (size_t)tok * D + key);
+        B[kc] = relu8(x);
+      }
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) acc = mfma_bf16(A[jb][kc], B[kc], acc);
+        if (tok < S) {
+          const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+          *(u32x2*)(o + (size_t)tok * D + 16 * jb + 4 * g) = pk;
+        }
+      }
+    }
+  } else {
+    // fp32: stage M^T in LDS; k index of MFMA step kc on lane group g is key g*(D/4)+kc
+    float* mt = (float*)smem;                        // [D][D + 1]
+    const float* snap = (const float*)a.snap + so;
+    for (int x = tid; x < D * D; x += kReadWaves * 64) mt[(x / D) * (D + 1) + (x % D)] = snap[x];
+    __syncthreads();
+    const float* q = (const float*)a.q + fo;
+    float* o = (float*)a.o + fo;
+    for (int tile = w; tile < ntile; tile += kReadWaves) {
+      const int tok = tile * 16 + n;
+      float B[D / 4];
+#pragma unroll
+      for (int kc = 0; kc < D / 4; ++kc) {
+        const float x = (tok < S) ? q[(size_t)tok * D + g * (D / 4) + kc] : 0.f;
+        B[kc] = x > 0.f ? x : 0.f;
+      }
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < D / 4; ++kc) acc = mfma_f32(mt[(16 * jb + n) * (D + 1) + g * (D / 4) + kc], B[kc], acc);
+        if (tok < S) *(f32x4*)(o + (size_t)tok * D + 16 * jb + 4 * g) = acc;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Launchers.
+// ----------------------------------------------------------------------------
+template <int D, bool BF16>
+static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStream_t stream,
+                              hipEvent_t* ev) {
+  using Sh = RecurShape<D, BF16>;
+  static bool attr_set = false;   // benign race: every setter writes the same value
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gdn_recur_kernel<D, BF16>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+    if (e != hipSuccess) return e;
+    if (!BF16) {
+      e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
+      if (e != hipSuccess) return e;
+    }
+    attr_set = true;
+  }
+  const int grid = 8 * ((ra.units + 7) / 8);
+  if (ev) { hipError_t e = hipEventRecord(ev[0], stream); if (e != hipSuccess) return e; }
+  hipLaunchKernelGGL((gdn_recur_kernel<D, BF16>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev) { e = hipEventRecord(ev[1], stream); if (e != hipSuccess) return e; }
+  const size_t rlds = BF16 ? 0 : (size_t)D * (D + 1) * 4;
+  hipLaunchKernelGGL((gdn_readout_kernel<D, BF16>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64), rlds, stream, ro);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev) { e = hipEventRecord(ev[2], stream); if (e != hipSuccess) return e; }
+  return hipSuccess;
+}
+
+hipError_t launch_chunk(int D, bool bf16, const RecurArgs& ra, const ReadoutArgs& ro,
+                        hipStream_t stream, hipEvent_t* ev) {
+#define GDN_CASE(DD)                                                          \
+  case DD:                                                                    \
+    return bf16 ? launch_pair<DD, true>(ra, ro, stream, ev)                   \
+                : launch_pair<DD, false>(ra, ro, stream, ev);
+  switch (D) {
+    GDN_CASE(16) GDN_CASE(32) GDN_CASE(48) GDN_CASE(64)
+    GDN_CASE(80) GDN_CASE(96) GDN_CASE(112) GDN_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef GDN_CASE
+}
+
+size_t recur_lds_bytes(int D, bool bf16) {
+#define GDN_LDS(DD) case DD: return bf16 ? RecurShape<DD, true>::lds_bytes : RecurShape<DD, false>::lds_bytes;
+  switch (D) {
+    GDN_LDS(16) GDN_LDS(32) GDN_LDS(48) GDN_LDS(64)
+    GDN_LDS(80) GDN_LDS(96) GDN_LDS(112) GDN_LDS(128)
+    default: return 0;
+  }
+#undef GDN_LDS
+}
+
+}  // namespace gdn

@@ -1,0 +1,163 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) frame-wise Gated DeltaNet forward path.
+ *
+ * What is computed.  SANA-WM's frame-wise GDN ("NVIDIA Apresenta SANA-WM ...",
+ * acheiumaia.com.br, section "1. Atencao Linear Hibrida com Gated DeltaNet
+ * (GDN)"; also the hybrid GDN + softmax design named in the abstract of
+ * "SANA-WM: Efficient Minute-Scale World Modeling with Hybrid Linear Diffusion
+ * Transformer"): every head carries a constant D x D state M[key][value] across
+ * latent frames; one recurrent step consumes a whole frame of S tokens:
+ *
+ *   Qf = ReLU(Q_t),  Kf = ReLU(K_t) / sqrt(D*S)
+ *   Md = gamma_t * M                                  (decay gate)
+ *   R  = V_t - beta_t * Kf Md        (ERASE)          (delta-rule residual)
+ *   R  = beta_t * (V_t - Kf Md)      (WRITE)
+ *   M  = Md + Kf^T R                                  (write)
+ *   O_t = Qf M                                        (readout, post-update)
+ *
+ * ERASE with beta = 0 and gamma = 1 is SANA-Video's cumulative ReLU linear
+ * attention (the block KV-cache of the talk "SANA-Video: Efficient Video
+ * Generation with Block Linear Diffusion Transformer"); WRITE with S = 1 is
+ * the token-wise gated delta rule.  gamma and beta are already activated
+ * fp32 scalars, one per (batch, head, frame).
+ *
+ * Layouts (all row-major, innermost last; every pointer is a DEVICE pointer):
+ *   q, k, v, o     [B][H][T][S][D]  io_dtype (bf16 or fp32)
+ *   gamma, beta    [B][H][T]        fp32
+ *   state_in/out   [B][H][D][D]     fp32, indexed [key][value]
+ *   state_norms    [B][H][T]        fp32, Frobenius norm of the post-update state
+ *
+ * Conventions.
+ *   - Ownership: the caller owns every buffer.  The library never allocates
+ *     device memory; scratch space comes in through `workspace`.
+ *   - Streams: every call only enqueues work on `stream` (a hipStream_t;
+ *     NULL = the default stream) and returns without synchronising.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Errors: arguments are checked on the host before anything is launched;
+ *     a failing check returns a status and launches nothing.  The library
+ *     never aborts.  gdn_last_error() gives a per-thread message.
+ *   - Aliasing: o must not overlap q, k, v, gamma, beta, the states or the
+ *     workspace.  state_out may equal state_in exactly (in-place update) but
+ *     may not partially overlap it.
+ *   - Alignment: q, k, v, o 16-byte aligned; gamma, beta, states, norms 4-byte
+ *     aligned; workspace 256-byte aligned.
+ *   - Shapes: B, H, T, S >= 1; D in {16, 32, 48, ..., 128}; the element counts
+ *     must fit the kernels' 32-bit per-head indexing (T*S*D < 2^31).
+ *   - Determinism: results do not depend on the workspace size or on how the
+ *     frames are split across calls; the same inputs give the same bits.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_beta_mode {
+  GDN_BETA_ERASE = 0, /* M = gM + Kf^T (V - b Kf gM): beta scales the correction */
+  GDN_BETA_WRITE = 1  /* M = gM + b Kf^T (V - Kf gM): beta scales the written residual */
+} gdn_beta_mode;
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* B, H, T or S out of range, or sizes overflow */
+  GDN_ERR_DTYPE = 3,       /* io_dtype or beta_mode not one of the enums */
+  GDN_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  GDN_ERR_ALIAS = 5,       /* forbidden overlap between buffers */
+  GDN_ERR_UNSUPPORTED = 6, /* D not in {16, 32, ..., 128}, or unknown flags */
+  GDN_ERR_ABI = 7,         /* desc->abi_version != GDN_ABI_VERSION */
+  GDN_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than one frame needs */
+  GDN_ERR_HIP = 9          /* a HIP runtime call failed (message in gdn_last_error) */
+} gdn_status;
+
+/* Record device time per kernel on `stream` (read back with gdn_kernel_times). */
+#define GDN_FLAG_TIME_KERNELS 0x1u
+
+typedef struct gdn_desc {
+  int32_t abi_version; /* GDN_ABI_VERSION */
+  int32_t B, H, T, S, D;
+  int32_t io_dtype;    /* gdn_dtype */
+  int32_t beta_mode;   /* gdn_beta_mode */
+  uint32_t flags;      /* GDN_FLAG_* */
+} gdn_desc;
+
+/* ABI version the library was built with. */
+int gdn_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* gdn_status_string(gdn_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+/*
+ * Workspace bytes the library would like for `d` (all T frames staged at once,
+ * capped at a few hundred frames); 0 if `d` is invalid.  Any workspace of at
+ * least gdn_workspace_min_size(d) bytes works: a smaller one makes the library
+ * process the frames in more pieces, with bitwise the same results.
+ */
+size_t gdn_workspace_size(const gdn_desc* d);
+size_t gdn_workspace_min_size(const gdn_desc* d);
+
+/*
+ * Host-only argument check shared by the two entry points; touches no device
+ * and can run where there is no GPU.  `state_in_required` is 1 for
+ * gdn_frame_step.  Returns GDN_OK or the first error found.
+ */
+gdn_status gdn_check_args(const gdn_desc* d, const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta, const float* state_in,
+                          const void* o, const float* state_out, const float* state_norms,
+                          const void* workspace, size_t workspace_bytes,
+                          int state_in_required);
+
+/*
+ * Whole-sequence forward (the offline / bidirectional-generation use of the
+ * article's three single-GPU variants, and any call that owns all T frames).
+ *   state_in     [B][H][D][D] or NULL for a zero initial state
+ *   state_out    [B][H][D][D] or NULL (final state not needed)
+ *   state_norms  [B][H][T] or NULL
+ *   workspace    device scratch of workspace_bytes >= gdn_workspace_min_size(d)
+ * Enqueues the work on `stream`; returns GDN_OK or an error status.
+ */
+gdn_status gdn_frame_forward(const gdn_desc* d, const void* q, const void* k, const void* v,
+                             const float* gamma, const float* beta, const float* state_in,
+                             void* o, float* state_out, float* state_norms,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One chunk of a chunk-causal streaming rollout (the article's chunk-causal
+ * autoregressive variant; the cached-state hand-off of SANA-Video's block
+ * KV cache): T = frames in this chunk (>= 1).  state_in is REQUIRED; state_out
+ * may be NULL (read the cached state without committing it, e.g. for every
+ * denoising step of a chunk) or equal to state_in (commit in place).
+ * Running the frames of a sequence through consecutive gdn_frame_step calls,
+ * the state handed from one to the next, gives bitwise the outputs and final
+ * state of one gdn_frame_forward call over the whole sequence.
+ */
+gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta, const float* state_in,
+                          void* o, float* state_out, float* state_norms,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Device time of the kernels launched by calls that set GDN_FLAG_TIME_KERNELS
+ * since the last reset: per kernel kind (0 = recurrence, 1 = readout) the total
+ * milliseconds and the number of launches.  Synchronises with the recorded
+ * events.  `reset` != 0 clears the record after reading.  Returns GDN_OK or
+ * GDN_ERR_HIP.
+ */
+gdn_status gdn_kernel_times(double ms_out[2], int64_t launches_out[2], int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

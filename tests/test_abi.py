@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/gdn.h declares, and rejects bad arguments on the host before any
+device work (addresses below are plain integers; nothing is dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import frame_wise_gated_gdn_amd as g
+    from frame_wise_gated_gdn_amd import build
+    if build.stale():
+        build.build()
+    g.lib()
+    return g
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(__import__("frame_wise_gated_gdn_amd").binding.EXPORTS)
+
+
+def test_exports_every_declared_symbol(gdn):
+    L = gdn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.gdn_abi_version() == 1
+
+
+def test_status_strings(gdn):
+    L = gdn.lib()
+    for s in range(10):
+        assert L.gdn_status_string(s).decode().startswith(gdn.binding.STATUS[s])
+    assert b"unknown" in L.gdn_status_string(99)
+
+
+BASE = 1 << 40           # fake, well-aligned, non-overlapping device addresses
+SPAN = 1 << 36
+
+
+def addrs(n=11):
+    return [BASE + i * SPAN for i in range(n)]
+
+
+def args_ok(gdn, d):
+    q, k, v, ga, be, si, o, so, nm, ws, _ = addrs()
+    return dict(q=q, k=k, v=v, gamma=ga, beta=be, state_in=si, o=o, state_out=so, norms=nm,
+                workspace=ws, workspace_bytes=gdn.workspace_size(d))
+
+
+def test_valid_arguments_pass(gdn):
+    for dt in ("bf16", "f32"):
+        for D in range(16, 129, 16):
+            d = gdn.make_desc(2, 3, 5, 17, D, dt)
+            assert gdn.check_args(d, **args_ok(gdn, d)) == 0, gdn.lib().gdn_last_error()
+
+
+def test_abi_and_enum_errors(gdn):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16", abi_version=2)
+    assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 7
+    d = gdn.make_desc(1, 2, 3, 16, 16, 5)
+    assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 3
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16", beta_mode=3)
+    assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 3
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16", flags=0x80)
+    assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 6
+    assert gdn.lib().gdn_check_args(None, *([None] * 10), 0, 0) == 1
+
+
+@pytest.mark.parametrize("shape,code", [((0, 1, 1, 1, 16), 2), ((1, 0, 1, 1, 16), 2), ((1, 1, 0, 1, 16), 2),
+                                        ((1, 1, 1, 0, 16), 2), ((1, 1, 1, 1, 0), 2), ((1, 1, 1, 1, 8), 6),
+                                        ((1, 1, 1, 1, 144), 6), ((1, 1, 1, 1, 120), 6),
+                                        ((1, 1, 100000, 100000, 128), 2)])
+def test_shape_errors(gdn, shape, code):
+    d = gdn.make_desc(*shape, "bf16")
+    good = gdn.make_desc(1, 1, 1, 1, 16, "bf16")
+    assert gdn.check_args(d, **args_ok(gdn, good)) == code
+    assert gdn.workspace_size(d) == 0
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "gamma", "beta", "o"])
+def test_null_errors(gdn, field):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    a = args_ok(gdn, d)
+    a[field] = 0
+    assert gdn.check_args(d, **a) == 1
+
+
+def test_step_requires_state_and_optional_outputs(gdn):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    a = args_ok(gdn, d)
+    a["state_in"] = 0
+    assert gdn.check_args(d, **a) == 0
+    assert gdn.check_args(d, **a, state_in_required=True) == 1
+    a = args_ok(gdn, d)
+    a["state_out"] = 0
+    a["norms"] = 0
+    assert gdn.check_args(d, **a, state_in_required=True) == 0
+
+
+def test_workspace_errors(gdn):
+    d = gdn.make_desc(1, 2, 30, 16, 32, "bf16")
+    a = args_ok(gdn, d)
+    a["workspace"] = 0
+    assert gdn.check_args(d, **a) == 8
+    a = args_ok(gdn, d)
+    a["workspace_bytes"] = gdn.workspace_min_size(d) - 1
+    assert gdn.check_args(d, **a) == 8
+    a["workspace_bytes"] = gdn.workspace_min_size(d)
+    assert gdn.check_args(d, **a) == 0
+    assert gdn.workspace_min_size(d) < gdn.workspace_size(d)
+
+
+@pytest.mark.parametrize("field,off,code", [("q", 2, 4), ("o", 8, 4), ("gamma", 2, 4), ("state_in", 1, 4),
+                                            ("norms", 2, 4), ("workspace", 64, 4)])
+def test_alignment_errors(gdn, field, off, code):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    a = args_ok(gdn, d)
+    a[field] += off
+    assert gdn.check_args(d, **a) == code
+
+
+def test_alias_errors(gdn):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    a = args_ok(gdn, d)
+    a["o"] = a["q"] + 64                       # o overlaps q
+    assert gdn.check_args(d, **a) == 5
+    a = args_ok(gdn, d)
+    a["state_out"] = a["state_in"]             # exact in-place state update is allowed
+    assert gdn.check_args(d, **a) == 0
+    a["state_out"] = a["state_in"] + 16        # partial overlap is not
+    assert gdn.check_args(d, **a) == 5
+    a = args_ok(gdn, d)
+    a["norms"] = a["v"]
+    assert gdn.check_args(d, **a) == 5
+    a = args_ok(gdn, d)
+    a["workspace"] = a["o"]
+    assert gdn.check_args(d, **a) == 5
+    a = args_ok(gdn, d)
+    a["k"] = a["q"]                            # inputs may alias each other
+    assert gdn.check_args(d, **a) == 0
+
+
+def test_last_error_message(gdn):
+    d = gdn.make_desc(1, 2, 3, 16, 24, "bf16")
+    assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 6
+    assert b"D=24" in gdn.lib().gdn_last_error()
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    assert gdn.check_args(d, **args_ok(gdn, d)) == 0
+    assert gdn.lib().gdn_last_error() == b""
+
+
+def test_workspace_sizes_grow_with_frames_until_cap(gdn):
+    sizes = [gdn.workspace_size(gdn.make_desc(1, 4, T, 64, 64, "bf16")) for T in (1, 10, 100, 1024, 4000)]
+    assert sizes == sorted(sizes) and sizes[-1] == sizes[-2]
+    mins = {gdn.workspace_min_size(gdn.make_desc(1, 4, T, 64, 64, "bf16")) for T in (1, 10, 100, 4000)}
+    assert len(mins) == 1        # the minimum does not depend on T
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    from frame_wise_gated_gdn_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.lib()
