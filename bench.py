@@ -120,13 +120,13 @@ def main():
     tokens = w.tokens
     value = tokens / (ms_step * 1e-3)
     D, BH, T, S = w.D, w.B * w.H, w.T, w.S
-    per_launch_frames = T                       # the workspace holds all frames: one launch each
-    rec_bytes = BH * T * S * 4 * D + BH * T * 8
+    # kernel time per step (sum over the launches of one step) and per launch
+    rec_ms_step, read_ms_step = ms_rec / args.steps, ms_read / args.steps
+    launches_per_step = max(n_rec // args.steps, 1)
+    rec_bytes = BH * T * S * 4 * D + BH * T * 8          # per step
     read_bytes = BH * T * S * 4 * D
-    avg_rec = ms_rec / max(n_rec, 1)
-    avg_read = ms_read / max(n_read, 1)
-    dom = "recurrence" if avg_rec >= avg_read else "readout"
-    dom_bytes, dom_ms = (rec_bytes, avg_rec) if dom == "recurrence" else (read_bytes, avg_read)
+    dom = "recurrence" if rec_ms_step >= read_ms_step else "readout"
+    dom_bytes, dom_ms = (rec_bytes, rec_ms_step) if dom == "recurrence" else (read_bytes, read_ms_step)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     path_bytes = BH * T * S * 8 * D
     path_flops = BH * T * S * 6 * D * D
@@ -146,15 +146,16 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V, uniform gamma/beta; no dataset)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "S": w.S, "D": w.D,
                    "io_dtype": w.dtype, "state_dtype": "f32", "beta_mode": w.beta_mode,
-                   "calls_per_step": 1, "frames_per_launch": per_launch_frames},
+                   "calls_per_step": 1, "launches_per_kernel_per_step": launches_per_step},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": pmc_traffic(dom),
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms},
+                     "algorithmic_bytes_per_launch": dom_bytes // launches_per_step,
+                     "avg_launch_ms": dom_ms / launches_per_step},
         "path_roofline": {"bound": "hbm", "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes,
                           "mfma_frac": path_flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
-        "kernels_ms_per_step": {"recurrence": avg_rec, "readout": avg_read},
+        "kernels_ms_per_step": {"recurrence": rec_ms_step, "readout": read_ms_step},
     }
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)

@@ -33,7 +33,7 @@ gdn_status fail(gdn_status s, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxFramesPerLaunch = 1024;
+using gdn::kMaxFramesPerLaunch;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
@@ -109,12 +109,17 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
   if (st != GDN_OK) return st;
   const Plan p = make_plan(d);
   const bool bf16 = d->io_dtype == GDN_BF16;
-  const size_t per_frame = p.snap_frame + p.norm_frame;
-  size_t frames = 1;  // the minimum-size check guarantees that one frame fits
-  if (workspace_bytes > p.carrier + 2 * kAlign) frames = std::max<size_t>(1, (workspace_bytes - p.carrier - 2 * kAlign) / per_frame);
-  while (frames > 1 && ws_bytes_for(p, frames) > workspace_bytes) --frames;
-  if (frames > (size_t)d->T) frames = (size_t)d->T;
-  if (frames > (size_t)kMaxFramesPerLaunch) frames = kMaxFramesPerLaunch;
+  // Largest frame count per launch whose staging fits the workspace (the
+  // minimum-size check guarantees that one frame fits).
+  size_t frames = std::min<size_t>((size_t)d->T, (size_t)kMaxFramesPerLaunch);
+  if (ws_bytes_for(p, frames) > workspace_bytes) {
+    size_t lo = 1, hi = frames;           // ws_bytes_for(lo) fits, ws_bytes_for(hi) does not
+    while (hi - lo > 1) {
+      const size_t mid = lo + (hi - lo) / 2;
+      (ws_bytes_for(p, mid) <= workspace_bytes ? lo : hi) = mid;
+    }
+    frames = lo;
+  }
 
   unsigned char* ws = (unsigned char*)workspace;
   float* carrier = (float*)ws;

@@ -7,6 +7,9 @@
 
 namespace gdn {
 
+// Frames per launch are capped so that per-frame scalars fit in LDS.
+constexpr int kMaxFramesPerLaunch = 1024;
+
 // One launch of the recurrence covers frames [t0, t0 + Tc) of the call.
 struct RecurArgs {
   const void* k;            // [BH][T][S][D]

@@ -121,7 +121,8 @@ struct RecurShape {
   static constexpr size_t vst_bytes = BF16 ? (size_t)kWaves * 32 * 16 * 2 : 0;
   static constexpr size_t red_bytes = (size_t)kWaves * NB * 64 * 16;
   static constexpr size_t mbt_bytes = (size_t)16 * MBS * ESZ;
-  static constexpr size_t lds_bytes = kst_bytes + vst_bytes + red_bytes + mbt_bytes + 64;
+  static constexpr size_t gb_bytes = (size_t)kMaxFramesPerLaunch * 8;   // gamma, beta per frame
+  static constexpr size_t lds_bytes = kst_bytes + vst_bytes + red_bytes + mbt_bytes + 64 + gb_bytes;
 };
 
 template <int D, bool BF16>
@@ -351,6 +352,247 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_kernel(RecurArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// bf16 recurrence with a register ring of prefetched chunks.
+//
+// Each wave walks the flattened sequence of its (frame, chunk) slots; slot s
+// uses register buffer s % kRing, and the loads of slot s + kRing are issued
+// right after slot s is consumed, so every chunk's keys and values are in
+// flight for kRing slots (one whole frame when a frame has kRing slots per
+// wave).  Nothing in a load depends on the state, so this prefetch crosses
+// frame boundaries freely.  The loads are buffer loads whose out-of-range
+// lanes (tokens past S, keys past D, chunks past the frame) are given an
+// offset beyond the buffer and so read zeros without touching memory: the
+// loads are branch-free and always issued, which keeps the wait counts exact.
+// The per-frame barriers only wait for LDS traffic, never for the prefetches.
+// ----------------------------------------------------------------------------
+constexpr int kRing = 4;
+constexpr uint32_t kOOB = 0x80000000u;      // offset past every buffer (buffers are < 2 GiB)
+constexpr int kBufWord3 = 0x00020000;       // gfx9 buffer descriptor word 3 (raw 32-bit dwords)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
+// its outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, bool ERASE>
+__global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a) {
+  using Sh = RecurShape<D, true>;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, KS = Sh::KS, MBS = Sh::MBS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
+  uint16_t* const kst = (uint16_t*)smem + (size_t)w * 32 * KS;
+  uint16_t* const vst = (uint16_t*)(smem + Sh::kst_bytes) + w * 32 * 16;
+  f32x4* const red = (f32x4*)(smem + Sh::kst_bytes + Sh::vst_bytes);
+  uint16_t* const mbt = (uint16_t*)(smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes);
+  float* const normp = (float*)(smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes + Sh::mbt_bytes);
+
+  const int unit = xcd_unit(a.units);
+  if (unit < 0) return;                       // whole workgroup leaves together
+  const int bh = unit / NB, jt = unit % NB, j0 = jt * 16;
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
+  const int S = a.S, T = a.T;
+  const float c = a.kscale;
+  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + (size_t)bh * T * S * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + (size_t)bh * T * S * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t snaprs = make_rsrc(a.snap, (uint32_t)((size_t)a.units / NB * a.Tc * D * D * 2));
+  const __amdgpu_buffer_rsrc_t normrs =
+      make_rsrc(a.norm_part, a.norm_part ? (uint32_t)((size_t)a.units * a.Tc * 4) : 0u);
+  // gamma and beta of the launch's frames, staged once in LDS
+  float2* const gb = (float2*)(smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes + Sh::mbt_bytes + 64);
+  for (int x = tid; x < a.Tc; x += kThreads)
+    gb[x] = make_float2(a.gamma[(size_t)bh * T + a.t0 + x], a.beta[(size_t)bh * T + a.t0 + x]);
+
+  // ---- initial state: wave w < NB owns key rows 16w..16w+15 of the tile (C layout)
+  f32x4 Mown = {0.f, 0.f, 0.f, 0.f};
+  if (w < NB && a.state_src) {
+    const float* src = a.state_src + (size_t)bh * D * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Mown[i] = src[(size_t)(16 * w + 4 * g + i) * D + j0 + n];
+  }
+  for (int x = tid; x < (int)(Sh::mbt_bytes / 4); x += kThreads) ((uint32_t*)mbt)[x] = 0u;
+  __syncthreads();
+  if (w < NB) {
+    const u32x2 pk = {pack_bf16(Mown[0], Mown[1]), pack_bf16(Mown[2], Mown[3])};
+    *(u32x2*)(mbt + n * MBS + 16 * w + 4 * g) = pk;
+  }
+  __syncthreads();
+  u32x4 MB[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) MB[kc] = *(const u32x4*)(mbt + n * MBS + 32 * kc + 8 * g);
+
+  const int nchunks = (S + 31) / 32;
+  const int NS = (nchunks + kWaves - 1) / kWaves;    // chunk slots per wave per frame
+  const int total = a.Tc * NS;
+
+  // ---- loads of one slot into a ring buffer (branch-free; zeros where out of
+  // range).  A chunk's keys are 32*D contiguous bf16: lane l of load j takes
+  // the 16-byte unit 64j + l, so every load is a fully coalesced 1 KB.
+  constexpr int UPR = D / 8;          // 16-byte units per token row
+  constexpr int NLD = D / 16;         // 1 KB loads per 32-token chunk
+  auto load_slot = [&](int s, u32x4 (&KU)[NLD], u32x4& VL) {
+    const int tl = s / NS, ch = w + kWaves * (s - tl * NS);
+    const int tb = ch * 32;
+    // valid tokens of the chunk (0 for null slots): a per-lane compare against
+    // this uniform limit selects the offset without any branch
+    const int lim = (ch < nchunks && s < total) ? min(32, S - tb) : 0;
+    const uint32_t cbase = ((uint32_t)(a.t0 + tl) * (uint32_t)S + (uint32_t)tb) * D * 2u;  // chunk's first byte
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int u = 64 * j + l;
+      KU[j] = buf_load16(krs, (u / UPR < lim) ? cbase + 16u * u : kOOB);
+    }
+    const uint32_t voff = ((l >> 1) < lim) ? cbase + ((l >> 1) * D + j0 + 8 * (l & 1)) * 2u : kOOB;
+    VL = buf_load16(vrs, voff);
+  };
+
+  float gam = gb[0].x, bet = gb[0].y;
+  f32x4 Wacc[NB];
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) Wacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- one chunk: prediction, residual, write
+  auto process = [&](int s, const u32x4 (&KU)[NLD], const u32x4& VL) {
+    const int tl = s / NS, ch = w + kWaves * (s - tl * NS);
+    if (ch >= nchunks || s >= total) return;   // wave-uniform
+    const float s_pred = bet * c * gam;
+    // stage ReLU(K) rows (padded stride KS) and the V tile
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int u = 64 * j + l;
+      *(u32x4*)(kst + (u / UPR) * KS + 8 * (u % UPR)) = relu8(KU[j]);
+    }
+    *(u32x4*)(vst + (l >> 1) * 16 + 8 * (l & 1)) = VL;
+    wave_lds_sync();
+    // prediction P = phi(K) bf16(M): A operands (token n, keys 32kc+8g..+7) from LDS
+    f32x4 P[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      P[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        u32x4 KA = {0u, 0u, 0u, 0u};
+        if (32 * kc + 8 * g < D) KA = *(const u32x4*)(kst + (16 * r + n) * KS + 32 * kc + 8 * g);
+        P[r] = mfma_bf16(KA, MB[kc], P[r]);
+      }
+    }
+    u32x4 RBhi, RBlo;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const u32x2 vv = lds_tr16(vst + (16 * r + 4 * g + (n >> 2)) * 16 + 4 * (n & 3));
+      float R[4];
+      const float v0 = bf16_lo_f32(vv[0]), v1 = bf16_hi_f32(vv[0]);
+      const float v2 = bf16_lo_f32(vv[1]), v3 = bf16_hi_f32(vv[1]);
+      if constexpr (ERASE) {
+        R[0] = v0 - s_pred * P[r][0]; R[1] = v1 - s_pred * P[r][1];
+        R[2] = v2 - s_pred * P[r][2]; R[3] = v3 - s_pred * P[r][3];
+      } else {
+        R[0] = bet * v0 - s_pred * P[r][0]; R[1] = bet * v1 - s_pred * P[r][1];
+        R[2] = bet * v2 - s_pred * P[r][2]; R[3] = bet * v3 - s_pred * P[r][3];
+      }
+      const uint32_t h01 = pack_bf16(R[0], R[1]), h23 = pack_bf16(R[2], R[3]);
+      RBhi[2 * r] = h01;
+      RBhi[2 * r + 1] = h23;
+      RBlo[2 * r] = pack_bf16(R[0] - bf16_lo_f32(h01), R[1] - bf16_hi_f32(h01));
+      RBlo[2 * r + 1] = pack_bf16(R[2] - bf16_lo_f32(h23), R[3] - bf16_hi_f32(h23));
+    }
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      const uint16_t* p0 = kst + (4 * g + (n >> 2)) * KS + 16 * kb + 4 * (n & 3);
+      const u32x2 a0 = lds_tr16(p0);
+      const u32x2 a1 = lds_tr16(p0 + 16 * KS);
+      const u32x4 A = {a0[0], a0[1], a1[0], a1[1]};
+      Wacc[kb] = mfma_bf16(A, RBhi, Wacc[kb]);
+      Wacc[kb] = mfma_bf16(A, RBlo, Wacc[kb]);
+    }
+    wave_lds_sync();
+  };
+
+  // ---- end of a frame: reduce the waves' partial writes (fixed order), update
+  // the owned 16-key block, publish bf16(M) to LDS and to the frame snapshot.
+  auto end_frame = [&](int tl) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) red[(w * NB + kb) * 64 + l] = Wacc[kb];
+    lds_barrier();
+    // waves w < NB own key block w; the others run the same instructions on a
+    // clamped block and drop their stores (offset beyond the buffer), so every
+    // wave issues the same memory operations (uniform wait counts)
+    const int ob = w < NB ? w : NB - 1;
+    f32x4 sum = red[ob * 64 + l];
+    for (int ww = 1; ww < kWaves; ++ww) {
+      const f32x4 x = red[(ww * NB + ob) * 64 + l];
+      sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
+    }
+    f32x4 Mn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Mn[i] = gam * Mown[i] + c * sum[i];
+    if (w < NB) Mown = Mn;
+    const u32x2 pk = {pack_bf16(Mn[0], Mn[1]), pack_bf16(Mn[2], Mn[3])};
+    if (w < NB) *(u32x2*)(mbt + n * MBS + 16 * w + 4 * g) = pk;
+    const uint32_t snap_off =
+        (uint32_t)(((size_t)(bh * a.Tc + tl) * D * D + (size_t)(j0 + n) * D + 16 * ob + 4 * g) * 2);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), snaprs, w < NB ? snap_off : kOOB, 0, 0);
+    if (a.norm_part) {
+      float sq = Mn[0] * Mn[0] + Mn[1] * Mn[1] + Mn[2] * Mn[2] + Mn[3] * Mn[3];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+      if (w < NB && l == 0) normp[w] = sq;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) MB[kc] = *(const u32x4*)(mbt + n * MBS + 32 * kc + 8 * g);
+    if (a.norm_part) {
+      float sq = 0.f;
+      for (int kb = 0; kb < NB; ++kb) sq += normp[kb];
+      const uint32_t noff = (uint32_t)((((size_t)bh * a.Tc + tl) * NB + jt) * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sq), normrs, tid == 0 ? noff : kOOB, 0, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) Wacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tl + 1 < a.Tc) { const float2 x = gb[tl + 1]; gam = x.x; bet = x.y; }
+  };
+
+  // Slots past `total` are null (their loads read zeros without touching
+  // memory); issuing every ring load unconditionally keeps the number of
+  // loads in flight the same on every path, so each wait is exact.
+  u32x4 KU[kRing][NLD];
+  u32x4 VL[kRing];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    load_slot(r, KU[r], VL[r]);
+    __builtin_amdgcn_sched_barrier(0);   // issue the prologue in ring order
+  }
+  for (int base = 0; base < total; base += kRing) {
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      const int s = base + r;
+      process(s, KU[r], VL[r]);
+      load_slot(s + kRing, KU[r], VL[r]);
+      // keep the prefetch where it is issued: the scheduler would otherwise
+      // sink these loads towards their use and shorten the prefetch distance
+      __builtin_amdgcn_sched_barrier(0);
+      const int tl = s / NS;
+      if (s < total && s - tl * NS == NS - 1) end_frame(tl);
+    }
+  }
+
+  if (w < NB && a.state_dst) {
+    float* dst = a.state_dst + (size_t)bh * D * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(size_t)(16 * w + 4 * g + i) * D + j0 + n] = Mown[i];
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Readout kernel: O_t = Qf M_t, computed as O^T = M^T Qf^T so that the Q rows
 // are natural B operands (16 contiguous bytes per lane) and each lane stores
 // 4 consecutive output columns of one token.
@@ -435,6 +677,123 @@ __global__ __launch_bounds__(kReadWaves * 64) void gdn_readout_kernel(ReadoutArg
 }
 
 // ----------------------------------------------------------------------------
+// bf16 readout.  One workgroup per (head, frame); every wave holds M_t^T as A
+// operands and walks 32-token chunks of the frame.  Q chunks are read with
+// fully coalesced 16-byte loads (a chunk is 32*D contiguous bf16), kept
+// kReadRing chunks ahead in registers, passed through ReLU and staged in the
+// wave's LDS tile, from which the B operands (token n, 8 consecutive keys) are
+// read.  The O chunk is assembled in a second LDS tile and written back with
+// the same coalesced pattern.  Out-of-range lanes use an offset beyond the
+// buffer: their loads read zeros and their stores are dropped, so the loop is
+// branch-free and its wait counts are exact.
+// ----------------------------------------------------------------------------
+constexpr int kReadRing = 3;
+
+template <int D>
+struct ReadShape {
+  static constexpr int NB = D / 16, NKC = (D + 31) / 32;
+  static constexpr int UPR = D / 8;              // 16-byte units per token row
+  static constexpr int NLD = D / 16;             // 1 KB loads per 32-token chunk (= 32*UPR/64)
+  static constexpr int RS = D + 8;               // LDS row stride (elements)
+  static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
+  static constexpr size_t lds_bytes = (size_t)kReadWaves * 2 * tile_bytes;
+};
+
+template <int D>
+__global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(ReadoutArgs a) {
+  using Sh = ReadShape<D>;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, UPR = Sh::UPR, NLD = Sh::NLD, RS = Sh::RS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int frame = blockIdx.x;                    // over BH * Tc
+  const int bh = frame / a.Tc, tl = frame % a.Tc, t = a.t0 + tl;
+  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* const qs = (uint16_t*)(smem + (size_t)w * 2 * Sh::tile_bytes);
+  uint16_t* const os = qs + 32 * RS;
+  const int S = a.S, T = a.T;
+  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const uint16_t*)a.q + (size_t)bh * T * S * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc((uint16_t*)a.o + (size_t)bh * T * S * D, head_bytes);
+  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * 2u;   // frame's first byte in the head
+  const int nchunk = (S + 31) / 32;
+  const int NC = (nchunk + kReadWaves - 1) / kReadWaves;     // chunk slots per wave
+
+  if (a.norms && tid == 0) {
+    float sq = 0.f;
+    for (int j = 0; j < NB; ++j) sq += a.norm_part[((size_t)bh * a.Tc + tl) * NB + j];
+    a.norms[(size_t)bh * T + t] = sqrtf(sq);
+  }
+
+  // byte offset of 16-byte unit u of a chunk (tokens past S -> beyond the buffer)
+  auto unit_off = [&](int ch, int u) -> uint32_t {
+    const int tok = ch * 32 + u / UPR;
+    return (ch < nchunk && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * 16u : kOOB;
+  };
+  auto load_chunk = [&](int i, u32x4 (&X)[NLD]) {
+    const int ch = w + kReadWaves * i;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) X[j] = buf_load16(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
+  };
+
+  // A operands: M_t^T rows (value column 16jb + n), keys 32kc + 8g .. +7
+  const uint16_t* snap = (const uint16_t*)a.snap + ((size_t)bh * a.Tc + tl) * D * D;
+  u32x4 A[NB][NKC];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int key = 32 * kc + 8 * g;
+      A[jb][kc] = (key < D) ? *(const u32x4*)(snap + (size_t)(16 * jb + n) * D + key) : u32x4{0u, 0u, 0u, 0u};
+    }
+  u32x4 X[kReadRing][NLD];
+#pragma unroll
+  for (int r = 0; r < kReadRing; ++r) load_chunk(r, X[r]);
+  // The snapshot loads were issued first: one use of the last of them makes
+  // the compiler wait for all of them here, once, instead of inside the loop.
+  asm volatile("" ::"v"(A[NB - 1][NKC - 1]));
+
+  for (int base = 0; base < NC; base += kReadRing) {
+#pragma unroll
+    for (int r = 0; r < kReadRing; ++r) {
+      const int i = base + r;
+      const int ch = w + kReadWaves * i;
+      // stage ReLU(Q) of the chunk (row-major, padded rows)
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int u = 64 * j + l;
+        *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(X[r][j]);
+      }
+      load_chunk(i + kReadRing, X[r]);
+      wave_lds_sync();
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 B[NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          B[kc] = u32x4{0u, 0u, 0u, 0u};
+          if (32 * kc + 8 * g < D) B[kc] = *(const u32x4*)(qs + (16 * half + n) * RS + 32 * kc + 8 * g);
+        }
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) acc = mfma_bf16(A[jb][kc], B[kc], acc);
+          const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+          *(u32x2*)(os + (16 * half + n) * RS + 16 * jb + 4 * g) = pk;
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int u = 64 * j + l;
+        const u32x4 y = *(const u32x4*)(os + (u / UPR) * RS + 8 * (u % UPR));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ors, i < NC ? unit_off(ch, u) : kOOB, 0, 0);
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------
 template <int D, bool BF16>
@@ -443,24 +802,48 @@ static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStr
   using Sh = RecurShape<D, BF16>;
   static bool attr_set = false;   // benign race: every setter writes the same value
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_recur_kernel<D, BF16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+    hipError_t e = hipSuccess;
+    if constexpr (BF16) {
+      e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+      if (e != hipSuccess) return e;
+      e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+    } else {
+      e = hipFuncSetAttribute((const void*)gdn_recur_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+    }
     if (e != hipSuccess) return e;
-    if (!BF16) {
+    if constexpr (BF16) {
+      e = hipFuncSetAttribute((const void*)gdn_readout_bf16_kernel<D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
+    } else {
       e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, BF16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
-      if (e != hipSuccess) return e;
     }
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int grid = 8 * ((ra.units + 7) / 8);
   if (ev) { hipError_t e = hipEventRecord(ev[0], stream); if (e != hipSuccess) return e; }
-  hipLaunchKernelGGL((gdn_recur_kernel<D, BF16>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+  if constexpr (BF16) {
+    if (ra.beta_mode == 0)
+      hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+    else
+      hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, false>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+  } else {
+    hipLaunchKernelGGL((gdn_recur_kernel<D, BF16>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev) { e = hipEventRecord(ev[1], stream); if (e != hipSuccess) return e; }
-  const size_t rlds = BF16 ? 0 : (size_t)D * (D + 1) * 4;
-  hipLaunchKernelGGL((gdn_readout_kernel<D, BF16>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64), rlds, stream, ro);
+  if constexpr (BF16) {
+    hipLaunchKernelGGL((gdn_readout_bf16_kernel<D>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
+                       ReadShape<D>::lds_bytes, stream, ro);
+  } else {
+    hipLaunchKernelGGL((gdn_readout_kernel<D, BF16>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
+                       (size_t)D * (D + 1) * 4, stream, ro);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev) { e = hipEventRecord(ev[2], stream); if (e != hipSuccess) return e; }
