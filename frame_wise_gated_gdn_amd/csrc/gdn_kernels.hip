@@ -383,17 +383,41 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The values enter the prediction MFMA as extra k-slots: the A operand of the
+// last k-chunk carries the 16 value columns of the tile in lanes g = 2, 3 and
+// the B operand holds -I there, so the MFMA returns P' = phi(K) bf16(s M) - V
+// = -R directly (s = beta c gamma for ERASE, c gamma for WRITE).  For D = 16
+// mod 32 these slots are the free half of the last key chunk; otherwise one
+// extra chunk is added.
+template <int D>
+struct BfShape {
+  static constexpr int NB = D / 16;
+  static constexpr int NKK = (D + 31) / 32;              // k-chunks holding keys
+  static constexpr bool VIN = (D % 32) == 16;            // values fit in the last key chunk
+  static constexpr int NKC = VIN ? NKK : NKK + 1;        // k-chunks of the prediction
+  static constexpr int UPR = D / 8;                      // 16-byte units per token row
+  static constexpr int NLD = D / 16;                     // 1 KB key loads per 32-token chunk
+  static constexpr int KS = D + 8;                       // LDS key row stride (elements)
+  static constexpr int MBS = 32 * NKC + 8;               // LDS B-operand row stride (elements)
+  static constexpr size_t kst_bytes = (size_t)kWaves * 32 * KS * 2;
+  static constexpr size_t red_bytes = (size_t)kWaves * NB * 64 * 16;
+  static constexpr size_t mbt_bytes = (size_t)16 * MBS * 2;
+  static constexpr size_t gb_bytes = (size_t)kMaxFramesPerLaunch * 8;
+  static constexpr size_t lds_bytes = kst_bytes + red_bytes + mbt_bytes + 64 + gb_bytes;
+};
+
 template <int D, bool ERASE>
 __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a) {
-  using Sh = RecurShape<D, true>;
-  constexpr int NB = Sh::NB, NKC = Sh::NKC, KS = Sh::KS, MBS = Sh::MBS;
+  using Sh = BfShape<D>;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, UPR = Sh::UPR, NLD = Sh::NLD, KS = Sh::KS, MBS = Sh::MBS;
+  constexpr bool VIN = Sh::VIN;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
   uint16_t* const kst = (uint16_t*)smem + (size_t)w * 32 * KS;
-  uint16_t* const vst = (uint16_t*)(smem + Sh::kst_bytes) + w * 32 * 16;
-  f32x4* const red = (f32x4*)(smem + Sh::kst_bytes + Sh::vst_bytes);
-  uint16_t* const mbt = (uint16_t*)(smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes);
-  float* const normp = (float*)(smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes + Sh::mbt_bytes);
+  f32x4* const red = (f32x4*)(smem + Sh::kst_bytes);
+  uint16_t* const mbt = (uint16_t*)(smem + Sh::kst_bytes + Sh::red_bytes);
+  float* const normp = (float*)(smem + Sh::kst_bytes + Sh::red_bytes + Sh::mbt_bytes);
+  float2* const gb = (float2*)(smem + Sh::kst_bytes + Sh::red_bytes + Sh::mbt_bytes + 64);
 
   const int unit = xcd_unit(a.units);
   if (unit < 0) return;                       // whole workgroup leaves together
@@ -407,11 +431,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
   const __amdgpu_buffer_rsrc_t snaprs = make_rsrc(a.snap, (uint32_t)((size_t)a.units / NB * a.Tc * D * D * 2));
   const __amdgpu_buffer_rsrc_t normrs =
       make_rsrc(a.norm_part, a.norm_part ? (uint32_t)((size_t)a.units * a.Tc * 4) : 0u);
-  // gamma and beta of the launch's frames, staged once in LDS
-  float2* const gb = (float2*)(smem + Sh::kst_bytes + Sh::vst_bytes + Sh::red_bytes + Sh::mbt_bytes + 64);
+
   for (int x = tid; x < a.Tc; x += kThreads)
     gb[x] = make_float2(a.gamma[(size_t)bh * T + a.t0 + x], a.beta[(size_t)bh * T + a.t0 + x]);
-
   // ---- initial state: wave w < NB owns key rows 16w..16w+15 of the tile (C layout)
   f32x4 Mown = {0.f, 0.f, 0.f, 0.f};
   if (w < NB && a.state_src) {
@@ -419,10 +441,18 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
 #pragma unroll
     for (int i = 0; i < 4; ++i) Mown[i] = src[(size_t)(16 * w + 4 * g + i) * D + j0 + n];
   }
+  // B operand rows: keys (filled per frame) and -I on the value slots
   for (int x = tid; x < (int)(Sh::mbt_bytes / 4); x += kThreads) ((uint32_t*)mbt)[x] = 0u;
   __syncthreads();
+  if (tid < 16) mbt[tid * MBS + 32 * (NKC - 1) + 16 + tid] = 0xBF80u;   // bf16(-1)
+  // scale of the state inside the prediction for frame tl
+  auto pred_scale = [&](int tl) {
+    const float2 x = gb[tl];
+    return ERASE ? x.y * c * x.x : c * x.x;
+  };
   if (w < NB) {
-    const u32x2 pk = {pack_bf16(Mown[0], Mown[1]), pack_bf16(Mown[2], Mown[3])};
+    const float s0 = pred_scale(0);
+    const u32x2 pk = {pack_bf16(s0 * Mown[0], s0 * Mown[1]), pack_bf16(s0 * Mown[2], s0 * Mown[3])};
     *(u32x2*)(mbt + n * MBS + 16 * w + 4 * g) = pk;
   }
   __syncthreads();
@@ -432,78 +462,85 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
 
   const int nchunks = (S + 31) / 32;
   const int NS = (nchunks + kWaves - 1) / kWaves;    // chunk slots per wave per frame
-  const int total = a.Tc * NS;
+  const uint32_t frame_bytes = (uint32_t)S * D * 2u;
+  // per-lane byte offsets of the value columns (lanes g >= 2) inside a chunk
+  const uint32_t voff0 = (uint32_t)(n * D + j0 + 8 * (g & 1)) * 2u;
+  const uint32_t voff1 = voff0 + 16u * D * 2u;
 
-  // ---- loads of one slot into a ring buffer (branch-free; zeros where out of
-  // range).  A chunk's keys are 32*D contiguous bf16: lane l of load j takes
-  // the 16-byte unit 64j + l, so every load is a fully coalesced 1 KB.
-  constexpr int UPR = D / 8;          // 16-byte units per token row
-  constexpr int NLD = D / 16;         // 1 KB loads per 32-token chunk
-  auto load_slot = [&](int s, u32x4 (&KU)[NLD], u32x4& VL) {
-    const int tl = s / NS, ch = w + kWaves * (s - tl * NS);
-    const int tb = ch * 32;
-    // valid tokens of the chunk (0 for null slots): a per-lane compare against
-    // this uniform limit selects the offset without any branch
-    const int lim = (ch < nchunks && s < total) ? min(32, S - tb) : 0;
-    const uint32_t cbase = ((uint32_t)(a.t0 + tl) * (uint32_t)S + (uint32_t)tb) * D * 2u;  // chunk's first byte
+  // ---- A slot is (frame tl, chunk slot i): the wave's chunk w + kWaves*i of
+  // frame tl.  Loads are branch-free: a null slot gets an offset past the
+  // buffer (a uniform select; offsets added to it stay past the buffer), rows
+  // past the frame are cleared when the chunk is used, reads past the head
+  // read zeros.
+  auto chunk_base = [&](int tl, int i) -> uint32_t {
+    const int ch = w + kWaves * i;
+    return (ch < nchunks && tl < a.Tc) ? (uint32_t)(a.t0 + tl) * frame_bytes + (uint32_t)ch * (64u * D) : kOOB;
+  };
+  auto load_k = [&](int tl, int i, u32x4 (&KU)[NLD]) {
+    const uint32_t cb = chunk_base(tl, i);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int u = 64 * j + l;
-      KU[j] = buf_load16(krs, (u / UPR < lim) ? cbase + 16u * u : kOOB);
-    }
-    const uint32_t voff = ((l >> 1) < lim) ? cbase + ((l >> 1) * D + j0 + 8 * (l & 1)) * 2u : kOOB;
-    VL = buf_load16(vrs, voff);
+    for (int j = 0; j < NLD; ++j) KU[j] = buf_load16(krs, cb + 16u * l + 1024u * j);
+  };
+  auto load_v = [&](int tl, int i, u32x4 (&VV)[2]) {
+    const uint32_t cb = chunk_base(tl, i);
+    VV[0] = buf_load16(vrs, g >= 2 ? cb + voff0 : kOOB);
+    VV[1] = buf_load16(vrs, g >= 2 ? cb + voff1 : kOOB);
   };
 
-  float gam = gb[0].x, bet = gb[0].y;
   f32x4 Wacc[NB];
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) Wacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- one chunk: prediction, residual, write
-  auto process = [&](int s, const u32x4 (&KU)[NLD], const u32x4& VL) {
-    const int tl = s / NS, ch = w + kWaves * (s - tl * NS);
-    if (ch >= nchunks || s >= total) return;   // wave-uniform
-    const float s_pred = bet * c * gam;
-    // stage ReLU(K) rows (padded stride KS) and the V tile
+  // ---- stage a chunk's keys: ReLU, then the wave's LDS tile (row-major,
+  // padded).  Lanes exchange data through this tile: LDS operations of one
+  // wave execute in program order, and the compiler keeps that order because
+  // the addresses are lane-dependent (may alias).
+  auto stage = [&](int tl, int i, u32x4 (&KU)[NLD]) {
+    const int ch = w + kWaves * i;
+    if (ch >= nchunks || tl >= a.Tc) return;   // wave-uniform
+    const int lim = S - ch * 32;               // valid rows of the chunk
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int u = 64 * j + l;
-      *(u32x4*)(kst + (u / UPR) * KS + 8 * (u % UPR)) = relu8(KU[j]);
+      u32x4 x = relu8(KU[j]);
+      if (lim < 32 && u / UPR >= lim) x = u32x4{0u, 0u, 0u, 0u};   // ragged last chunk
+      *(u32x4*)(kst + (u / UPR) * KS + 8 * (u % UPR)) = x;
     }
-    *(u32x4*)(vst + (l >> 1) * 16 + 8 * (l & 1)) = VL;
-    wave_lds_sync();
-    // prediction P = phi(K) bf16(M): A operands (token n, keys 32kc+8g..+7) from LDS
+  };
+
+  // ---- one staged chunk: P' = -R from the MFMA, its hi/lo split, write accumulation
+  auto compute = [&](int tl, int i, const u32x4 (&VV)[2]) {
+    const int ch = w + kWaves * i;
+    if (ch >= nchunks || tl >= a.Tc) return;   // wave-uniform
+    const int lim = S - ch * 32;
     f32x4 P[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       P[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const u32x4 vr = (16 * r + n < lim) ? VV[r] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        u32x4 KA = {0u, 0u, 0u, 0u};
-        if (32 * kc + 8 * g < D) KA = *(const u32x4*)(kst + (16 * r + n) * KS + 32 * kc + 8 * g);
-        P[r] = mfma_bf16(KA, MB[kc], P[r]);
+        u32x4 A;
+        if (kc < NKC - 1) {
+          A = *(const u32x4*)(kst + (16 * r + n) * KS + 32 * kc + 8 * g);
+        } else if constexpr (VIN) {
+          const u32x4 kk = *(const u32x4*)(kst + (16 * r + n) * KS + 32 * kc + 8 * (g & 1));
+          A = (g >= 2) ? vr : kk;
+        } else {
+          A = (g >= 2) ? vr : u32x4{0u, 0u, 0u, 0u};
+        }
+        P[r] = mfma_bf16(A, MB[kc], P[r]);
       }
     }
+    // P' = -R: split into bf16 hi + lo for the write's B operand
     u32x4 RBhi, RBlo;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const u32x2 vv = lds_tr16(vst + (16 * r + 4 * g + (n >> 2)) * 16 + 4 * (n & 3));
-      float R[4];
-      const float v0 = bf16_lo_f32(vv[0]), v1 = bf16_hi_f32(vv[0]);
-      const float v2 = bf16_lo_f32(vv[1]), v3 = bf16_hi_f32(vv[1]);
-      if constexpr (ERASE) {
-        R[0] = v0 - s_pred * P[r][0]; R[1] = v1 - s_pred * P[r][1];
-        R[2] = v2 - s_pred * P[r][2]; R[3] = v3 - s_pred * P[r][3];
-      } else {
-        R[0] = bet * v0 - s_pred * P[r][0]; R[1] = bet * v1 - s_pred * P[r][1];
-        R[2] = bet * v2 - s_pred * P[r][2]; R[3] = bet * v3 - s_pred * P[r][3];
-      }
-      const uint32_t h01 = pack_bf16(R[0], R[1]), h23 = pack_bf16(R[2], R[3]);
+      const uint32_t h01 = pack_bf16(P[r][0], P[r][1]), h23 = pack_bf16(P[r][2], P[r][3]);
       RBhi[2 * r] = h01;
       RBhi[2 * r + 1] = h23;
-      RBlo[2 * r] = pack_bf16(R[0] - bf16_lo_f32(h01), R[1] - bf16_hi_f32(h01));
-      RBlo[2 * r + 1] = pack_bf16(R[2] - bf16_lo_f32(h23), R[3] - bf16_hi_f32(h23));
+      RBlo[2 * r] = pack_bf16(P[r][0] - bf16_lo_f32(h01), P[r][1] - bf16_hi_f32(h01));
+      RBlo[2 * r + 1] = pack_bf16(P[r][2] - bf16_lo_f32(h23), P[r][3] - bf16_hi_f32(h23));
     }
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
@@ -514,33 +551,36 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
       Wacc[kb] = mfma_bf16(A, RBhi, Wacc[kb]);
       Wacc[kb] = mfma_bf16(A, RBlo, Wacc[kb]);
     }
-    wave_lds_sync();
   };
 
   // ---- end of a frame: reduce the waves' partial writes (fixed order), update
-  // the owned 16-key block, publish bf16(M) to LDS and to the frame snapshot.
+  // the owned 16-key block (M = gamma M + c alpha Kf^T R, alpha = 1 or beta),
+  // publish bf16(M) to the snapshot and bf16(s' M) to LDS for the next frame.
   auto end_frame = [&](int tl) {
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) red[(w * NB + kb) * 64 + l] = Wacc[kb];
     lds_barrier();
-    // waves w < NB own key block w; the others run the same instructions on a
-    // clamped block and drop their stores (offset beyond the buffer), so every
-    // wave issues the same memory operations (uniform wait counts)
+    // waves w >= NB run the same instructions on a clamped block and drop
+    // their stores, so every wave issues the same memory operations
     const int ob = w < NB ? w : NB - 1;
     f32x4 sum = red[ob * 64 + l];
     for (int ww = 1; ww < kWaves; ++ww) {
       const f32x4 x = red[(ww * NB + ob) * 64 + l];
       sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
     }
+    const float2 gbt = gb[tl];
+    const float upd = ERASE ? c : c * gbt.y;        // sum accumulated -R
     f32x4 Mn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Mn[i] = gam * Mown[i] + c * sum[i];
+    for (int i = 0; i < 4; ++i) Mn[i] = gbt.x * Mown[i] - upd * sum[i];
     if (w < NB) Mown = Mn;
     const u32x2 pk = {pack_bf16(Mn[0], Mn[1]), pack_bf16(Mn[2], Mn[3])};
-    if (w < NB) *(u32x2*)(mbt + n * MBS + 16 * w + 4 * g) = pk;
     const uint32_t snap_off =
         (uint32_t)(((size_t)(bh * a.Tc + tl) * D * D + (size_t)(j0 + n) * D + 16 * ob + 4 * g) * 2);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), snaprs, w < NB ? snap_off : kOOB, 0, 0);
+    const float s1 = pred_scale(tl + 1 < a.Tc ? tl + 1 : tl);
+    const u32x2 pm = {pack_bf16(s1 * Mn[0], s1 * Mn[1]), pack_bf16(s1 * Mn[2], s1 * Mn[3])};
+    if (w < NB) *(u32x2*)(mbt + n * MBS + 16 * w + 4 * g) = pm;
     if (a.norm_part) {
       float sq = Mn[0] * Mn[0] + Mn[1] * Mn[1] + Mn[2] * Mn[2] + Mn[3] * Mn[3];
 #pragma unroll
@@ -558,30 +598,59 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
     }
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) Wacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tl + 1 < a.Tc) { const float2 x = gb[tl + 1]; gam = x.x; bet = x.y; }
   };
 
-  // Slots past `total` are null (their loads read zeros without touching
-  // memory); issuing every ring load unconditionally keeps the number of
-  // loads in flight the same on every path, so each wait is exact.
+  // Software pipeline over the wave's slots (s = 0, 1, ...): iteration s
+  // computes slot s from the staged LDS tile and the values loaded kRing slots
+  // earlier, then stages slot s + 1 (its ReLU and LDS writes overlap the MFMAs
+  // of slot s), and refills the two register rings: values of slot s + kRing,
+  // keys of slot s + 1 + kRing.  Slots past the last frame are null: their
+  // loads read zeros without touching memory, so every ring load is issued
+  // unconditionally and each wait count is exact.  The prologue issues its
+  // loads in the loop's order (keys s+1 after values s) for the same reason.
   u32x4 KU[kRing][NLD];
-  u32x4 VL[kRing];
+  u32x4 VV[kRing][2];
+  int ktl = 0, ki = 0;                       // next slot whose keys are loaded
+  int vtl = 0, vi = 0;                       // next slot whose values are loaded
+  auto advance = [&](int& tl, int& i) {
+    if (++i == NS) { i = 0; ++tl; }
+  };
+  load_k(ktl, ki, KU[0]);
+  advance(ktl, ki);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
-    load_slot(r, KU[r], VL[r]);
-    __builtin_amdgcn_sched_barrier(0);   // issue the prologue in ring order
+    load_v(vtl, vi, VV[r]);
+    advance(vtl, vi);
+    __builtin_amdgcn_sched_barrier(0);
+    if (r + 1 < kRing) {
+      load_k(ktl, ki, KU[r + 1]);
+      advance(ktl, ki);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  for (int base = 0; base < total; base += kRing) {
+  stage(0, 0, KU[0]);
+  load_k(ktl, ki, KU[0]);
+  advance(ktl, ki);
+  __builtin_amdgcn_sched_barrier(0);
+  int ptl = 0, pi = 0;                       // slot being computed
+  int qtl = 0, qi = 0;                       // slot to stage next (= computed + 1)
+  advance(qtl, qi);
+  while (ptl < a.Tc) {
 #pragma unroll
     for (int r = 0; r < kRing; ++r) {
-      const int s = base + r;
-      process(s, KU[r], VL[r]);
-      load_slot(s + kRing, KU[r], VL[r]);
-      // keep the prefetch where it is issued: the scheduler would otherwise
-      // sink these loads towards their use and shorten the prefetch distance
-      __builtin_amdgcn_sched_barrier(0);
-      const int tl = s / NS;
-      if (s < total && s - tl * NS == NS - 1) end_frame(tl);
+      compute(ptl, pi, VV[r]);
+      load_v(vtl, vi, VV[r]);
+      advance(vtl, vi);
+      stage(qtl, qi, KU[(r + 1) % kRing]);
+      load_k(ktl, ki, KU[(r + 1) % kRing]);
+      advance(ktl, ki);
+      // keep the prefetch loads where they are issued (the scheduler would
+      // otherwise sink them towards their use); other work may move across
+      __builtin_amdgcn_sched_barrier(0x78F);
+      if (pi == NS - 1 && ptl < a.Tc) end_frame(ptl);
+      advance(ptl, pi);
+      advance(qtl, qi);
     }
   }
 
@@ -805,10 +874,10 @@ static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStr
     hipError_t e = hipSuccess;
     if constexpr (BF16) {
       e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)BfShape<D>::lds_bytes);
       if (e != hipSuccess) return e;
       e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)BfShape<D>::lds_bytes);
     } else {
       e = hipFuncSetAttribute((const void*)gdn_recur_kernel<D, BF16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
@@ -828,9 +897,11 @@ static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStr
   if (ev) { hipError_t e = hipEventRecord(ev[0], stream); if (e != hipSuccess) return e; }
   if constexpr (BF16) {
     if (ra.beta_mode == 0)
-      hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+      hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), BfShape<D>::lds_bytes,
+                         stream, ra);
     else
-      hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, false>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
+      hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, false>), dim3(grid), dim3(kThreads), BfShape<D>::lds_bytes,
+                         stream, ra);
   } else {
     hipLaunchKernelGGL((gdn_recur_kernel<D, BF16>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
   }
