@@ -74,7 +74,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-heads", type=int, default=3, help="oracle heads timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="oracle heads timed for cpu_baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (for rocprofv3 counter calibration)")
     args = ap.parse_args()
