@@ -7,11 +7,16 @@ already resident in HBM.  Prints ONE JSON line with tokens/s (B*H*T*S per
 second), the roofline of the dominant kernel, the whole-path roofline and the
 oracle's CPU rate on a bounded sample.
 
-Roofline bookkeeping (algorithmic bytes only; the per-frame state snapshots
-and the re-reads of keys by the column tiles are overhead, not algorithm):
+The default bf16 path is the Gram pipeline (gram pass, serial state pass,
+readout); --path direct times the single-pass recurrence instead.
+
+Roofline bookkeeping (algorithmic bytes only; the per-frame G/B staging, the
+state snapshots and any re-reads are overhead, not algorithm):
   whole path   8*D bytes per token-head (Q, K, V read; O written, bf16)
+  gram         4*D bytes per token-head (K, V read)
   recurrence   4*D bytes per token-head (K, V read) + 8 per frame-head (gamma, beta)
-  readout      4*D bytes per token-head (Q read, O written) + 4 per frame-head if norms
+  state        8 bytes per frame-head (gamma, beta)
+  readout      4*D bytes per token-head (Q read, O written)
 """
 from __future__ import annotations
 
@@ -27,12 +32,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFS = 2500.0    # dense bf16 MFMA, TFLOP/s
-KERNEL_SRC = os.path.join(ROOT, "frame_wise_gated_gdn_amd", "csrc", "gdn_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "frame_wise_gated_gdn_amd", "csrc", f)
+               for f in ("gdn_device.h", "gdn_kernels.hip", "gdn_gram.hip")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_minute720p.json")
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the device sources (the counters are only valid for the kernels they were taken on)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def pmc_traffic(kernel: str):
@@ -75,6 +85,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=12, help="oracle heads timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--path", choices=("auto", "direct"), default="auto",
+                    help="bf16 path: Gram pipeline (auto) or single-pass recurrence (direct)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (for rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -92,13 +104,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = wl.generate(w, device=dev)
-    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode,
+                         gdn.binding.FLAG_DIRECT if args.path == "direct" else 0)
     ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])
     st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
     call = lambda timed: gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
                                            beta_mode=w.beta_mode, out=out, state_out=st, workspace=ws,
-                                           time_kernels=timed)
+                                           time_kernels=timed, path=args.path)
     for _ in range(args.warmup):
         call(False)
     torch.cuda.synchronize()
@@ -109,7 +122,7 @@ def main():
         call(True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    (ms_rec, ms_read), (n_rec, n_read) = gdn.kernel_times(reset=True)
+    ktimes = gdn.kernel_times(reset=True)
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -121,12 +134,13 @@ def main():
     value = tokens / (ms_step * 1e-3)
     D, BH, T, S = w.D, w.B * w.H, w.T, w.S
     # kernel time per step (sum over the launches of one step) and per launch
-    rec_ms_step, read_ms_step = ms_rec / args.steps, ms_read / args.steps
-    launches_per_step = max(n_rec // args.steps, 1)
-    rec_bytes = BH * T * S * 4 * D + BH * T * 8          # per step
-    read_bytes = BH * T * S * 4 * D
-    dom = "recurrence" if rec_ms_step >= read_ms_step else "readout"
-    dom_bytes, dom_ms = (rec_bytes, rec_ms_step) if dom == "recurrence" else (read_bytes, read_ms_step)
+    kms = {name: ms / args.steps for name, (ms, n) in ktimes.items() if n > 0}
+    klaunch = {name: n // args.steps for name, (ms, n) in ktimes.items() if n > 0}
+    alg_bytes = {"gram": BH * T * S * 4 * D, "recurrence": BH * T * S * 4 * D + BH * T * 8,
+                 "state": BH * T * 8, "readout": BH * T * S * 4 * D}
+    dom = max(kms, key=kms.get)
+    launches_per_step = max(klaunch[dom], 1)
+    dom_bytes, dom_ms = alg_bytes[dom], kms[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     path_bytes = BH * T * S * 8 * D
     path_flops = BH * T * S * 6 * D * D
@@ -146,6 +160,7 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V, uniform gamma/beta; no dataset)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "S": w.S, "D": w.D,
                    "io_dtype": w.dtype, "state_dtype": "f32", "beta_mode": w.beta_mode,
+                   "path": "gram" if args.path == "auto" else "direct",
                    "calls_per_step": 1, "launches_per_kernel_per_step": launches_per_step},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -155,7 +170,7 @@ def main():
         "path_roofline": {"bound": "hbm", "achieved": path_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes,
                           "mfma_frac": path_flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
-        "kernels_ms_per_step": {"recurrence": rec_ms_step, "readout": read_ms_step},
+        "kernels_ms_per_step": kms,
     }
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Dict, Optional, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdn.so")
@@ -17,6 +17,9 @@ ABI_VERSION = 1
 F32, BF16 = 0, 1
 ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
+FLAG_DIRECT = 0x2
+# kernel kinds of gdn_kernel_times, in slot order
+KERNELS = ("recurrence", "readout", "gram", "state")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_ABI", 8: "GDN_ERR_WORKSPACE",
           9: "GDN_ERR_HIP"}
@@ -103,20 +106,26 @@ def check_args(desc: Desc, q=0, k=0, v=0, gamma=0, beta=0, state_in=0, o=0, stat
                                     int(bool(state_in_required))))
 
 
-def kernel_times(reset: bool = True) -> Tuple[Tuple[float, float], Tuple[int, int]]:
-    """(ms_recurrence, ms_readout), (launches_recurrence, launches_readout) recorded so far."""
-    ms = (ctypes.c_double * 2)()
-    n = (ctypes.c_int64 * 2)()
+def kernel_times(reset: bool = True) -> Dict[str, Tuple[float, int]]:
+    """{kernel kind: (total ms, launches)} recorded by timed calls so far."""
+    ms = (ctypes.c_double * len(KERNELS))()
+    n = (ctypes.c_int64 * len(KERNELS))()
     _raise(lib().gdn_kernel_times(ms, n, int(reset)))
-    return (ms[0], ms[1]), (int(n[0]), int(n[1]))
+    return {name: (ms[i], int(n[i])) for i, name in enumerate(KERNELS)}
 
 
 def _addr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _flags(path: str, time_kernels: bool) -> int:
+    if path not in ("auto", "direct"):
+        raise ValueError('path must be "auto" or "direct"')
+    return (FLAG_TIME_KERNELS if time_kernels else 0) | (FLAG_DIRECT if path == "direct" else 0)
+
+
 def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out, norms, workspace,
-          stream, time_kernels: bool):
+          stream, flags: int):
     import torch
     if q.dim() != 5:
         raise ValueError("q, k, v must be [B, H, T, S, D]")
@@ -138,7 +147,7 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
     if gamma.shape != (B, H, T) or beta.shape != (B, H, T) or gamma.dtype != torch.float32 \
             or beta.dtype != torch.float32:
         raise ValueError("gamma and beta must be float32 [B, H, T]")
-    desc = make_desc(B, H, T, S, D, io, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
+    desc = make_desc(B, H, T, S, D, io, beta_mode, flags)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
@@ -158,9 +167,10 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
 
 def frame_forward(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None, state_out=None,
                   norms=None, want_state=True, want_norms=False, workspace=None, stream=None,
-                  time_kernels=False):
+                  time_kernels=False, path="auto"):
     """Whole-sequence forward.  q, k, v [B,H,T,S,D] (bf16 or fp32), gamma/beta [B,H,T] fp32,
-    state [B,H,D,D] fp32 or None (zeros).  Returns (o, state_out, norms)."""
+    state [B,H,D,D] fp32 or None (zeros).  path="direct" selects the single-pass
+    recurrence for bf16 (GDN_FLAG_DIRECT).  Returns (o, state_out, norms)."""
     import torch
     B, H, T, S, D = q.shape
     if state_out is None and want_state:
@@ -168,12 +178,12 @@ def frame_forward(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None,
     if norms is None and want_norms:
         norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     out = _call("gdn_frame_forward", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
-                workspace, stream, time_kernels)
+                workspace, stream, _flags(path, time_kernels))
     return out, state_out, norms
 
 
 def frame_step(q, k, v, gamma, beta, state, beta_mode="erase", out=None, state_out=None, norms=None,
-               commit="new", workspace=None, stream=None, time_kernels=False):
+               commit="new", workspace=None, stream=None, time_kernels=False, path="auto"):
     """One chunk of a chunk-causal rollout; `state` [B,H,D,D] fp32 is required.
 
     commit: "new" -> the updated state goes to a new tensor (or `state_out`);
@@ -191,5 +201,5 @@ def frame_step(q, k, v, gamma, beta, state, beta_mode="erase", out=None, state_o
     elif state_out is None:
         state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     out = _call("gdn_frame_step", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
-                workspace, stream, time_kernels)
+                workspace, stream, _flags(path, time_kernels))
     return out, state_out, norms

@@ -37,9 +37,10 @@ using gdn::kMaxFramesPerLaunch;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
+  bool gram;                      // bf16 Gram pipeline (else the single-pass recurrence)
   size_t bh, esz, nb;
   size_t io_bytes, gb_bytes, state_bytes;
-  size_t carrier, snap_frame, norm_frame;
+  size_t carrier, snap_frame, norm_frame, gfr_frame, bfr_frame;
 };
 
 // Shapes already validated.
@@ -52,13 +53,20 @@ Plan make_plan(const gdn_desc* d) {
   p.gb_bytes = p.bh * (size_t)d->T * 4;
   p.state_bytes = p.bh * (size_t)d->D * (size_t)d->D * 4;
   p.carrier = round_up(p.state_bytes);
+  p.gram = d->io_dtype == GDN_BF16 && !(d->flags & GDN_FLAG_DIRECT);
   p.snap_frame = p.bh * (size_t)d->D * (size_t)d->D * p.esz;
-  p.norm_frame = p.bh * p.nb * 4;
+  // per-frame staging: the single-pass recurrence writes fp32 norm partials,
+  // the Gram pipeline writes G_t and B_t (the readout takes norms from the
+  // snapshots)
+  p.norm_frame = p.gram ? 0 : p.bh * p.nb * 4;
+  p.gfr_frame = p.gram ? p.bh * gdn::gram_frame_bytes(d->D) : 0;
+  p.bfr_frame = p.gram ? p.bh * gdn::input_frame_bytes(d->D) : 0;
   return p;
 }
 
 size_t ws_bytes_for(const Plan& p, size_t frames) {
-  return p.carrier + round_up(frames * p.snap_frame) + round_up(frames * p.norm_frame);
+  return p.carrier + round_up(frames * p.snap_frame) + round_up(frames * p.norm_frame) +
+         round_up(frames * p.gfr_frame) + round_up(frames * p.bfr_frame);
 }
 
 gdn_status check_desc(const gdn_desc* d) {
@@ -69,7 +77,8 @@ gdn_status check_desc(const gdn_desc* d) {
     return fail(GDN_ERR_DTYPE, "io_dtype %d is not GDN_F32 or GDN_BF16", d->io_dtype);
   if (d->beta_mode != GDN_BETA_ERASE && d->beta_mode != GDN_BETA_WRITE)
     return fail(GDN_ERR_DTYPE, "beta_mode %d is not GDN_BETA_ERASE or GDN_BETA_WRITE", d->beta_mode);
-  if (d->flags & ~GDN_FLAG_TIME_KERNELS) return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(GDN_FLAG_TIME_KERNELS | GDN_FLAG_DIRECT))
+    return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->S < 1 || d->D < 1)
     return fail(GDN_ERR_SHAPE, "B=%d H=%d T=%d S=%d D=%d: every size must be >= 1", d->B, d->H, d->T, d->S, d->D);
   if (d->D % 16 != 0 || d->D > 128)
@@ -93,13 +102,17 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool misaligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
 
+// Events around the kernels of one range of frames: kernel i ran between
+// ev[i] and ev[i + 1] and is booked under slot[i].
 struct TimedLaunch {
-  hipEvent_t ev[3];
+  hipEvent_t ev[4];
+  int slot[3];
+  int nk;
 };
 std::mutex g_time_mu;
 std::vector<TimedLaunch> g_timed;
-double g_time_ms[2] = {0.0, 0.0};
-int64_t g_time_n[2] = {0, 0};
+double g_time_ms[GDN_KERNEL_SLOTS] = {};
+int64_t g_time_n[GDN_KERNEL_SLOTS] = {};
 
 gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
                const float* beta, const float* state_in, void* o, float* state_out, float* norms,
@@ -108,7 +121,6 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
                                  workspace_bytes, is_step);
   if (st != GDN_OK) return st;
   const Plan p = make_plan(d);
-  const bool bf16 = d->io_dtype == GDN_BF16;
   // Largest frame count per launch whose staging fits the workspace (the
   // minimum-size check guarantees that one frame fits).
   size_t frames = std::min<size_t>((size_t)d->T, (size_t)kMaxFramesPerLaunch);
@@ -122,44 +134,75 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
   }
 
   unsigned char* ws = (unsigned char*)workspace;
-  float* carrier = (float*)ws;
-  void* snap = ws + p.carrier;
-  float* norm_part = (float*)(ws + p.carrier + round_up(frames * p.snap_frame));
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { void* r = ws + off; off += round_up(bytes); return r; };
+  float* carrier = (float*)carve(p.carrier);
+  void* snap = carve(frames * p.snap_frame);
+  float* norm_part = (float*)carve(frames * p.norm_frame);
+  void* gfr = carve(frames * p.gfr_frame);
+  void* bfr = carve(frames * p.bfr_frame);
 
   // The state travels between launches through state_out when the caller gave
   // one (in-place per workgroup tile), else through the workspace carrier.
   float* hand = state_out ? state_out : carrier;
-  const float kscale = (float)(1.0 / std::sqrt((double)d->D * (double)d->S));
+  const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
   const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
   hipStream_t s = (hipStream_t)stream;
 
   for (int t0 = 0; t0 < d->T; t0 += (int)frames) {
     const int tc = (int)std::min<size_t>(frames, (size_t)(d->T - t0));
     const bool last = t0 + tc >= d->T;
-    gdn::RecurArgs ra;
-    ra.k = k; ra.v = v; ra.gamma = gamma; ra.beta = beta;
-    ra.state_src = (t0 == 0) ? state_in : hand;
-    ra.state_dst = last ? state_out : hand;
-    ra.snap = snap;
-    ra.norm_part = norms ? norm_part : nullptr;
-    ra.units = (int)(p.bh * p.nb);
-    ra.T = d->T; ra.S = d->S; ra.t0 = t0; ra.Tc = tc;
-    ra.beta_mode = d->beta_mode;
-    ra.kscale = kscale;
+    const float* src = (t0 == 0) ? state_in : hand;
+    float* dst = last ? state_out : hand;
     gdn::ReadoutArgs ro;
-    ro.q = q; ro.o = o; ro.snap = snap; ro.norm_part = ra.norm_part; ro.norms = norms;
+    ro.q = q; ro.o = o; ro.snap = snap; ro.norms = norms;
+    ro.norm_part = (norms && !p.gram) ? norm_part : nullptr;
     ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
 
-    TimedLaunch tl;
+    TimedLaunch tl{};
+    tl.nk = p.gram ? 3 : 2;
+    if (p.gram) { tl.slot[0] = GDN_KERNEL_GRAM; tl.slot[1] = GDN_KERNEL_STATE; tl.slot[2] = GDN_KERNEL_READOUT; }
+    else { tl.slot[0] = GDN_KERNEL_RECURRENCE; tl.slot[1] = GDN_KERNEL_READOUT; }
     if (timed) {
-      for (int i = 0; i < 3; ++i) {
+      for (int i = 0; i <= tl.nk; ++i) {
         hipError_t e = hipEventCreate(&tl.ev[i]);
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
       }
     }
-    hipError_t e = gdn::launch_chunk(d->D, bf16, ra, ro, s, timed ? tl.ev : nullptr);
-    if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1,
-                                     hipGetErrorString(e));
+    int ki = 0;
+    auto mark = [&]() -> hipError_t { return timed ? hipEventRecord(tl.ev[ki++], s) : hipSuccess; };
+    hipError_t e = mark();
+    if (p.gram) {
+      gdn::GramArgs ga;
+      ga.k = k; ga.v = v; ga.gfr = gfr; ga.bfr = bfr;
+      ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
+      ga.kscale = (float)c; ga.kscale2 = (float)(c * c);
+      gdn::StateArgs sa;
+      sa.gfr = gfr; sa.bfr = bfr; sa.gamma = gamma; sa.beta = beta;
+      sa.state_src = src; sa.state_dst = dst; sa.snap = snap;
+      sa.BH = (int)p.bh; sa.T = d->T; sa.t0 = t0; sa.Tc = tc; sa.beta_mode = d->beta_mode;
+      if (e == hipSuccess) e = gdn::launch_gram(d->D, ga, s);
+      if (e == hipSuccess) e = mark();
+      if (e == hipSuccess) e = gdn::launch_state(d->D, sa, s);
+    } else {
+      gdn::RecurArgs ra;
+      ra.k = k; ra.v = v; ra.gamma = gamma; ra.beta = beta;
+      ra.state_src = src; ra.state_dst = dst; ra.snap = snap;
+      ra.norm_part = (norms && !p.gram) ? norm_part : nullptr;
+      ra.units = (int)(p.bh * p.nb);
+      ra.T = d->T; ra.S = d->S; ra.t0 = t0; ra.Tc = tc;
+      ra.beta_mode = d->beta_mode;
+      ra.kscale = (float)c;
+      if (e == hipSuccess) e = gdn::launch_recurrence(d->D, p.esz == 2, ra, s);
+    }
+    if (e == hipSuccess) e = mark();
+    if (e == hipSuccess) e = gdn::launch_readout(d->D, p.esz == 2, ro, s);
+    if (e == hipSuccess) e = mark();
+    if (e != hipSuccess) {
+      if (timed)
+        for (int i = 0; i <= tl.nk; ++i) (void)hipEventDestroy(tl.ev[i]);
+      return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1, hipGetErrorString(e));
+    }
     if (timed) {
       std::lock_guard<std::mutex> lk(g_time_mu);
       g_timed.push_back(tl);
@@ -260,26 +303,29 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
              stream, 1);
 }
 
-gdn_status gdn_kernel_times(double ms_out[2], int64_t launches_out[2], int reset) {
+gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_out[GDN_KERNEL_SLOTS],
+                            int reset) {
   std::lock_guard<std::mutex> lk(g_time_mu);
   gdn_status st = GDN_OK;
   for (TimedLaunch& tl : g_timed) {
-    float a = 0.f, b = 0.f;
-    hipError_t e = hipEventSynchronize(tl.ev[2]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&a, tl.ev[0], tl.ev[1]);
-    if (e == hipSuccess) e = hipEventElapsedTime(&b, tl.ev[1], tl.ev[2]);
-    if (e != hipSuccess) {
-      st = fail(GDN_ERR_HIP, "kernel timing: %s", hipGetErrorString(e));
-    } else {
-      g_time_ms[0] += a; g_time_ms[1] += b;
-      g_time_n[0] += 1; g_time_n[1] += 1;
+    hipError_t e = hipEventSynchronize(tl.ev[tl.nk]);
+    for (int i = 0; i < tl.nk && e == hipSuccess; ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, tl.ev[i], tl.ev[i + 1]);
+      if (e == hipSuccess) {
+        g_time_ms[tl.slot[i]] += ms;
+        g_time_n[tl.slot[i]] += 1;
+      }
     }
-    for (int i = 0; i < 3; ++i) (void)hipEventDestroy(tl.ev[i]);
+    if (e != hipSuccess) st = fail(GDN_ERR_HIP, "kernel timing: %s", hipGetErrorString(e));
+    for (int i = 0; i <= tl.nk; ++i) (void)hipEventDestroy(tl.ev[i]);
   }
   g_timed.clear();
-  if (ms_out) { ms_out[0] = g_time_ms[0]; ms_out[1] = g_time_ms[1]; }
-  if (launches_out) { launches_out[0] = g_time_n[0]; launches_out[1] = g_time_n[1]; }
-  if (reset) { g_time_ms[0] = g_time_ms[1] = 0.0; g_time_n[0] = g_time_n[1] = 0; }
+  for (int i = 0; i < GDN_KERNEL_SLOTS; ++i) {
+    if (ms_out) ms_out[i] = g_time_ms[i];
+    if (launches_out) launches_out[i] = g_time_n[i];
+    if (reset) { g_time_ms[i] = 0.0; g_time_n[i] = 0; }
+  }
   return st;
 }
 

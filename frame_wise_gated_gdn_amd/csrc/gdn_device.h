@@ -1,0 +1,100 @@
+// Device helpers shared by the gfx950 kernels of the frame-wise GDN path:
+// vector types, MFMA wrappers, bf16 packing, ReLU on packed bf16, LDS
+// transposed reads, buffer resources with out-of-range offsets and an
+// LDS-only workgroup barrier.
+//
+// MFMA lane layouts used (gfx950, wave64; l = lane, g = l/16):
+//   v_mfma_f32_16x16x32_bf16: A lane holds row l%16, k = 8g..8g+7;
+//                             B lane holds col l%16, k = 8g..8g+7;
+//                             C lane holds col l%16, rows 4g..4g+3.
+//   v_mfma_f32_16x16x4_f32:   A row l%16, k = g; B col l%16, k = g; C as above.
+//   ds_read_b64_tr_b16: in each 16-lane group, lane j supplies the address of
+//   4 consecutive 16-bit values (row j/4, columns 4(j%4)..+3 of a 4 x 16 block);
+//   lane i receives column i (rows 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ReLU on two packed bf16: a negative bf16 has its sign bit set, i.e. it is a
+// negative int16, so an int16 max with 0 zeroes it and keeps the rest.
+__device__ __forceinline__ uint32_t relu2(uint32_t x) {
+  i16x2 v = __builtin_bit_cast(i16x2, x);
+  i16x2 z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, z));
+}
+__device__ __forceinline__ u32x4 relu8(u32x4 x) {
+  return u32x4{relu2(x[0]), relu2(x[1]), relu2(x[2]), relu2(x[3])};
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 8-byte transposed LDS read (see header comment for the lane mapping).
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Wave-local LDS ordering: LDS operations of one wave complete in order; the
+// fence stops the compiler from moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Pack two floats into two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// XCD-aware unit for this workgroup: units are split into 8 contiguous ranges,
+// range x is served by the workgroups that land on XCD x (ids = x mod 8).
+__device__ __forceinline__ int xcd_unit(int units) {
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int start = (int)(((long long)x * units) >> 3);
+  const int end = (int)(((long long)(x + 1) * units) >> 3);
+  return (start + slot < end) ? start + slot : -1;
+}
+
+constexpr uint32_t kOOB = 0x80000000u;      // offset past every buffer (buffers are < 2 GiB)
+constexpr int kBufWord3 = 0x00020000;       // gfx9 buffer descriptor word 3 (raw 32-bit dwords)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
+// its outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace gdn

@@ -30,17 +30,42 @@ struct ReadoutArgs {
   const void* q;            // [BH][T][S][D]
   void* o;                  // [BH][T][S][D]
   const void* snap;         // as in RecurArgs
-  const float* norm_part;   // as in RecurArgs, or nullptr
+  const float* norm_part;   // as in RecurArgs; nullptr: norms from the bf16 snapshot
   float* norms;             // [BH][T] or nullptr
   int BH, T, S, t0, Tc;
 };
 
-// Enqueue recurrence + readout for one range of frames.  `ev`, when not null,
-// holds three events recorded before, between and after the two kernels.
-hipError_t launch_chunk(int D, bool bf16, const RecurArgs& ra, const ReadoutArgs& ro,
-                        hipStream_t stream, hipEvent_t* ev);
+// Gram pass (bf16 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
+struct GramArgs {
+  const void* k;            // [BH][T][S][D] bf16
+  const void* v;            // [BH][T][S][D] bf16
+  void* gfr;                // [BH][Tc] x gram_frame_bytes(D): G as state-pass A operands
+  void* bfr;                // [BH][Tc] x input_frame_bytes(D): B in accumulator layout
+  int BH, T, S, t0, Tc;
+  float kscale, kscale2;    // 1/sqrt(D*S) and 1/(D*S), each rounded once to fp32
+};
 
-// Dynamic LDS bytes of the recurrence kernel for (D, dtype).
-size_t recur_lds_bytes(int D, bool bf16);
+// State pass (bf16 I/O): the serial frame loop over G and B.
+struct StateArgs {
+  const void* gfr;          // as in GramArgs
+  const void* bfr;          // as in GramArgs
+  const float* gamma;       // [BH][T]
+  const float* beta;        // [BH][T]
+  const float* state_src;   // [BH][D][D] or nullptr (zero state)
+  float* state_dst;         // [BH][D][D] or nullptr
+  void* snap;               // [BH][Tc][D][D] bf16 snapshots, transposed ([value][key])
+  int BH, T, t0, Tc;
+  int beta_mode;            // 0 ERASE, 1 WRITE
+};
+
+// Kernel launchers (enqueue only).  D in {16, ..., 128}.
+hipError_t launch_recurrence(int D, bool bf16, const RecurArgs& ra, hipStream_t stream);
+hipError_t launch_readout(int D, bool bf16, const ReadoutArgs& ro, hipStream_t stream);
+hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream);
+hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream);
+
+// Workspace bytes per (head, frame) of the Gram pass outputs.
+size_t gram_frame_bytes(int D);
+size_t input_frame_bytes(int D);
 
 }  // namespace gdn

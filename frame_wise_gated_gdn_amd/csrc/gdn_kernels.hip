@@ -24,86 +24,18 @@
 // the 8 XCDs round-robin by id), so the re-reads of a frame's keys by the
 // head's column tiles hit that XCD's L2.
 //
-// MFMA lane layouts used (gfx950, wave64; l = lane, g = l/16):
-//   v_mfma_f32_16x16x32_bf16: A lane holds row l%16, k = 8g..8g+7;
-//                             B lane holds col l%16, k = 8g..8g+7;
-//                             C lane holds col l%16, rows 4g..4g+3.
-//   v_mfma_f32_16x16x4_f32:   A row l%16, k = g; B col l%16, k = g; C as above.
-//   ds_read_b64_tr_b16: in each 16-lane group, lane j supplies the address of
-//   4 consecutive 16-bit values (row j/4, columns 4(j%4)..+3 of a 4 x 16 block);
-//   lane i receives column i (rows 0..3).
+// MFMA and LDS lane layouts are listed in gdn_device.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kWaves = 8;          // waves per recurrence workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kReadWaves = 4;      // waves per readout workgroup
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// ReLU on two packed bf16: a negative bf16 has its sign bit set, i.e. it is a
-// negative int16, so an int16 max with 0 zeroes it and keeps the rest.
-__device__ __forceinline__ uint32_t relu2(uint32_t x) {
-  i16x2 v = __builtin_bit_cast(i16x2, x);
-  i16x2 z = {0, 0};
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, z));
-}
-__device__ __forceinline__ u32x4 relu8(u32x4 x) {
-  return u32x4{relu2(x[0]), relu2(x[1]), relu2(x[2]), relu2(x[3])};
-}
-__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// 8-byte transposed LDS read (see header comment for the lane mapping).
-__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// Wave-local LDS ordering: LDS operations of one wave complete in order; the
-// fence stops the compiler from moving LDS accesses across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Pack two floats into two bf16 (round to nearest even).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  bf2 r = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// XCD-aware unit for this workgroup: units are split into 8 contiguous ranges,
-// range x is served by the workgroups that land on XCD x (ids = x mod 8).
-__device__ __forceinline__ int xcd_unit(int units) {
-  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int start = (int)(((long long)x * units) >> 3);
-  const int end = (int)(((long long)(x + 1) * units) >> 3);
-  return (start + slot < end) ? start + slot : -1;
-}
 
 // ----------------------------------------------------------------------------
 // Recurrence kernel.
@@ -366,22 +298,6 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_kernel(RecurArgs a) {
 // The per-frame barriers only wait for LDS traffic, never for the prefetches.
 // ----------------------------------------------------------------------------
 constexpr int kRing = 4;
-constexpr uint32_t kOOB = 0x80000000u;      // offset past every buffer (buffers are < 2 GiB)
-constexpr int kBufWord3 = 0x00020000;       // gfx9 buffer descriptor word 3 (raw 32-bit dwords)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
-// its outstanding global loads.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // The values enter the prediction MFMA as extra k-slots: the A operand of the
 // last k-chunk carries the 16 value columns of the tile in lanes g = 2, 3 and
@@ -787,7 +703,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
   const int nchunk = (S + 31) / 32;
   const int NC = (nchunk + kReadWaves - 1) / kReadWaves;     // chunk slots per wave
 
-  if (a.norms && tid == 0) {
+  if (a.norms && a.norm_part && tid == 0) {
     float sq = 0.f;
     for (int j = 0; j < NB; ++j) sq += a.norm_part[((size_t)bh * a.Tc + tl) * NB + j];
     a.norms[(size_t)bh * T + t] = sqrtf(sq);
@@ -820,6 +736,23 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
   // The snapshot loads were issued first: one use of the last of them makes
   // the compiler wait for all of them here, once, instead of inside the loop.
   asm volatile("" ::"v"(A[NB - 1][NKC - 1]));
+  if (a.norms && !a.norm_part && w == 0) {
+    // state norm from the bf16 snapshot: each element of M_t sits in exactly
+    // one lane of one fragment of every wave
+    float sq = 0.f;
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = bf16_lo_f32(A[jb][kc][e]), y = bf16_hi_f32(A[jb][kc][e]);
+          sq += x * x + y * y;
+        }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) sq += __shfl_xor(sq, s, 64);
+    if (l == 0) a.norms[(size_t)bh * T + t] = sqrtf(sq);
+  }
 
   for (int base = 0; base < NC; base += kReadRing) {
 #pragma unroll
@@ -866,8 +799,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
 // Launchers.
 // ----------------------------------------------------------------------------
 template <int D, bool BF16>
-static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStream_t stream,
-                              hipEvent_t* ev) {
+static hipError_t launch_recurrence_t(const RecurArgs& ra, hipStream_t stream) {
   using Sh = RecurShape<D, BF16>;
   static bool attr_set = false;   // benign race: every setter writes the same value
   if (!attr_set) {
@@ -883,18 +815,9 @@ static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStr
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
     }
     if (e != hipSuccess) return e;
-    if constexpr (BF16) {
-      e = hipFuncSetAttribute((const void*)gdn_readout_bf16_kernel<D>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
-    } else {
-      e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, BF16>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
-    }
-    if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int grid = 8 * ((ra.units + 7) / 8);
-  if (ev) { hipError_t e = hipEventRecord(ev[0], stream); if (e != hipSuccess) return e; }
   if constexpr (BF16) {
     if (ra.beta_mode == 0)
       hipLaunchKernelGGL((gdn_recur_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), BfShape<D>::lds_bytes,
@@ -905,9 +828,24 @@ static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStr
   } else {
     hipLaunchKernelGGL((gdn_recur_kernel<D, BF16>), dim3(grid), dim3(kThreads), Sh::lds_bytes, stream, ra);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) { e = hipEventRecord(ev[1], stream); if (e != hipSuccess) return e; }
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e;
+    if constexpr (BF16) {
+      e = hipFuncSetAttribute((const void*)gdn_readout_bf16_kernel<D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
+    } else {
+      e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
+    }
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   if constexpr (BF16) {
     hipLaunchKernelGGL((gdn_readout_bf16_kernel<D>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
                        ReadShape<D>::lds_bytes, stream, ro);
@@ -915,34 +853,28 @@ static hipError_t launch_pair(const RecurArgs& ra, const ReadoutArgs& ro, hipStr
     hipLaunchKernelGGL((gdn_readout_kernel<D, BF16>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
                        (size_t)D * (D + 1) * 4, stream, ro);
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) { e = hipEventRecord(ev[2], stream); if (e != hipSuccess) return e; }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
-hipError_t launch_chunk(int D, bool bf16, const RecurArgs& ra, const ReadoutArgs& ro,
-                        hipStream_t stream, hipEvent_t* ev) {
-#define GDN_CASE(DD)                                                          \
-  case DD:                                                                    \
-    return bf16 ? launch_pair<DD, true>(ra, ro, stream, ev)                   \
-                : launch_pair<DD, false>(ra, ro, stream, ev);
-  switch (D) {
-    GDN_CASE(16) GDN_CASE(32) GDN_CASE(48) GDN_CASE(64)
-    GDN_CASE(80) GDN_CASE(96) GDN_CASE(112) GDN_CASE(128)
-    default: return hipErrorInvalidValue;
+#define GDN_DISPATCH2(FN, ARGS)                                                                  \
+  switch (D) {                                                                                   \
+    case 16: return bf16 ? FN<16, true> ARGS : FN<16, false> ARGS;                               \
+    case 32: return bf16 ? FN<32, true> ARGS : FN<32, false> ARGS;                               \
+    case 48: return bf16 ? FN<48, true> ARGS : FN<48, false> ARGS;                               \
+    case 64: return bf16 ? FN<64, true> ARGS : FN<64, false> ARGS;                               \
+    case 80: return bf16 ? FN<80, true> ARGS : FN<80, false> ARGS;                               \
+    case 96: return bf16 ? FN<96, true> ARGS : FN<96, false> ARGS;                               \
+    case 112: return bf16 ? FN<112, true> ARGS : FN<112, false> ARGS;                            \
+    case 128: return bf16 ? FN<128, true> ARGS : FN<128, false> ARGS;                            \
+    default: return hipErrorInvalidValue;                                                        \
   }
-#undef GDN_CASE
-}
 
-size_t recur_lds_bytes(int D, bool bf16) {
-#define GDN_LDS(DD) case DD: return bf16 ? RecurShape<DD, true>::lds_bytes : RecurShape<DD, false>::lds_bytes;
-  switch (D) {
-    GDN_LDS(16) GDN_LDS(32) GDN_LDS(48) GDN_LDS(64)
-    GDN_LDS(80) GDN_LDS(96) GDN_LDS(112) GDN_LDS(128)
-    default: return 0;
-  }
-#undef GDN_LDS
+hipError_t launch_recurrence(int D, bool bf16, const RecurArgs& ra, hipStream_t stream) {
+  GDN_DISPATCH2(launch_recurrence_t, (ra, stream))
 }
+hipError_t launch_readout(int D, bool bf16, const ReadoutArgs& ro, hipStream_t stream) {
+  GDN_DISPATCH2(launch_readout_t, (ro, stream))
+}
+#undef GDN_DISPATCH2
 
 }  // namespace gdn

@@ -44,7 +44,8 @@
  *   - Shapes: B, H, T, S >= 1; D in {16, 32, 48, ..., 128}; the element counts
  *     must fit the kernels' 32-bit per-head indexing (T*S*D < 2^31).
  *   - Determinism: results do not depend on the workspace size or on how the
- *     frames are split across calls; the same inputs give the same bits.
+ *     frames are split across calls; the same inputs and flags give the same
+ *     bits.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -80,6 +81,22 @@ typedef enum gdn_status {
 
 /* Record device time per kernel on `stream` (read back with gdn_kernel_times). */
 #define GDN_FLAG_TIME_KERNELS 0x1u
+/*
+ * bf16 I/O only: run the single-pass recurrence (keys and values streamed by
+ * every value-column tile of the state, the state product in the same sweep)
+ * instead of the default Gram pipeline (frame-parallel G_t = Kf^T Kf and
+ * B_t = Kf^T V, then a serial D x D state pass).  Slower; needs no G/B
+ * staging in the workspace.  The two agree to rounding, not bitwise.  fp32 I/O
+ * always runs the single-pass recurrence.
+ */
+#define GDN_FLAG_DIRECT 0x2u
+
+/* Kernel kinds booked by gdn_kernel_times. */
+#define GDN_KERNEL_RECURRENCE 0 /* single-pass recurrence */
+#define GDN_KERNEL_READOUT 1    /* O_t = Qf M_t from the per-frame state snapshots */
+#define GDN_KERNEL_GRAM 2       /* Gram pass: G_t, B_t per (head, frame) */
+#define GDN_KERNEL_STATE 3      /* serial state pass over G_t, B_t */
+#define GDN_KERNEL_SLOTS 4
 
 typedef struct gdn_desc {
   int32_t abi_version; /* GDN_ABI_VERSION */
@@ -149,12 +166,13 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
 
 /*
  * Device time of the kernels launched by calls that set GDN_FLAG_TIME_KERNELS
- * since the last reset: per kernel kind (0 = recurrence, 1 = readout) the total
- * milliseconds and the number of launches.  Synchronises with the recorded
- * events.  `reset` != 0 clears the record after reading.  Returns GDN_OK or
- * GDN_ERR_HIP.
+ * since the last reset: per kernel kind (GDN_KERNEL_*) the total milliseconds
+ * and the number of launches.  Either pointer may be NULL.  Synchronises with
+ * the recorded events.  `reset` != 0 clears the record after reading.
+ * Returns GDN_OK or GDN_ERR_HIP.
  */
-gdn_status gdn_kernel_times(double ms_out[2], int64_t launches_out[2], int reset);
+gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_out[GDN_KERNEL_SLOTS],
+                            int reset);
 
 #ifdef __cplusplus
 }

@@ -3,7 +3,9 @@
 Bar (relative Frobenius error over the compared tensor): 1e-4 for fp32 I/O,
 2e-2 for bf16 I/O, the same for the final state.  Chunked streaming must equal
 the one-shot forward bitwise, and the result must not depend on the workspace
-size or on the run.
+size or on the run.  bf16 I/O has two paths: the default Gram pipeline
+(path="auto") and the single-pass recurrence (path="direct"); both are held to
+the same bar.
 """
 import json
 import os
@@ -111,27 +113,31 @@ def test_worked_examples_exact_fp32(env, mode, idx):
 
 
 # ------------------------------------------------------------------ small sweeps
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+DTYPE_PATHS = [("f32", "auto"), ("bf16", "auto"), ("bf16", "direct")]
+
+
+@pytest.mark.parametrize("dtype,path", DTYPE_PATHS)
 @pytest.mark.parametrize("D", [16, 32, 48, 64, 80, 96, 112, 128])
-def test_head_dims_ragged_tokens(env, dtype, D):
+def test_head_dims_ragged_tokens(env, dtype, path, D):
     torch, gdn, wl, go = env
     w = wl.Workload("sweep", 1, 3, 5, 77, D, dtype=dtype, gamma=(0.8, 1.0), beta=(0.0, 1.0))
     inp = gen(env, w)
-    out, st, nm = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True)
+    out, st, nm = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True,
+                                    path=path)
     torch.cuda.synchronize()
     check(env, inp, out, st, run_oracle(env, inp, want_norms=True), TOL[dtype], norms=nm)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype,path", DTYPE_PATHS)
 @pytest.mark.parametrize("S", [1, 15, 16, 31, 32, 33, 257])
 @pytest.mark.parametrize("mode", ["erase", "write"])
-def test_token_counts_and_modes(env, dtype, S, mode):
+def test_token_counts_and_modes(env, dtype, path, S, mode):
     torch, gdn, wl, go = env
     w = wl.Workload("tok", 2, 2, 6, S, 32, dtype=dtype, gamma=(0.7, 1.0), beta=(0.0, 1.0))
     inp = gen(env, w)
     state = torch.randn((2, 2, 32, 32), generator=torch.Generator().manual_seed(5)).cuda()
     out, st, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], state=state,
-                                   beta_mode=mode)
+                                   beta_mode=mode, path=path)
     torch.cuda.synchronize()
     check(env, inp, out, st, run_oracle(env, inp, mode=mode, state=state), TOL[dtype])
 
@@ -145,27 +151,40 @@ def test_tiny_config_fp32(env):
     assert worst < 1e-5
 
 
-def test_short_clip_config_all_heads(env):
+@pytest.mark.parametrize("path", ["auto", "direct"])
+def test_short_clip_config_all_heads(env, path):
     torch, gdn, wl, go = env
     inp = gen(env, wl.SHORT)
-    out, st, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    out, st, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], path=path)
     torch.cuda.synchronize()
     check(env, inp, out, st, run_oracle(env, inp), TOL["bf16"])
 
 
+def test_gram_and_direct_paths_agree(env):
+    """The two bf16 paths compute the same recurrence with different roundings."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.SHORT.with_(H=4))
+    a = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True)
+    b = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True, path="direct")
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert rel(to_f64(torch, x), to_f64(torch, y)) < 1e-2
+
+
 # ------------------------------------------------------------------ streaming
-def test_chunked_rollout_equals_one_shot_bitwise(env):
+@pytest.mark.parametrize("path", ["auto", "direct"])
+def test_chunked_rollout_equals_one_shot_bitwise(env, path):
     torch, gdn, wl, go = env
     w = wl.CHUNKED
     inp = gen(env, w)
-    out1, st1, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    out1, st1, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], path=path)
     B, H, T, S, D = inp["q"].shape
     state = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
     outs = []
     for t0 in range(0, T, w.chunk):                 # 20 chunks of 4 frames and a tail of 1
         sl = slice(t0, min(T, t0 + w.chunk))
         o, _, _ = gdn.frame_step(*(inp[n][:, :, sl].contiguous() for n in ("q", "k", "v", "gamma", "beta")),
-                                 state, commit="inplace")
+                                 state, commit="inplace", path=path)
         outs.append(o)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(outs, dim=2), out1)
