@@ -261,7 +261,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
       make_rsrc((unsigned char*)a.snap + (size_t)bh * Tc * D * D * 2, (uint32_t)(Tc * D * D * 2));
   const uint32_t gbase = (uint32_t)(I * NKC * 1024 + l * 16);
   const uint32_t bbase = (uint32_t)((j * NB + I) * 512 + l * 8);
-  const uint32_t sbase = (uint32_t)((col * D + row0) * 2);
+  const uint32_t sbase = (uint32_t)(((j * NB + I) * 64 + l) * 8);
 
   u32x4 Gf[kStateRing][NKC];
   u32x2 Bf[kStateRing];
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
       }
       load_frame(f + kStateRing, r);
       const u32x2 pub = publish((r & 1) ^ 1, m);
-      // snapshot of M_t^T (value-major rows), 4 consecutive keys per lane
+      // bf16 snapshot of M_t: this wave's block, lane-linear (512 contiguous bytes)
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pub), srs,
                                             ok ? sbase + (uint32_t)f * (uint32_t)(D * D * 2) : kOOB, 0, 0);
       lds_barrier();

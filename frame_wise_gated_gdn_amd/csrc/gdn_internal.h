@@ -18,7 +18,9 @@ struct RecurArgs {
   const float* beta;        // [BH][T]
   const float* state_src;   // [BH][D][D] or nullptr (zero state)
   float* state_dst;         // [BH][D][D] or nullptr
-  void* snap;               // [BH][Tc][D][D] state snapshots, transposed ([value][key])
+  void* snap;               // per (head, frame) state snapshot: fp32 I/O [D][D] transposed
+                            // ([value][key]); bf16 I/O D*D bf16 as blocks [jt][I] of
+                            // 64 lanes x 4, lane (n, g) holding M[16I+4g+r][16jt+n]
   float* norm_part;         // [BH][Tc][D/16] or nullptr
   int units;                // BH * (D/16) workgroups with work
   int T, S, t0, Tc;
@@ -53,7 +55,7 @@ struct StateArgs {
   const float* beta;        // [BH][T]
   const float* state_src;   // [BH][D][D] or nullptr (zero state)
   float* state_dst;         // [BH][D][D] or nullptr
-  void* snap;               // [BH][Tc][D][D] bf16 snapshots, transposed ([value][key])
+  void* snap;               // as in RecurArgs (bf16 block layout)
   int BH, T, t0, Tc;
   int beta_mode;            // 0 ERASE, 1 WRITE
 };

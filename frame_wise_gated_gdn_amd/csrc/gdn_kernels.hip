@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
     if (w < NB) Mown = Mn;
     const u32x2 pk = {pack_bf16(Mn[0], Mn[1]), pack_bf16(Mn[2], Mn[3])};
     const uint32_t snap_off =
-        (uint32_t)(((size_t)(bh * a.Tc + tl) * D * D + (size_t)(j0 + n) * D + 16 * ob + 4 * g) * 2);
+        (uint32_t)((size_t)(bh * a.Tc + tl) * D * D * 2 + (size_t)((jt * NB + ob) * 64 + l) * 8);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), snaprs, w < NB ? snap_off : kOOB, 0, 0);
     const float s1 = pred_scale(tl + 1 < a.Tc ? tl + 1 : tl);
     const u32x2 pm = {pack_bf16(s1 * Mn[0], s1 * Mn[1]), pack_bf16(s1 * Mn[2], s1 * Mn[3])};
@@ -720,15 +720,19 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
     for (int j = 0; j < NLD; ++j) X[j] = buf_load16(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
   };
 
-  // A operands: M_t^T rows (value column 16jb + n), keys 32kc + 8g .. +7
-  const uint16_t* snap = (const uint16_t*)a.snap + ((size_t)bh * a.Tc + tl) * D * D;
+  // A operands: M_t^T rows (value column 16jb + n); k-step kc holds keys
+  // 32kc + 4g..+3 and 32kc + 16 + 4g..+3, i.e. the snapshot blocks (jb, 2kc)
+  // and (jb, 2kc + 1) of this lane
+  const unsigned char* snap = (const unsigned char*)a.snap + ((size_t)bh * a.Tc + tl) * D * D * 2;
   u32x4 A[NB][NKC];
 #pragma unroll
   for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      const int key = 32 * kc + 8 * g;
-      A[jb][kc] = (key < D) ? *(const u32x4*)(snap + (size_t)(16 * jb + n) * D + key) : u32x4{0u, 0u, 0u, 0u};
+      const u32x2 lo = *(const u32x2*)(snap + ((size_t)(jb * NB + 2 * kc) * 64 + l) * 8);
+      const u32x2 hi = (2 * kc + 1 < NB) ? *(const u32x2*)(snap + ((size_t)(jb * NB + 2 * kc + 1) * 64 + l) * 8)
+                                         : u32x2{0u, 0u};
+      A[jb][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   u32x4 X[kReadRing][NLD];
 #pragma unroll
@@ -772,8 +776,11 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
         u32x4 B[NKC];
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          B[kc] = u32x4{0u, 0u, 0u, 0u};
-          if (32 * kc + 8 * g < D) B[kc] = *(const u32x4*)(qs + (16 * half + n) * RS + 32 * kc + 8 * g);
+          // keys in the k-slot order of the A operands
+          const uint16_t* rp = qs + (16 * half + n) * RS + 32 * kc + 4 * g;
+          const u32x2 lo = *(const u32x2*)rp;
+          const u32x2 hi = (32 * kc + 32 <= D) ? *(const u32x2*)(rp + 16) : u32x2{0u, 0u};
+          B[kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
