@@ -102,17 +102,175 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 bool misaligned(const void* p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
 
-// Events around the kernels of one range of frames: kernel i ran between
-// ev[i] and ev[i + 1] and is booked under slot[i].
-struct TimedLaunch {
-  hipEvent_t ev[4];
-  int slot[3];
-  int nk;
+// ---------------------------------------------------------------------------
+// Kernel timing (GDN_FLAG_TIME_KERNELS): every timed kernel is bracketed by two
+// events on its own stream; gdn_kernel_times reads them and returns them to a
+// pool for reuse.
+// ---------------------------------------------------------------------------
+struct TimedKernel {
+  int slot;
+  hipEvent_t ev[2];
 };
 std::mutex g_time_mu;
-std::vector<TimedLaunch> g_timed;
+std::vector<TimedKernel> g_timed;          // recorded, not read yet
+std::vector<hipEvent_t> g_free_events;     // timing events ready for reuse
 double g_time_ms[GDN_KERNEL_SLOTS] = {};
 int64_t g_time_n[GDN_KERNEL_SLOTS] = {};
+
+hipError_t take_timing_event(hipEvent_t* e) {
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    if (!g_free_events.empty()) {
+      *e = g_free_events.back();
+      g_free_events.pop_back();
+      return hipSuccess;
+    }
+  }
+  return hipEventCreate(e);
+}
+
+void give_timing_event(hipEvent_t e) {
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  g_free_events.push_back(e);
+}
+
+// Enqueue one kernel (`fn` launches it on `s`), bracketed by timing events when
+// `timed`.
+template <class Fn>
+hipError_t launch_timed(bool timed, int slot, hipStream_t s, Fn&& fn) {
+  if (!timed) return fn();
+  TimedKernel tk{slot, {nullptr, nullptr}};
+  hipError_t e = take_timing_event(&tk.ev[0]);
+  if (e != hipSuccess) return e;
+  e = take_timing_event(&tk.ev[1]);
+  if (e != hipSuccess) { give_timing_event(tk.ev[0]); return e; }
+  e = hipEventRecord(tk.ev[0], s);
+  if (e == hipSuccess) e = fn();
+  if (e == hipSuccess) e = hipEventRecord(tk.ev[1], s);
+  if (e != hipSuccess) {
+    give_timing_event(tk.ev[0]);
+    give_timing_event(tk.ev[1]);
+    return e;
+  }
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  g_timed.push_back(tk);
+  return hipSuccess;
+}
+
+struct Ptrs {
+  const void *q, *k, *v;
+  const float *gamma, *beta, *state_in;
+  void* o;
+  float *state_out, *norms;
+};
+
+// Largest frame count per launch whose staging fits a workspace of `wb` bytes
+// (the minimum-size check guarantees that one frame fits).
+size_t frames_per_launch(const Plan& p, int T, size_t wb) {
+  size_t frames = std::min<size_t>((size_t)T, (size_t)kMaxFramesPerLaunch);
+  if (ws_bytes_for(p, frames) > wb) {
+    size_t lo = 1, hi = frames;           // ws_bytes_for(lo) fits, ws_bytes_for(hi) does not
+    while (hi - lo > 1) {
+      const size_t mid = lo + (hi - lo) / 2;
+      (ws_bytes_for(p, mid) <= wb ? lo : hi) = mid;
+    }
+    frames = lo;
+  }
+  return frames;
+}
+
+// Gram path: per range of frames, the gram pass, the serial state pass and
+// the readout, in that order on the caller's stream.  (Running the state pass
+// of one range concurrently with the HBM-bound passes of neighbouring ranges
+// on side streams was measured slower: the latency-bound state pass loses its
+// CUs to them, and the shorter launches pay their tails.)
+gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* workspace, size_t wb,
+                    hipStream_t s) {
+  const size_t F = frames_per_launch(p, d->T, wb);
+  unsigned char* ws = (unsigned char*)workspace;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { void* r = ws + off; off += round_up(bytes); return r; };
+  float* carrier = (float*)carve(p.carrier);
+  void* snap = carve(F * p.snap_frame);
+  carve(0);
+  void* gfr = carve(F * p.gfr_frame);
+  void* bfr = carve(F * p.bfr_frame);
+
+  // The state travels between launches through state_out when the caller gave
+  // one (in-place per workgroup tile), else through the workspace carrier.
+  float* hand = x.state_out ? x.state_out : carrier;
+  const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+
+  for (int t0 = 0; t0 < d->T; t0 += (int)F) {
+    const int tc = (int)std::min<size_t>(F, (size_t)(d->T - t0));
+    const bool last = t0 + tc >= d->T;
+    gdn::GramArgs ga;
+    ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
+    ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
+    ga.kscale = (float)c; ga.kscale2 = (float)(c * c);
+    gdn::StateArgs sa;
+    sa.gfr = gfr; sa.bfr = bfr; sa.gamma = x.gamma; sa.beta = x.beta;
+    sa.state_src = (t0 == 0) ? x.state_in : hand;
+    sa.state_dst = last ? x.state_out : hand;
+    sa.snap = snap;
+    sa.BH = (int)p.bh; sa.T = d->T; sa.t0 = t0; sa.Tc = tc; sa.beta_mode = d->beta_mode;
+    gdn::ReadoutArgs ro;
+    ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = nullptr;
+    ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
+    hipError_t e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(d->D, ga, s); });
+    if (e == hipSuccess)
+      e = launch_timed(timed, GDN_KERNEL_STATE, s, [&] { return gdn::launch_state(d->D, sa, s); });
+    if (e == hipSuccess)
+      e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_readout(d->D, true, ro, s); });
+    if (e != hipSuccess)
+      return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1, hipGetErrorString(e));
+  }
+  return GDN_OK;
+}
+
+gdn_status run_direct(const gdn_desc* d, const Plan& p, const Ptrs& x, void* workspace, size_t wb,
+                      hipStream_t s) {
+  const size_t frames = frames_per_launch(p, d->T, wb);
+  unsigned char* ws = (unsigned char*)workspace;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { void* r = ws + off; off += round_up(bytes); return r; };
+  float* carrier = (float*)carve(p.carrier);
+  void* snap = carve(frames * p.snap_frame);
+  float* norm_part = (float*)carve(frames * p.norm_frame);
+
+  // The state travels between launches through state_out when the caller gave
+  // one (in-place per workgroup tile), else through the workspace carrier.
+  float* hand = x.state_out ? x.state_out : carrier;
+  const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const bool bf16 = p.esz == 2;
+
+  for (int t0 = 0; t0 < d->T; t0 += (int)frames) {
+    const int tc = (int)std::min<size_t>(frames, (size_t)(d->T - t0));
+    const bool last = t0 + tc >= d->T;
+    gdn::RecurArgs ra;
+    ra.k = x.k; ra.v = x.v; ra.gamma = x.gamma; ra.beta = x.beta;
+    ra.state_src = (t0 == 0) ? x.state_in : hand;
+    ra.state_dst = last ? x.state_out : hand;
+    ra.snap = snap;
+    ra.norm_part = x.norms ? norm_part : nullptr;
+    ra.units = (int)(p.bh * p.nb);
+    ra.T = d->T; ra.S = d->S; ra.t0 = t0; ra.Tc = tc;
+    ra.beta_mode = d->beta_mode;
+    ra.kscale = (float)c;
+    gdn::ReadoutArgs ro;
+    ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = ra.norm_part;
+    ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
+    hipError_t e = launch_timed(timed, GDN_KERNEL_RECURRENCE, s,
+                                [&] { return gdn::launch_recurrence(d->D, bf16, ra, s); });
+    if (e == hipSuccess)
+      e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_readout(d->D, bf16, ro, s); });
+    if (e != hipSuccess)
+      return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1, hipGetErrorString(e));
+  }
+  return GDN_OK;
+}
 
 gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
                const float* beta, const float* state_in, void* o, float* state_out, float* norms,
@@ -121,94 +279,10 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
                                  workspace_bytes, is_step);
   if (st != GDN_OK) return st;
   const Plan p = make_plan(d);
-  // Largest frame count per launch whose staging fits the workspace (the
-  // minimum-size check guarantees that one frame fits).
-  size_t frames = std::min<size_t>((size_t)d->T, (size_t)kMaxFramesPerLaunch);
-  if (ws_bytes_for(p, frames) > workspace_bytes) {
-    size_t lo = 1, hi = frames;           // ws_bytes_for(lo) fits, ws_bytes_for(hi) does not
-    while (hi - lo > 1) {
-      const size_t mid = lo + (hi - lo) / 2;
-      (ws_bytes_for(p, mid) <= workspace_bytes ? lo : hi) = mid;
-    }
-    frames = lo;
-  }
-
-  unsigned char* ws = (unsigned char*)workspace;
-  size_t off = 0;
-  auto carve = [&](size_t bytes) { void* r = ws + off; off += round_up(bytes); return r; };
-  float* carrier = (float*)carve(p.carrier);
-  void* snap = carve(frames * p.snap_frame);
-  float* norm_part = (float*)carve(frames * p.norm_frame);
-  void* gfr = carve(frames * p.gfr_frame);
-  void* bfr = carve(frames * p.bfr_frame);
-
-  // The state travels between launches through state_out when the caller gave
-  // one (in-place per workgroup tile), else through the workspace carrier.
-  float* hand = state_out ? state_out : carrier;
-  const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
-  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const Ptrs x{q, k, v, gamma, beta, state_in, o, state_out, norms};
   hipStream_t s = (hipStream_t)stream;
-
-  for (int t0 = 0; t0 < d->T; t0 += (int)frames) {
-    const int tc = (int)std::min<size_t>(frames, (size_t)(d->T - t0));
-    const bool last = t0 + tc >= d->T;
-    const float* src = (t0 == 0) ? state_in : hand;
-    float* dst = last ? state_out : hand;
-    gdn::ReadoutArgs ro;
-    ro.q = q; ro.o = o; ro.snap = snap; ro.norms = norms;
-    ro.norm_part = (norms && !p.gram) ? norm_part : nullptr;
-    ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
-
-    TimedLaunch tl{};
-    tl.nk = p.gram ? 3 : 2;
-    if (p.gram) { tl.slot[0] = GDN_KERNEL_GRAM; tl.slot[1] = GDN_KERNEL_STATE; tl.slot[2] = GDN_KERNEL_READOUT; }
-    else { tl.slot[0] = GDN_KERNEL_RECURRENCE; tl.slot[1] = GDN_KERNEL_READOUT; }
-    if (timed) {
-      for (int i = 0; i <= tl.nk; ++i) {
-        hipError_t e = hipEventCreate(&tl.ev[i]);
-        if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
-      }
-    }
-    int ki = 0;
-    auto mark = [&]() -> hipError_t { return timed ? hipEventRecord(tl.ev[ki++], s) : hipSuccess; };
-    hipError_t e = mark();
-    if (p.gram) {
-      gdn::GramArgs ga;
-      ga.k = k; ga.v = v; ga.gfr = gfr; ga.bfr = bfr;
-      ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
-      ga.kscale = (float)c; ga.kscale2 = (float)(c * c);
-      gdn::StateArgs sa;
-      sa.gfr = gfr; sa.bfr = bfr; sa.gamma = gamma; sa.beta = beta;
-      sa.state_src = src; sa.state_dst = dst; sa.snap = snap;
-      sa.BH = (int)p.bh; sa.T = d->T; sa.t0 = t0; sa.Tc = tc; sa.beta_mode = d->beta_mode;
-      if (e == hipSuccess) e = gdn::launch_gram(d->D, ga, s);
-      if (e == hipSuccess) e = mark();
-      if (e == hipSuccess) e = gdn::launch_state(d->D, sa, s);
-    } else {
-      gdn::RecurArgs ra;
-      ra.k = k; ra.v = v; ra.gamma = gamma; ra.beta = beta;
-      ra.state_src = src; ra.state_dst = dst; ra.snap = snap;
-      ra.norm_part = (norms && !p.gram) ? norm_part : nullptr;
-      ra.units = (int)(p.bh * p.nb);
-      ra.T = d->T; ra.S = d->S; ra.t0 = t0; ra.Tc = tc;
-      ra.beta_mode = d->beta_mode;
-      ra.kscale = (float)c;
-      if (e == hipSuccess) e = gdn::launch_recurrence(d->D, p.esz == 2, ra, s);
-    }
-    if (e == hipSuccess) e = mark();
-    if (e == hipSuccess) e = gdn::launch_readout(d->D, p.esz == 2, ro, s);
-    if (e == hipSuccess) e = mark();
-    if (e != hipSuccess) {
-      if (timed)
-        for (int i = 0; i <= tl.nk; ++i) (void)hipEventDestroy(tl.ev[i]);
-      return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1, hipGetErrorString(e));
-    }
-    if (timed) {
-      std::lock_guard<std::mutex> lk(g_time_mu);
-      g_timed.push_back(tl);
-    }
-  }
-  return GDN_OK;
+  return p.gram ? run_gram(d, p, x, workspace, workspace_bytes, s)
+                : run_direct(d, p, x, workspace, workspace_bytes, s);
 }
 
 }  // namespace
@@ -305,23 +379,31 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
 
 gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_out[GDN_KERNEL_SLOTS],
                             int reset) {
-  std::lock_guard<std::mutex> lk(g_time_mu);
-  gdn_status st = GDN_OK;
-  for (TimedLaunch& tl : g_timed) {
-    hipError_t e = hipEventSynchronize(tl.ev[tl.nk]);
-    for (int i = 0; i < tl.nk && e == hipSuccess; ++i) {
-      float ms = 0.f;
-      e = hipEventElapsedTime(&ms, tl.ev[i], tl.ev[i + 1]);
-      if (e == hipSuccess) {
-        g_time_ms[tl.slot[i]] += ms;
-        g_time_n[tl.slot[i]] += 1;
-      }
-    }
-    if (e != hipSuccess) st = fail(GDN_ERR_HIP, "kernel timing: %s", hipGetErrorString(e));
-    for (int i = 0; i <= tl.nk; ++i) (void)hipEventDestroy(tl.ev[i]);
+  std::vector<TimedKernel> todo;
+  {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    todo.swap(g_timed);
   }
-  g_timed.clear();
+  gdn_status st = GDN_OK;
+  double ms_add[GDN_KERNEL_SLOTS] = {};
+  int64_t n_add[GDN_KERNEL_SLOTS] = {};
+  for (TimedKernel& tk : todo) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(tk.ev[1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, tk.ev[0], tk.ev[1]);
+    if (e == hipSuccess) {
+      ms_add[tk.slot] += ms;
+      n_add[tk.slot] += 1;
+    } else {
+      st = fail(GDN_ERR_HIP, "kernel timing: %s", hipGetErrorString(e));
+    }
+    give_timing_event(tk.ev[0]);
+    give_timing_event(tk.ev[1]);
+  }
+  std::lock_guard<std::mutex> lk(g_time_mu);
   for (int i = 0; i < GDN_KERNEL_SLOTS; ++i) {
+    g_time_ms[i] += ms_add[i];
+    g_time_n[i] += n_add[i];
     if (ms_out) ms_out[i] = g_time_ms[i];
     if (launches_out) launches_out[i] = g_time_n[i];
     if (reset) { g_time_ms[i] = 0.0; g_time_n[i] = 0; }

@@ -20,18 +20,23 @@
 // Only the second pass is sequential, and it reads 2*D*D*2 bytes per frame
 // instead of the frame's 2*S*D*2 bytes of keys and values.
 //
-// Register layouts (see gdn_device.h for the MFMA lane maps).  The Gram pass
-// builds its operands with transposed LDS reads, so the 8 k-slots of lane
-// (i, g) of a 32-token chunk hold tokens 4g..4g+3 and 16+4g..16+4g+3.  Its
-// accumulator C(L, I) for 16-key blocks L and I therefore holds, in lane
-// (b, g), G[16L + 4g + r][16I + b] for r = 0..3.  The state pass uses the
-// matching k-slot order over keys: slot e of lane (x, g) in k-step kb is key
-// 32kb + 16(e/4) + 4g + e%4.  With G symmetric, its A operand for output block
-// I and k-step kb is, lane by lane, C(2kb, I) followed by C(2kb+1, I): the
-// Gram pass stores exactly that, 1 KB per (I, kb), with no data movement.  In
-// the same order the state pass's B operand is its own accumulator layout
-// (lane (n, g) holds M[16I + 4g + r][n]), so the bf16 copy of the state that
-// the waves exchange each frame is a lane-linear 8 bytes per lane per block.
+// Layouts (see gdn_device.h for the MFMA lane maps).  The Gram pass builds
+// its operands with transposed LDS reads, so the 8 k-slots of lane (i, g) of a
+// 32-token chunk hold tokens 4g..4g+3 and 16+4g..16+4g+3.  Its accumulator
+// C(L, I) for 16-key blocks L and I therefore holds, in lane (b, g),
+// G[16L + 4g + r][16I + b] for r = 0..3.  G is symmetric, so only the blocks
+// (I, L) with I >= L are stored, each as a row-major 16 x 16 bf16 tile
+// (512 bytes): by symmetry block (I, L) is C(L, I) read with rows and columns
+// swapped, which makes lane (b, g) own the 8 contiguous bytes at b*32 + g*8 --
+// one coalesced 512-byte store.  The state pass uses the k-slot order over
+// keys in which slot e of lane group g in k-step kb is key
+// 32kb + 16(e/4) + 4g + e%4.  Its A operand for output block I and k-step kb
+// takes, in lane (a, g), row a, columns 4g..4g+3 of the blocks (I, 2kb) and
+// (I, 2kb+1): a plain 8-byte read from a stored block when I >= L, and a
+// transposed 8-byte LDS read (ds_read_b64_tr_b16) from the stored block
+// (L, I) when L > I.  In the same order the state pass's B operand is its own
+// accumulator layout (lane (n, g) holds M[16I + 4g + r][n]), so the bf16 copy
+// of the state exchanged each frame is lane-linear, 8 bytes per lane per block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,7 +67,8 @@ struct GramShape {
   static constexpr int RS = D + 8;                    // LDS row stride (elements)
   static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
   static constexpr size_t lds_bytes = 2 * 2 * tile_bytes;   // (K, V) x 2 buffers
-  static constexpr size_t g_frame_bytes = (size_t)NB * NKC * 1024;   // per (head, frame)
+  static constexpr int NBLK = NB * (NB + 1) / 2;       // stored G blocks (I >= L)
+  static constexpr size_t g_frame_bytes = (size_t)(NBLK + 1) / 2 * 1024;   // per (head, frame), 1 KB units
   static constexpr size_t b_frame_bytes = (size_t)NB * NB * 512;
 };
 
@@ -154,7 +160,8 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
     }
   }
 
-  // G: A operand (I, kb) = C(2kb, I) ++ C(2kb+1, I), scaled by c^2.
+  // G blocks (I, L), I >= L, row-major bf16, scaled by c^2: lane (b, g) owns
+  // row b, columns 4g..4g+3, i.e. C(L, I) lane values r = 0..3.
   const size_t fh = (size_t)bh * a.Tc + tl;
   unsigned char* gout = (unsigned char*)a.gfr + fh * Sh::g_frame_bytes;
   unsigned char* bout = (unsigned char*)a.bfr + fh * Sh::b_frame_bytes;
@@ -163,12 +170,10 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   for (int m = 0; m < NMY; ++m) {
     const int I = I0 + m;
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb) {
-      const f32x4 x = accG[m][2 * kb];
-      const f32x4 y = (2 * kb + 1 < NB) ? accG[m][2 * kb + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
-      const u32x4 v = {pack_bf16(c2 * x[0], c2 * x[1]), pack_bf16(c2 * x[2], c2 * x[3]),
-                       pack_bf16(c2 * y[0], c2 * y[1]), pack_bf16(c2 * y[2], c2 * y[3])};
-      *(u32x4*)(gout + ((size_t)I * NKC + kb) * 1024 + l * 16) = v;
+    for (int L = 0; L <= I; ++L) {
+      const f32x4 x = accG[m][L];
+      const u32x2 v = {pack_bf16(c2 * x[0], c2 * x[1]), pack_bf16(c2 * x[2], c2 * x[3])};
+      *(u32x2*)(gout + (size_t)(I * (I + 1) / 2 + L) * 512 + n * 32 + g * 8) = v;
     }
     // B: block (row block L, value block I) in accumulator layout, scaled by c
 #pragma unroll
@@ -197,28 +202,34 @@ __global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_bf16_kernel
 // State pass.  One workgroup per (head, 16-wide value tile j), placed so that
 // the tiles of a head share an XCD (they read the same G_t).  Wave I owns the
 // 16 x 16 block M[16I..16I+15][16j..16j+15] in fp32 registers.  Per frame it
-// forms (G_t bf16(M_{t-1}))[block I] with NKC MFMAs whose B operands come from
-// the bf16 copy of the tile's state column published by all waves in LDS at
-// the end of the previous frame, applies the gate, the input term and the
-// erase, and publishes its new bf16 block.  G_t fragments and B_t blocks are
-// prefetched kStateRing frames ahead (they do not depend on the state).
+// forms (G_t bf16(M_{t-1}))[block I] with NKC MFMAs: the A operands come from
+// the frame's stored G blocks, staged in LDS by all waves together (each G
+// block is fetched once per workgroup), the B operands from the bf16 copy of
+// the tile's state column that every wave published in LDS at the end of the
+// previous frame.  Then the gate, the input term and the erase, the bf16
+// publish and the snapshot store.  The global loads of G_t and B_t run
+// kStateRing frames ahead in registers (they do not depend on the state); G
+// moves from registers to its LDS slot one frame ahead of use.
 // ----------------------------------------------------------------------------
-constexpr int kStateRing = 8;   // even: the LDS exchange buffer is frame % 2
+constexpr int kStateRing = 8;   // even: the LDS buffers alternate with the frame parity
 
 template <int D>
 struct StateShape {
   static constexpr int NB = D / 16;
   static constexpr int NKC = (NB + 1) / 2;
+  static constexpr int NGL = (int)(GramShape<D>::g_frame_bytes / 1024);   // 1 KB pieces of a frame's G
+  static constexpr int LPG = (NGL + NB - 1) / NB;                        // pieces per wave
+  static constexpr size_t g_slot = GramShape<D>::g_frame_bytes;
   // exchange slot (kb, lane): 16 bytes = blocks 2kb and 2kb+1 of that lane
   static constexpr size_t xch_bytes = (size_t)2 * NKC * 64 * 16;
   static constexpr size_t gb_bytes = (size_t)kMaxFramesPerLaunch * 8;
-  static constexpr size_t lds_bytes = xch_bytes + gb_bytes;
+  static constexpr size_t lds_bytes = 2 * g_slot + xch_bytes + gb_bytes;
 };
 
 template <int D, bool ERASE>
 __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArgs a) {
   using Sh = StateShape<D>;
-  constexpr int NB = Sh::NB, NKC = Sh::NKC;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, NGL = Sh::NGL, LPG = Sh::LPG;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int unit = xcd_unit(a.BH * NB);
   if (unit < 0) return;                       // whole workgroup: no work on this slot
@@ -226,8 +237,9 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
   const int I = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Tc = a.Tc;
-  unsigned char* xch = smem;
-  float2* gb = (float2*)(smem + Sh::xch_bytes);
+  unsigned char* gsl = smem;                                  // 2 G slots
+  unsigned char* xch = smem + 2 * Sh::g_slot;                 // 2 exchange buffers
+  float2* gb = (float2*)(xch + Sh::xch_bytes);
 
   for (int i = tid; i < Tc; i += NB * 64)
     gb[i] = make_float2(a.gamma[(size_t)bh * a.T + a.t0 + i], a.beta[(size_t)bh * a.T + a.t0 + i]);
@@ -259,22 +271,42 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
       make_rsrc((const unsigned char*)a.bfr + (size_t)bh * Tc * bfb, (uint32_t)(Tc * bfb));
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc((unsigned char*)a.snap + (size_t)bh * Tc * D * D * 2, (uint32_t)(Tc * D * D * 2));
-  const uint32_t gbase = (uint32_t)(I * NKC * 1024 + l * 16);
   const uint32_t bbase = (uint32_t)((j * NB + I) * 512 + l * 8);
   const uint32_t sbase = (uint32_t)(((j * NB + I) * 64 + l) * 8);
 
-  u32x4 Gf[kStateRing][NKC];
+  u32x4 Gr[kStateRing][LPG];                  // this wave's 1 KB pieces of a frame's G
   u32x2 Bf[kStateRing];
   auto load_frame = [&](int f, int r) {
     const bool ok = f < Tc;
 #pragma unroll
-    for (int kb = 0; kb < NKC; ++kb)
-      Gf[r][kb] = buf_load16(grs, ok ? gbase + (uint32_t)f * (uint32_t)gfb + kb * 1024 : kOOB);
+    for (int i = 0; i < LPG; ++i) {
+      const int q = I + NB * i;             // piece index (uniform)
+      Gr[r][i] = buf_load16(grs, (ok && q < NGL) ? (uint32_t)f * (uint32_t)gfb + q * 1024 + l * 16 : kOOB);
+    }
     Bf[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                           brs, ok ? bbase + (uint32_t)f * (uint32_t)bfb : kOOB, 0, 0));
   };
+  auto stage_g = [&](int slot, int r) {
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int q = I + NB * i;
+      if (q < NGL) *(u32x4*)(gsl + (size_t)slot * Sh::g_slot + q * 1024 + l * 16) = Gr[r][i];
+    }
+  };
+  // A operand half: row a = n of block (I, L), columns 4g..4g+3
+  auto g_half = [&](const unsigned char* gs, int L) -> u32x2 {
+    if (L >= NB) return u32x2{0u, 0u};
+    if (L <= I)
+      return *(const u32x2*)(gs + (size_t)(I * (I + 1) / 2 + L) * 512 + n * 32 + g * 8);
+    // block (I, L) = transpose of the stored block (L, I): column n of its
+    // rows 4g..4g+3, through a transposed read
+    const unsigned char* blk = gs + (size_t)(L * (L + 1) / 2 + I) * 512;
+    return lds_tr16((const uint16_t*)(blk + (4 * g + (n >> 2)) * 32 + (n & 3) * 8));
+  };
+
 #pragma unroll
   for (int r = 0; r < kStateRing; ++r) load_frame(r, r);
+  stage_g(0, 0);
   lds_barrier();
 
   for (int base = 0; base < Tc; base += kStateRing) {
@@ -282,11 +314,14 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
     for (int r = 0; r < kStateRing; ++r) {
       const int f = base + r;
       const unsigned char* xr = xch + (size_t)(r & 1) * (Sh::xch_bytes / 2);
+      const unsigned char* gs = gsl + (size_t)(r & 1) * Sh::g_slot;
       f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb) {
+        const u32x2 lo = g_half(gs, 2 * kb), hi = g_half(gs, 2 * kb + 1);
+        const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
         const u32x4 bop = *(const u32x4*)(xr + ((size_t)kb * 64 + l) * 16);
-        p = mfma_bf16(Gf[r][kb], bop, p);
+        p = mfma_bf16(aop, bop, p);
       }
       const float2 gbv = gb[f < Tc ? f : 0];
       const float gm = gbv.x, bt = gbv.y, bg = bt * gm;
@@ -298,6 +333,8 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
         const float nv = gm * m[e] - bg * p[e] + (ERASE ? bin[e] : bt * bin[e]);
         m[e] = ok ? nv : m[e];
       }
+      // G of the next frame into the other LDS slot (read by everyone after the barrier)
+      stage_g((r + 1) & 1, (r + 1) % kStateRing);
       load_frame(f + kStateRing, r);
       const u32x2 pub = publish((r & 1) ^ 1, m);
       // bf16 snapshot of M_t: this wave's block, lane-linear (512 contiguous bytes)
@@ -375,7 +412,10 @@ hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream) {
 }
 #undef GDN_DISPATCH
 
-size_t gram_frame_bytes(int D) { return (size_t)(D / 16) * ((D / 16 + 1) / 2) * 1024; }
+size_t gram_frame_bytes(int D) {
+  const size_t nb = (size_t)D / 16;
+  return (nb * (nb + 1) / 2 + 1) / 2 * 1024;
+}
 size_t input_frame_bytes(int D) { return (size_t)(D / 16) * (D / 16) * 512; }
 
 }  // namespace gdn
