@@ -45,6 +45,19 @@
 
 namespace gdn {
 
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+// f(Int<0>{}), ..., f(Int<N-1>{})
+template <int N, int K = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(Int<K>{});
+    static_for<N, K + 1>(f);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Gram pass.  One workgroup per (head, frame); wave w owns the 16-key blocks
 // I = 2w, 2w+1: it accumulates C(L, I) for every L (the G columns of its
@@ -226,16 +239,14 @@ struct StateShape {
   static constexpr size_t lds_bytes = 2 * g_slot + xch_bytes + gb_bytes;
 };
 
-template <int D, bool ERASE>
-__global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArgs a) {
+// Wave I of a state workgroup (I is a template parameter so that every block
+// index below is a constant: which G blocks are read directly and which
+// through a transposed read is fixed per wave, with no branches).
+template <int D, bool ERASE, int I>
+__device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* smem, int bh, int j) {
   using Sh = StateShape<D>;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, NGL = Sh::NGL, LPG = Sh::LPG;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int unit = xcd_unit(a.BH * NB);
-  if (unit < 0) return;                       // whole workgroup: no work on this slot
-  const int bh = unit / NB, j = unit % NB;
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
-  const int I = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Tc = a.Tc;
   unsigned char* gsl = smem;                                  // 2 G slots
   unsigned char* xch = smem + 2 * Sh::g_slot;                 // 2 exchange buffers
@@ -294,14 +305,18 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
     }
   };
   // A operand half: row a = n of block (I, L), columns 4g..4g+3
-  auto g_half = [&](const unsigned char* gs, int L) -> u32x2 {
-    if (L >= NB) return u32x2{0u, 0u};
-    if (L <= I)
+  auto g_half = [&](const unsigned char* gs, auto Lc) -> u32x2 {
+    constexpr int L = decltype(Lc)::value;
+    if constexpr (L >= NB) {
+      return u32x2{0u, 0u};
+    } else if constexpr (L <= I) {
       return *(const u32x2*)(gs + (size_t)(I * (I + 1) / 2 + L) * 512 + n * 32 + g * 8);
-    // block (I, L) = transpose of the stored block (L, I): column n of its
-    // rows 4g..4g+3, through a transposed read
-    const unsigned char* blk = gs + (size_t)(L * (L + 1) / 2 + I) * 512;
-    return lds_tr16((const uint16_t*)(blk + (4 * g + (n >> 2)) * 32 + (n & 3) * 8));
+    } else {
+      // block (I, L) = transpose of the stored block (L, I): column n of its
+      // rows 4g..4g+3, through a transposed read
+      const unsigned char* blk = gs + (size_t)(L * (L + 1) / 2 + I) * 512;
+      return lds_tr16((const uint16_t*)(blk + (4 * g + (n >> 2)) * 32 + (n & 3) * 8));
+    }
   };
 
 #pragma unroll
@@ -315,15 +330,19 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
       const int f = base + r;
       const unsigned char* xr = xch + (size_t)(r & 1) * (Sh::xch_bytes / 2);
       const unsigned char* gs = gsl + (size_t)(r & 1) * Sh::g_slot;
+      // all operand reads first (one LDS latency per frame), then the MFMA chain
+      u32x4 aop[NKC], bop[NKC];
+      static_for<NKC>([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        const u32x2 lo = g_half(gs, Int<2 * kb>{}), hi = g_half(gs, Int<2 * kb + 1>{});
+        aop[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        bop[kb] = *(const u32x4*)(xr + ((size_t)kb * 64 + l) * 16);
+      });
+      const float2 gbv = gb[f < Tc ? f : 0];
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKC; ++kb) {
-        const u32x2 lo = g_half(gs, 2 * kb), hi = g_half(gs, 2 * kb + 1);
-        const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
-        const u32x4 bop = *(const u32x4*)(xr + ((size_t)kb * 64 + l) * 16);
-        p = mfma_bf16(aop, bop, p);
-      }
-      const float2 gbv = gb[f < Tc ? f : 0];
+      for (int kb = 0; kb < NKC; ++kb) p = mfma_bf16(aop[kb], bop[kb], p);
       const float gm = gbv.x, bt = gbv.y, bg = bt * gm;
       const u32x2 bw = Bf[r];
       const f32x4 bin = {bf16_lo_f32(bw[0]), bf16_hi_f32(bw[0]), bf16_lo_f32(bw[1]), bf16_hi_f32(bw[1])};
@@ -349,6 +368,20 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[(size_t)(row0 + r) * D + col] = m[r];
   }
+}
+
+template <int D, bool ERASE>
+__global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArgs a) {
+  constexpr int NB = D / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int unit = xcd_unit(a.BH * NB);
+  if (unit < 0) return;                       // whole workgroup: no work on this slot
+  const int bh = unit / NB, j = unit % NB;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  static_for<NB>([&](auto ic) {
+    constexpr int I = decltype(ic)::value;
+    if (w == I) state_wave<D, ERASE, I>(a, smem, bh, j);
+  });
 }
 
 // ----------------------------------------------------------------------------
