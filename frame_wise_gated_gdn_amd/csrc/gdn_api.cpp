@@ -179,11 +179,42 @@ size_t frames_per_launch(const Plan& p, int T, size_t wb) {
   return frames;
 }
 
-// Gram path: per range of frames, the gram pass, the serial state pass and
-// the readout, in that order on the caller's stream.  (Running the state pass
-// of one range concurrently with the HBM-bound passes of neighbouring ranges
-// on side streams was measured slower: the latency-bound state pass loses its
-// CUs to them, and the shorter launches pay their tails.)
+// Side stream of the Gram path, one per (thread, device), created on first use
+// at default priority and kept for the life of the process, with a small ring
+// of events.  An event is recorded again only after every wait on its
+// previous record has been enqueued (the enqueue order below guarantees it).
+constexpr int kStateSplit = 4;             // state/readout sub-ranges per gram range
+constexpr int kMinSplitFrames = 64;        // frames per sub-range at least
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t ev[2 * kStateSplit + 2] = {};
+};
+thread_local std::vector<SideStream*> t_side;   // by device id
+
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)t_side.size() <= dev) t_side.resize(dev + 1, nullptr);
+  if (!t_side[dev]) {
+    SideStream* ss = new SideStream();
+    e = hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking);
+    for (hipEvent_t& ev : ss->ev)
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;   // a partly built side stream is not kept
+    t_side[dev] = ss;
+  }
+  *out = t_side[dev];
+  return hipSuccess;
+}
+
+// Gram path.  Per range of up to kMaxFramesPerLaunch frames: the gram pass
+// (all frames in parallel) on the caller's stream; then the serial state pass
+// in kStateSplit sub-ranges on the side stream, and the readout of each
+// sub-range on the caller's stream as soon as its states exist.  The state
+// pass is latency-bound and light on resources, so the state of sub-range
+// i+1 runs on the CUs next to the HBM-bound readout of sub-range i.  The state
+// crosses sub-ranges and ranges in fp32, so any split gives the same bits.
 gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* workspace, size_t wb,
                     hipStream_t s) {
   const size_t F = frames_per_launch(p, d->T, wb);
@@ -201,30 +232,59 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
   float* hand = x.state_out ? x.state_out : carrier;
   const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
   const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  SideStream* ss = nullptr;
+  hipError_t e = hipSuccess;
+  int failed_t0 = 0;
 
-  for (int t0 = 0; t0 < d->T; t0 += (int)F) {
+  for (int t0 = 0; t0 < d->T && e == hipSuccess; t0 += (int)F) {
+    failed_t0 = t0;
     const int tc = (int)std::min<size_t>(F, (size_t)(d->T - t0));
-    const bool last = t0 + tc >= d->T;
+    const int nsub = std::max(1, std::min(kStateSplit, tc / kMinSplitFrames));
     gdn::GramArgs ga;
     ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
     ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
     ga.kscale = (float)c; ga.kscale2 = (float)(c * c);
-    gdn::StateArgs sa;
-    sa.gfr = gfr; sa.bfr = bfr; sa.gamma = x.gamma; sa.beta = x.beta;
-    sa.state_src = (t0 == 0) ? x.state_in : hand;
-    sa.state_dst = last ? x.state_out : hand;
-    sa.snap = snap;
-    sa.BH = (int)p.bh; sa.T = d->T; sa.t0 = t0; sa.Tc = tc; sa.beta_mode = d->beta_mode;
-    gdn::ReadoutArgs ro;
-    ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = nullptr;
-    ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
-    hipError_t e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(d->D, ga, s); });
-    if (e == hipSuccess)
-      e = launch_timed(timed, GDN_KERNEL_STATE, s, [&] { return gdn::launch_state(d->D, sa, s); });
-    if (e == hipSuccess)
-      e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_readout(d->D, true, ro, s); });
-    if (e != hipSuccess)
-      return fail(GDN_ERR_HIP, "kernel launch (frames %d..%d): %s", t0, t0 + tc - 1, hipGetErrorString(e));
+    e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(d->D, ga, s); });
+    hipStream_t st = s;
+    if (e == hipSuccess && nsub > 1) {
+      e = side_stream(&ss);
+      if (e == hipSuccess) {
+        st = ss->stream;
+        e = hipEventRecord(ss->ev[0], s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
+      }
+    }
+    // state sub-ranges (side stream), then their readouts (caller's stream)
+    for (int i = 0; i < nsub && e == hipSuccess; ++i) {
+      const int f0 = (int)((long long)tc * i / nsub), f1 = (int)((long long)tc * (i + 1) / nsub);
+      gdn::StateArgs sa;
+      sa.gfr = gfr; sa.bfr = bfr; sa.gamma = x.gamma; sa.beta = x.beta;
+      sa.state_src = (t0 == 0 && i == 0) ? x.state_in : hand;
+      sa.state_dst = (t0 + tc >= d->T && i == nsub - 1) ? x.state_out : hand;
+      sa.snap = snap;
+      sa.BH = (int)p.bh; sa.T = d->T; sa.t0 = t0 + f0; sa.Tc = f1 - f0;
+      sa.Fs = tc; sa.f0 = f0; sa.beta_mode = d->beta_mode;
+      e = launch_timed(timed, GDN_KERNEL_STATE, st, [&] { return gdn::launch_state(d->D, sa, st); });
+      if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
+    }
+    for (int i = 0; i < nsub && e == hipSuccess; ++i) {
+      const int f0 = (int)((long long)tc * i / nsub), f1 = (int)((long long)tc * (i + 1) / nsub);
+      if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + i], 0);
+      gdn::ReadoutArgs ro;
+      ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = nullptr;
+      ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0 + f0; ro.Tc = f1 - f0;
+      ro.Fs = tc; ro.f0 = f0;
+      if (e == hipSuccess)
+        e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_readout(d->D, true, ro, s); });
+    }
+  }
+  if (e != hipSuccess) {
+    // keep the caller's stream ordered after anything already on the side stream
+    if (ss) {
+      const int last = 2 * kStateSplit + 1;
+      if (hipEventRecord(ss->ev[last], ss->stream) == hipSuccess) (void)hipStreamWaitEvent(s, ss->ev[last], 0);
+    }
+    return fail(GDN_ERR_HIP, "kernel launch (frames from %d): %s", failed_t0, hipGetErrorString(e));
   }
   return GDN_OK;
 }
@@ -262,6 +322,7 @@ gdn_status run_direct(const gdn_desc* d, const Plan& p, const Ptrs& x, void* wor
     gdn::ReadoutArgs ro;
     ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = ra.norm_part;
     ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
+    ro.Fs = tc; ro.f0 = 0;
     hipError_t e = launch_timed(timed, GDN_KERNEL_RECURRENCE, s,
                                 [&] { return gdn::launch_recurrence(d->D, bf16, ra, s); });
     if (e == hipSuccess)

@@ -59,13 +59,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // ----------------------------------------------------------------------------
-// Gram pass.  One workgroup per (head, frame); wave w owns the 16-key blocks
-// I = 2w, 2w+1: it accumulates C(L, I) for every L (the G columns of its
-// blocks) and Kf^T V for the value blocks j = 2w, 2w+1.  The frame's tokens
+// Gram pass.  One workgroup per (head, frame).  Its output is the NB*NB blocks
+// of B = Kf^T V and the NB(NB+1)/2 stored blocks (I >= L) of G = Kf^T Kf, in
+// 16 x 16 blocks (NB = D/16); the list of output blocks is cut into equal
+// contiguous ranges, one per wave, fixed at compile time.  The frame's tokens
 // are walked in 32-token chunks: each chunk of K and V is loaded once
 // (coalesced 1 KB loads spread over the waves, kept kGramRing chunks ahead in
 // registers), passed through ReLU (keys) and staged in a double-buffered LDS
-// tile, from which every wave takes its operands with transposed reads.
+// tile, from which every wave takes the operands its blocks need with
+// transposed reads, one MFMA per block and chunk.
 // ----------------------------------------------------------------------------
 constexpr int kGramRing = 4;   // chunks in flight per workgroup (even: LDS buffer = slot % 2)
 
@@ -81,16 +83,50 @@ struct GramShape {
   static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
   static constexpr size_t lds_bytes = 2 * 2 * tile_bytes;   // (K, V) x 2 buffers
   static constexpr int NBLK = NB * (NB + 1) / 2;       // stored G blocks (I >= L)
+  static constexpr int NBB = NB * NB;                  // B blocks
+  static constexpr int NOUT = NBB + NBLK;              // output blocks: B blocks, then G blocks
   static constexpr size_t g_frame_bytes = (size_t)(NBLK + 1) / 2 * 1024;   // per (head, frame), 1 KB units
   static constexpr size_t b_frame_bytes = (size_t)NB * NB * 512;
 };
 
+// stored G block k = I(I+1)/2 + L (I >= L) -> I, L
+constexpr int gblk_row(int k) {
+  int I = 0;
+  while ((I + 1) * (I + 2) / 2 <= k) ++I;
+  return I;
+}
+constexpr int gblk_col(int k) { return k - gblk_row(k) * (gblk_row(k) + 1) / 2; }
+
+// Output block b of the gram pass: b < NBB is B block (value block j = b / NB,
+// key block L = b % NB), accumulated as MFMA(X_L, Y_j); b >= NBB is stored G
+// block k = b - NBB = (I, L), accumulated as MFMA(X_L, X_I) = C(L, I).
+// Bit masks of the key (X) and value (Y) operand blocks that the output
+// blocks [b0, b1) use.
+constexpr uint32_t gram_xmask(int NB, int b0, int b1) {
+  uint32_t m = 0;
+  for (int b = b0; b < b1; ++b) {
+    if (b < NB * NB) {
+      m |= 1u << (b % NB);
+    } else {
+      m |= 1u << gblk_row(b - NB * NB);
+      m |= 1u << gblk_col(b - NB * NB);
+    }
+  }
+  return m;
+}
+constexpr uint32_t gram_ymask(int NB, int b0, int b1) {
+  uint32_t m = 0;
+  for (int b = b0; b < b1 && b < NB * NB; ++b) m |= 1u << (b / NB);
+  return m;
+}
+
 template <int D, int W>
 __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem, int bh, int tl) {
   using Sh = GramShape<D>;
-  constexpr int NB = Sh::NB, NKC = Sh::NKC, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW,
-                RS = Sh::RS;
-  constexpr int I0 = 2 * W, NMY = (2 * W + 1 < NB) ? 2 : 1;   // my blocks: I0 .. I0 + NMY - 1
+  constexpr int NB = Sh::NB, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, RS = Sh::RS;
+  constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT;
+  constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
+  constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
   const int l = lane_id(), g = l >> 4, n = l & 15;
   const int S = a.S, T = a.T, t = a.t0 + tl;
   const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
@@ -134,14 +170,9 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
     return u32x4{x[0], x[1], y[0], y[1]};
   };
 
-  f32x4 accG[NMY][NB], accB[NMY][NB];
+  f32x4 acc[NMB];
 #pragma unroll
-  for (int m = 0; m < NMY; ++m)
-#pragma unroll
-    for (int L = 0; L < NB; ++L) {
-      accG[m][L] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accB[m][L] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int i = 0; i < NMB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 R[kGramRing][LPW];
 #pragma unroll
@@ -157,45 +188,43 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
       if (c < nch) {
         const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
         const uint16_t* vt = kt + 32 * RS;
-        u32x4 X[NB];
-#pragma unroll
-        for (int L = 0; L < NB; ++L) X[L] = frag(kt, L);
-#pragma unroll
-        for (int m = 0; m < NMY; ++m) {
-          const u32x4 Y = frag(vt, I0 + m);
-#pragma unroll
-          for (int L = 0; L < NB; ++L) {
-            accG[m][L] = mfma_bf16(X[L], X[I0 + m], accG[m][L]);
-            accB[m][L] = mfma_bf16(X[L], Y, accB[m][L]);
+        u32x4 X[NB], Y[NB];
+        static_for<NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
+          if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
+        });
+        static_for<NMB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value, b = B0 + i;
+          if constexpr (b < NBB) {
+            acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
+          } else {
+            constexpr int k = b - NBB;
+            acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
           }
-        }
+        });
       }
     }
   }
 
-  // G blocks (I, L), I >= L, row-major bf16, scaled by c^2: lane (b, g) owns
-  // row b, columns 4g..4g+3, i.e. C(L, I) lane values r = 0..3.
+  // B blocks in accumulator layout scaled by c; G blocks (I, L), I >= L,
+  // row-major scaled by c^2: lane (b, g) owns row b, columns 4g..4g+3 of the
+  // block, i.e. the values of C(L, I).
   const size_t fh = (size_t)bh * a.Tc + tl;
   unsigned char* gout = (unsigned char*)a.gfr + fh * Sh::g_frame_bytes;
   unsigned char* bout = (unsigned char*)a.bfr + fh * Sh::b_frame_bytes;
   const float c2 = a.kscale2, c1 = a.kscale;
-#pragma unroll
-  for (int m = 0; m < NMY; ++m) {
-    const int I = I0 + m;
-#pragma unroll
-    for (int L = 0; L <= I; ++L) {
-      const f32x4 x = accG[m][L];
-      const u32x2 v = {pack_bf16(c2 * x[0], c2 * x[1]), pack_bf16(c2 * x[2], c2 * x[3])};
-      *(u32x2*)(gout + (size_t)(I * (I + 1) / 2 + L) * 512 + n * 32 + g * 8) = v;
-    }
-    // B: block (row block L, value block I) in accumulator layout, scaled by c
-#pragma unroll
-    for (int L = 0; L < NB; ++L) {
-      const f32x4 x = accB[m][L];
+  static_for<NMB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value, b = B0 + i;
+    const f32x4 x = acc[i];
+    if constexpr (b < NBB) {
       const u32x2 v = {pack_bf16(c1 * x[0], c1 * x[1]), pack_bf16(c1 * x[2], c1 * x[3])};
-      *(u32x2*)(bout + ((size_t)I * NB + L) * 512 + l * 8) = v;
+      *(u32x2*)(bout + (size_t)b * 512 + l * 8) = v;
+    } else {
+      const u32x2 v = {pack_bf16(c2 * x[0], c2 * x[1]), pack_bf16(c2 * x[2], c2 * x[3])};
+      *(u32x2*)(gout + (size_t)(b - NBB) * 512 + n * 32 + g * 8) = v;
     }
-  }
+  });
 }
 
 template <int D>
@@ -224,7 +253,7 @@ __global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_bf16_kernel
 // kStateRing frames ahead in registers (they do not depend on the state); G
 // moves from registers to its LDS slot one frame ahead of use.
 // ----------------------------------------------------------------------------
-constexpr int kStateRing = 8;   // even: the LDS buffers alternate with the frame parity
+constexpr int kStateRing = 6;   // even: the LDS buffers alternate with the frame parity
 
 template <int D>
 struct StateShape {
@@ -235,8 +264,7 @@ struct StateShape {
   static constexpr size_t g_slot = GramShape<D>::g_frame_bytes;
   // exchange slot (kb, lane): 16 bytes = blocks 2kb and 2kb+1 of that lane
   static constexpr size_t xch_bytes = (size_t)2 * NKC * 64 * 16;
-  static constexpr size_t gb_bytes = (size_t)kMaxFramesPerLaunch * 8;
-  static constexpr size_t lds_bytes = 2 * g_slot + xch_bytes + gb_bytes;
+  static constexpr size_t lds_bytes = 2 * g_slot + xch_bytes;
 };
 
 // Wave I of a state workgroup (I is a template parameter so that every block
@@ -250,10 +278,8 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
   const int Tc = a.Tc;
   unsigned char* gsl = smem;                                  // 2 G slots
   unsigned char* xch = smem + 2 * Sh::g_slot;                 // 2 exchange buffers
-  float2* gb = (float2*)(xch + Sh::xch_bytes);
+  (void)tid;
 
-  for (int i = tid; i < Tc; i += NB * 64)
-    gb[i] = make_float2(a.gamma[(size_t)bh * a.T + a.t0 + i], a.beta[(size_t)bh * a.T + a.t0 + i]);
   // block NB of an odd block count is a zero pad of the last k-step
   if ((NB & 1) && I == 0) {
     *(u32x2*)(xch + ((size_t)(NKC - 1) * 64 + l) * 16 + 8) = u32x2{0u, 0u};
@@ -275,20 +301,25 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
   publish(0, m);
 
   const size_t gfb = GramShape<D>::g_frame_bytes, bfb = GramShape<D>::b_frame_bytes;
-  // per-head buffer resources: a head's frames of one launch span < 2^31 bytes
-  const __amdgpu_buffer_rsrc_t grs =
-      make_rsrc((const unsigned char*)a.gfr + (size_t)bh * Tc * gfb, (uint32_t)(Tc * gfb));
-  const __amdgpu_buffer_rsrc_t brs =
-      make_rsrc((const unsigned char*)a.bfr + (size_t)bh * Tc * bfb, (uint32_t)(Tc * bfb));
+  // per-head buffer resources over this launch's frames of the staging
+  // arrays ([head][Fs] frames, this launch from frame f0): < 2^31 bytes each
+  const size_t fb = (size_t)bh * a.Fs + a.f0;
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc((const unsigned char*)a.gfr + fb * gfb, (uint32_t)(Tc * gfb));
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc((const unsigned char*)a.bfr + fb * bfb, (uint32_t)(Tc * bfb));
   const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc((unsigned char*)a.snap + (size_t)bh * Tc * D * D * 2, (uint32_t)(Tc * D * D * 2));
+      make_rsrc((unsigned char*)a.snap + fb * D * D * 2, (uint32_t)(Tc * D * D * 2));
+  const __amdgpu_buffer_rsrc_t gars = make_rsrc(a.gamma + (size_t)bh * a.T + a.t0, (uint32_t)(Tc * 4));
+  const __amdgpu_buffer_rsrc_t bers = make_rsrc(a.beta + (size_t)bh * a.T + a.t0, (uint32_t)(Tc * 4));
   const uint32_t bbase = (uint32_t)((j * NB + I) * 512 + l * 8);
   const uint32_t sbase = (uint32_t)(((j * NB + I) * 64 + l) * 8);
 
   u32x4 Gr[kStateRing][LPG];                  // this wave's 1 KB pieces of a frame's G
   u32x2 Bf[kStateRing];
+  float Ga[kStateRing], Be[kStateRing];       // gamma_t, beta_t
   auto load_frame = [&](int f, int r) {
     const bool ok = f < Tc;
+    Ga[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gars, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
+    Be[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bers, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
 #pragma unroll
     for (int i = 0; i < LPG; ++i) {
       const int q = I + NB * i;             // piece index (uniform)
@@ -338,12 +369,11 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
         aop[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         bop[kb] = *(const u32x4*)(xr + ((size_t)kb * 64 + l) * 16);
       });
-      const float2 gbv = gb[f < Tc ? f : 0];
       __builtin_amdgcn_sched_barrier(0);
       f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKC; ++kb) p = mfma_bf16(aop[kb], bop[kb], p);
-      const float gm = gbv.x, bt = gbv.y, bg = bt * gm;
+      const float gm = Ga[r], bt = Be[r], bg = bt * gm;
       const u32x2 bw = Bf[r];
       const f32x4 bin = {bf16_lo_f32(bw[0]), bf16_hi_f32(bw[0]), bf16_lo_f32(bw[1]), bf16_hi_f32(bw[1])};
       const bool ok = f < Tc;

@@ -35,6 +35,7 @@ struct ReadoutArgs {
   const float* norm_part;   // as in RecurArgs; nullptr: norms from the bf16 snapshot
   float* norms;             // [BH][T] or nullptr
   int BH, T, S, t0, Tc;
+  int Fs, f0;               // snapshots (and norm partials) hold [BH][Fs] frames from f0
 };
 
 // Gram pass (bf16 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
@@ -57,6 +58,7 @@ struct StateArgs {
   float* state_dst;         // [BH][D][D] or nullptr
   void* snap;               // as in RecurArgs (bf16 block layout)
   int BH, T, t0, Tc;
+  int Fs, f0;               // staging arrays hold [BH][Fs] frames; this launch's first frame is f0
   int beta_mode;            // 0 ERASE, 1 WRITE
 };
 

@@ -591,12 +591,13 @@ __global__ __launch_bounds__(kReadWaves * 64) void gdn_readout_kernel(ReadoutArg
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), g = l >> 4, n = l & 15;
   const int S = a.S, T = a.T;
   const size_t fo = ((size_t)bh * T + t) * S * D;
-  const size_t so = ((size_t)bh * a.Tc + tl) * D * D;
+  const size_t sf = (size_t)bh * a.Fs + a.f0 + tl;   // staging frame of (head, frame)
+  const size_t so = sf * D * D;
   const int ntile = (S + 15) / 16;
 
   if (a.norms && tid == 0) {
     float sq = 0.f;
-    for (int j = 0; j < NB; ++j) sq += a.norm_part[((size_t)bh * a.Tc + tl) * NB + j];
+    for (int j = 0; j < NB; ++j) sq += a.norm_part[sf * NB + j];
     a.norms[(size_t)bh * T + t] = sqrtf(sq);
   }
 
@@ -702,10 +703,11 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
   const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * 2u;   // frame's first byte in the head
   const int nchunk = (S + 31) / 32;
   const int NC = (nchunk + kReadWaves - 1) / kReadWaves;     // chunk slots per wave
+  const size_t sf = (size_t)bh * a.Fs + a.f0 + tl;           // staging frame of (head, frame)
 
   if (a.norms && a.norm_part && tid == 0) {
     float sq = 0.f;
-    for (int j = 0; j < NB; ++j) sq += a.norm_part[((size_t)bh * a.Tc + tl) * NB + j];
+    for (int j = 0; j < NB; ++j) sq += a.norm_part[sf * NB + j];
     a.norms[(size_t)bh * T + t] = sqrtf(sq);
   }
 
@@ -723,7 +725,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
   // A operands: M_t^T rows (value column 16jb + n); k-step kc holds keys
   // 32kc + 4g..+3 and 32kc + 16 + 4g..+3, i.e. the snapshot blocks (jb, 2kc)
   // and (jb, 2kc + 1) of this lane
-  const unsigned char* snap = (const unsigned char*)a.snap + ((size_t)bh * a.Tc + tl) * D * D * 2;
+  const unsigned char* snap = (const unsigned char*)a.snap + sf * D * D * 2;
   u32x4 A[NB][NKC];
 #pragma unroll
   for (int jb = 0; jb < NB; ++jb)

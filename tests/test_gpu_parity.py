@@ -221,6 +221,25 @@ def test_workspace_size_does_not_change_bits(env):
         assert torch.equal(o, res[0][0]) and torch.equal(s, res[0][1]) and torch.equal(n, res[0][2])
 
 
+def test_long_rollout_split_schedule_bitwise_and_parity(env):
+    """T = 300 frames: the default workspace runs the state pass in sub-ranges
+    on a side stream next to the readouts; a minimal workspace runs one frame
+    per launch on one stream.  Same bits, and both match the oracle."""
+    torch, gdn, wl, go = env
+    w = wl.Workload("split", 1, 3, 300, 64, 64, gamma=(0.9, 1.0), beta=(0.2, 1.0))
+    inp = gen(env, w)
+    d = gdn.make_desc(1, 3, 300, 64, 64, "bf16")
+    res = []
+    for nbytes in (gdn.workspace_size(d), gdn.workspace_min_size(d)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        res.append(gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], workspace=ws,
+                                     want_norms=True))
+    torch.cuda.synchronize()
+    for x, y in zip(res[0], res[1]):
+        assert torch.equal(x, y)
+    check(env, inp, res[0][0], res[0][1], run_oracle(env, inp, want_norms=True), TOL["bf16"], norms=res[0][2])
+
+
 def test_repeat_runs_are_bitwise_equal(env):
     torch, gdn, wl, go = env
     inp = gen(env, wl.SHORT.with_(H=4, T=9))
