@@ -240,6 +240,41 @@ def test_long_rollout_split_schedule_bitwise_and_parity(env):
     check(env, inp, res[0][0], res[0][1], run_oracle(env, inp, want_norms=True), TOL["bf16"], norms=res[0][2])
 
 
+@pytest.mark.parametrize("path", ["auto", "direct"])
+def test_write_mode_short_clip_all_heads(env, path):
+    """WRITE mode (beta on the whole residual) at the short-clip shape."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.SHORT.with_(beta_mode="write"))
+    out, st, nm = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], beta_mode="write",
+                                    want_norms=True, path=path)
+    torch.cuda.synchronize()
+    check(env, inp, out, st, run_oracle(env, inp, mode="write", want_norms=True), TOL["bf16"], norms=nm)
+
+
+def test_streaming_long_chunks_bitwise(env):
+    """gdn_frame_step over chunks long enough to use the split schedule
+    (150 + 150 frames) gives the bits of one 300-frame forward."""
+    torch, gdn, wl, go = env
+    w = wl.Workload("stream", 1, 2, 300, 48, 128, gamma=(0.8, 1.0), beta=(0.0, 1.0))
+    inp = gen(env, w)
+    s0 = torch.randn((1, 2, 128, 128), generator=torch.Generator().manual_seed(7)).cuda()
+    o1, st1, n1 = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], state=s0,
+                                    want_norms=True)
+    state = s0.clone()
+    outs, norms = [], []
+    for t0 in (0, 150):
+        sl = slice(t0, t0 + 150)
+        nm = torch.empty((1, 2, 150), dtype=torch.float32, device="cuda")
+        o, _, _ = gdn.frame_step(*(inp[n][:, :, sl].contiguous() for n in ("q", "k", "v", "gamma", "beta")),
+                                 state, commit="inplace", norms=nm)
+        outs.append(o)
+        norms.append(nm)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2), o1) and torch.equal(state, st1)
+    assert torch.equal(torch.cat(norms, dim=2), n1)
+    check(env, inp, o1, st1, run_oracle(env, inp, state=s0, want_norms=True), TOL["bf16"], norms=n1)
+
+
 def test_repeat_runs_are_bitwise_equal(env):
     torch, gdn, wl, go = env
     inp = gen(env, wl.SHORT.with_(H=4, T=9))
