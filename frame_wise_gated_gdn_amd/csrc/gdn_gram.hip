@@ -25,10 +25,12 @@
 // 32-token chunk hold tokens 4g..4g+3 and 16+4g..16+4g+3.  Its accumulator
 // C(L, I) for 16-key blocks L and I therefore holds, in lane (b, g),
 // G[16L + 4g + r][16I + b] for r = 0..3.  G is symmetric, so only the blocks
-// (I, L) with I >= L are stored, each as a row-major 16 x 16 bf16 tile
-// (512 bytes): by symmetry block (I, L) is C(L, I) read with rows and columns
-// swapped, which makes lane (b, g) own the 8 contiguous bytes at b*32 + g*8 --
-// one coalesced 512-byte store.  The state pass uses the k-slot order over
+// (I, L) with I >= L are stored, each as a 16 x 16 bf16 tile of 512 bytes in
+// which the 4 elements (row x, columns 4c..4c+3) sit at byte (16c + x) * 8:
+// by symmetry block (I, L) is C(L, I) read with rows and columns swapped, so
+// lane l = 16g + b of C(L, I) owns exactly bytes 8l..8l+7 of block (I, L) --
+// one store of 512 contiguous bytes in lane order.  The state pass uses the
+// k-slot order over
 // keys in which slot e of lane group g in k-step kb is key
 // 32kb + 16(e/4) + 4g + e%4.  Its A operand for output block I and k-step kb
 // takes, in lane (a, g), row a, columns 4g..4g+3 of the blocks (I, 2kb) and
@@ -208,8 +210,9 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   }
 
   // B blocks in accumulator layout scaled by c; G blocks (I, L), I >= L,
-  // row-major scaled by c^2: lane (b, g) owns row b, columns 4g..4g+3 of the
-  // block, i.e. the values of C(L, I).
+  // scaled by c^2: lane l = 16g + b owns row b, columns 4g..4g+3 of the block
+  // (the values of C(L, I)) at bytes 8l..8l+7.  Both are written with
+  // non-temporal stores: the state pass reads them long after this kernel.
   const size_t fh = (size_t)bh * a.Tc + tl;
   unsigned char* gout = (unsigned char*)a.gfr + fh * Sh::g_frame_bytes;
   unsigned char* bout = (unsigned char*)a.bfr + fh * Sh::b_frame_bytes;
@@ -219,10 +222,10 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
     const f32x4 x = acc[i];
     if constexpr (b < NBB) {
       const u32x2 v = {pack_bf16(c1 * x[0], c1 * x[1]), pack_bf16(c1 * x[2], c1 * x[3])};
-      *(u32x2*)(bout + (size_t)b * 512 + l * 8) = v;
+      __builtin_nontemporal_store(v, (u32x2*)(bout + (size_t)b * 512 + l * 8));
     } else {
       const u32x2 v = {pack_bf16(c2 * x[0], c2 * x[1]), pack_bf16(c2 * x[2], c2 * x[3])};
-      *(u32x2*)(gout + (size_t)(b - NBB) * 512 + n * 32 + g * 8) = v;
+      __builtin_nontemporal_store(v, (u32x2*)(gout + (size_t)(b - NBB) * 512 + l * 8));
     }
   });
 }
@@ -341,12 +344,13 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
     if constexpr (L >= NB) {
       return u32x2{0u, 0u};
     } else if constexpr (L <= I) {
-      return *(const u32x2*)(gs + (size_t)(I * (I + 1) / 2 + L) * 512 + n * 32 + g * 8);
+      return *(const u32x2*)(gs + (size_t)(I * (I + 1) / 2 + L) * 512 + l * 8);
     } else {
       // block (I, L) = transpose of the stored block (L, I): column n of its
-      // rows 4g..4g+3, through a transposed read
+      // rows 4g..4g+3, through a transposed read in which lane j of the
+      // 16-lane group supplies row 4g + j/4, columns 4(j%4)..+3
       const unsigned char* blk = gs + (size_t)(L * (L + 1) / 2 + I) * 512;
-      return lds_tr16((const uint16_t*)(blk + (4 * g + (n >> 2)) * 32 + (n & 3) * 8));
+      return lds_tr16((const uint16_t*)(blk + ((n & 3) * 16 + 4 * g + (n >> 2)) * 8));
     }
   };
 
