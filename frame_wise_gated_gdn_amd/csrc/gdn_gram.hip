@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -244,6 +246,200 @@ __global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_bf16_kernel
 }
 
 // ----------------------------------------------------------------------------
+// Gram pass, streaming form (used when a frame has enough chunks, see
+// gram_stream_ok).  A persistent workgroup walks the (head, frame) pairs
+// fh = wg, wg + G, ... of the launch, and all their chunks as one sequence, so
+// the K/V prefetch runs across frame boundaries.  A finished frame's G and B
+// go to an LDS staging buffer; during the next frame each wave copies one
+// 1 KB piece of it to HBM per chunk.  Loads and stores share one in-order
+// counter per wave: a load issued after a store can only be waited for once
+// that store is done, so the stores are kept small, spread out and at least
+// kGramRing chunks ahead of any load that is waited for -- writing a whole
+// frame's output at once (the per-frame kernel above) stalls the load stream
+// behind it.  The loop is branch-free except for the compute of real chunks
+// and the frame-end staging, which hold no global memory operations.
+// ----------------------------------------------------------------------------
+template <int D>
+struct GramStream {
+  using Sh = GramShape<D>;
+  static constexpr int GB = Sh::NBLK * 512;                  // G bytes per frame-head
+  static constexpr int BB = Sh::NBB * 512;                   // B bytes per frame-head
+  static constexpr int NGG = (GB + 1023) / 1024;             // 1 KB pieces of G
+  static constexpr int NGB = (BB + 1023) / 1024;             // 1 KB pieces of B
+  static constexpr int NP = NGG + NGB;                       // pieces per frame-head
+  static constexpr size_t stage_off = Sh::lds_bytes;         // after the K/V tiles
+  static constexpr size_t lds_bytes = stage_off + (size_t)NP * 1024;
+};
+
+// The staging buffer of a frame is fully copied out within ceil(NP/NW) chunks
+// of the next frame, and a barrier must separate the last copy from the next
+// frame-end staging.
+template <int D>
+constexpr int gram_stream_min_chunks() {
+  return (GramStream<D>::NP + GramShape<D>::NW - 1) / GramShape<D>::NW + 1;
+}
+// ... and two workgroups must fit a CU's 160 KB of LDS (the per-frame kernel
+// serves the head dims where they do not).
+template <int D>
+constexpr bool gram_stream_fits() {
+  return 2 * GramStream<D>::lds_bytes <= 160 * 1024;
+}
+
+template <int D, int W>
+__device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned char* smem) {
+  using Sh = GramShape<D>;
+  using St = GramStream<D>;
+  constexpr int NB = Sh::NB, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, RS = Sh::RS;
+  constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT, NGG = St::NGG, NP = St::NP;
+  constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
+  constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  const int S = a.S, T = a.T, Tc = a.Tc;
+  const int G = (int)gridDim.x, wg = (int)blockIdx.x, nfh = a.BH * Tc;
+  const int nmine = wg < nfh ? (nfh - wg + G - 1) / G : 0;
+  const int nch = (S + 31) / 32;
+  const int total = nmine * nch;
+  const int nit = (total + kGramRing - 1) / kGramRing * kGramRing;
+  const uint32_t frame_bytes = (uint32_t)S * D * 2u;
+  unsigned char* stage_buf = smem + St::stage_off;
+
+  // Uniform conditions that decide whether a memory operation is real are
+  // taken through a vector register, so that they become per-lane offset
+  // selects instead of branches around the memory operation (a branch around
+  // a load or store would make the compiler drain the whole counter).
+  auto vgpr = [](int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  int lk = 0, lch = 0;   // next chunk to load: frame lk of this workgroup, chunk lch
+  auto load_next = [&](u32x4 (&X)[LPW]) {
+    const int kk = lk < nmine ? lk : nmine - 1;          // a valid frame for the addresses
+    const bool valid = vgpr(lk) < nmine;
+    const int fh = wg + kk * G, bh = fh / Tc, tl = fh - bh * Tc;
+    const size_t fe = ((size_t)bh * T + a.t0 + tl) * (size_t)S * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + fe, frame_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + fe, frame_bytes);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int p = W + NW * i;
+      const int u = 64 * (p % NLD) + l;
+      const int tok = lch * 32 + u / UPR;
+      const bool ok = valid && p < 2 * NLD && tok < S;
+      // offset past the buffer when !ok, by arithmetic (no select to branch on)
+      const uint32_t off = (uint32_t)(lch * 32 * UPR + u) * 16u | ((uint32_t)!ok << 31);
+      X[i] = buf_load16(p < NLD ? krs : vrs, off);
+    }
+    const bool wrap = lch + 1 == nch;
+    lch = wrap ? 0 : lch + 1;
+    lk += wrap ? 1 : 0;
+  };
+  auto stage = [&](int buf, const u32x4 (&X)[LPW]) {
+    uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
+    uint16_t* vt = kt + 32 * RS;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int p = W + NW * i;
+      if (p < 2 * NLD) {
+        const int u = 64 * (p % NLD) + l;
+        uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
+        *(u32x4*)dst = p < NLD ? relu8(X[i]) : X[i];
+      }
+    }
+  };
+  auto frag = [&](const uint16_t* tile, int blk) -> u32x4 {
+    const uint16_t* p0 = tile + (4 * g + (n >> 2)) * RS + 16 * blk + 4 * (n & 3);
+    const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
+    return u32x4{x[0], x[1], y[0], y[1]};
+  };
+  // copy piece p of the staged frame k to its place in HBM (out-of-range
+  // lanes, pieces and frames go to an offset past the buffer: no branch)
+  auto store_piece = [&](int k, int p) {
+    const int pp = p < NP ? p : 0;
+    const int kk = k < 0 ? 0 : (k < nmine ? k : nmine - 1);
+    const int kv = vgpr(k), pv = vgpr(p);
+    const bool valid = kv >= 0 && kv < nmine && pv < NP;
+    const u32x4 v = *(const u32x4*)(stage_buf + (size_t)pp * 1024 + l * 16);
+    const size_t fh = (size_t)wg + (size_t)kk * G;
+    const bool isg = pp < NGG;
+    const __amdgpu_buffer_rsrc_t ors =
+        isg ? make_rsrc((unsigned char*)a.gfr + fh * Sh::g_frame_bytes, (uint32_t)St::GB)
+            : make_rsrc((unsigned char*)a.bfr + fh * Sh::b_frame_bytes, (uint32_t)St::BB);
+    const uint32_t off = (uint32_t)((isg ? pp : pp - NGG) * 1024 + l * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ors, valid ? off : kOOB, 0, 2 /* nt */);
+  };
+  const float c2 = a.kscale2, c1 = a.kscale;
+
+  f32x4 acc[NMB];
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 R[kGramRing][LPW];
+#pragma unroll
+  for (int r = 0; r < kGramRing; ++r) load_next(R[r]);
+
+  int ck = 0, cch = 0;   // chunk being computed: frame ck of this workgroup, chunk cch
+  for (int base = 0; base < nit; base += kGramRing) {
+#pragma unroll
+    for (int r = 0; r < kGramRing; ++r) {
+      const int q = base + r;
+      stage(r & 1, R[r]);
+      load_next(R[r]);
+      lds_barrier();
+      // the previous frame's output, one piece per wave and chunk
+      store_piece(ck - 1, cch * NW + W);
+      if (q < total) {
+        const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
+        const uint16_t* vt = kt + 32 * RS;
+        u32x4 X[NB], Y[NB];
+        static_for<NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
+          if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
+        });
+        static_for<NMB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value, b = B0 + i;
+          if constexpr (b < NBB) {
+            acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
+          } else {
+            constexpr int k = b - NBB;
+            acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+          }
+        });
+        if (cch == nch - 1) {
+          // frame complete: stage its blocks (B scaled by c, G by c^2, as in
+          // the per-frame kernel) and start the next frame
+          static_for<NMB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, b = B0 + i;
+            const f32x4 x = acc[i];
+            const float cc = b < NBB ? c1 : c2;
+            const u32x2 v = {pack_bf16(cc * x[0], cc * x[1]), pack_bf16(cc * x[2], cc * x[3])};
+            const size_t so = b < NBB ? (size_t)NGG * 1024 + (size_t)b * 512 : (size_t)(b - NBB) * 512;
+            *(u32x2*)(stage_buf + so + l * 8) = v;
+            acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          });
+        }
+        const bool wrap = cch + 1 == nch;
+        cch = wrap ? 0 : cch + 1;
+        ck += wrap ? 1 : 0;
+      }
+    }
+  }
+  // the last frame's output
+  lds_barrier();
+  for (int p = W; p < NP; p += NW) store_piece(nmine - 1, p);
+}
+
+template <int D>
+__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_stream_bf16_kernel(GramArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  static_for<GramShape<D>::NW>([&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    if (w == W) gram_stream_wave<D, W>(a, smem);
+  });
+}
+
+// ----------------------------------------------------------------------------
 // State pass.  One workgroup per (head, 16-wide value tile j), placed so that
 // the tiles of a head share an XCD (they read the same G_t).  Wave I owns the
 // 16 x 16 block M[16I..16I+15][16j..16j+15] in fp32 registers.  Per frame it
@@ -424,14 +620,34 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
 template <int D>
 static hipError_t launch_gram_t(const GramArgs& ga, hipStream_t stream) {
   static bool attr_set = false;   // benign race: every setter writes the same value
+  static int slots = 0;            // resident workgroups of the streaming kernel on the device
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_bf16_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gdn_gram_stream_bf16_kernel<D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramStream<D>::lds_bytes);
+    int dev = 0, cus = 0, per_cu = 0;
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)gdn_gram_stream_bf16_kernel<D>,
+                                                       GramShape<D>::NW * 64, GramStream<D>::lds_bytes);
     if (e != hipSuccess) return e;
+    slots = std::max(1, per_cu) * cus;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gdn_gram_bf16_kernel<D>), dim3(ga.BH * ga.Tc), dim3(GramShape<D>::NW * 64),
-                     GramShape<D>::lds_bytes, stream, ga);
+  const long long nfh = (long long)ga.BH * ga.Tc;
+  const int nch = (ga.S + 31) / 32;
+  if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {
+    // persistent: one workgroup per resident slot
+    const int grid = (int)std::min<long long>(nfh, slots);
+    hipLaunchKernelGGL((gdn_gram_stream_bf16_kernel<D>), dim3(grid), dim3(GramShape<D>::NW * 64),
+                       GramStream<D>::lds_bytes, stream, ga);
+  } else {
+    hipLaunchKernelGGL((gdn_gram_bf16_kernel<D>), dim3((unsigned)nfh), dim3(GramShape<D>::NW * 64),
+                       GramShape<D>::lds_bytes, stream, ga);
+  }
   return hipGetLastError();
 }
 

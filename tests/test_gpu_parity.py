@@ -275,6 +275,22 @@ def test_streaming_long_chunks_bitwise(env):
     check(env, inp, o1, st1, run_oracle(env, inp, state=s0, want_norms=True), TOL["bf16"], norms=n1)
 
 
+@pytest.mark.parametrize("B,H,T,S,D", [(1, 3, 7, 400, 112), (2, 2, 5, 352, 96), (1, 5, 33, 290, 64),
+                                        (1, 2, 9, 1000, 48)])
+def test_streaming_gram_kernel_shapes(env, B, H, T, S, D):
+    """Frames long enough for the persistent gram kernel (output staged in LDS,
+    written during the next frame): ragged last chunks, fewer frame-heads than
+    workgroups, several frames per workgroup; both beta modes."""
+    torch, gdn, wl, go = env
+    w = wl.Workload("gstream", B, H, T, S, D, gamma=(0.8, 1.0), beta=(0.0, 1.0))
+    inp = gen(env, w)
+    for mode in ("erase", "write"):
+        out, st, nm = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], beta_mode=mode,
+                                        want_norms=True)
+        torch.cuda.synchronize()
+        check(env, inp, out, st, run_oracle(env, inp, mode=mode, want_norms=True), TOL["bf16"], norms=nm)
+
+
 def test_repeat_runs_are_bitwise_equal(env):
     torch, gdn, wl, go = env
     inp = gen(env, wl.SHORT.with_(H=4, T=9))
