@@ -10,6 +10,12 @@ oracle's CPU rate on a bounded sample.
 The default bf16 path is the Gram pipeline (gram pass, serial state pass,
 readout); --path direct times the single-pass recurrence instead.
 
+Timing: `value` and `ms_per_step` come from K plain steps between two device
+synchronisations.  The per-kernel device times come from a second run of the
+same K steps in which the library brackets every launch with HIP events on the
+stream it runs on (the events cost a little, reported as
+`ms_per_step_with_kernel_events`).
+
 Roofline bookkeeping (algorithmic bytes only; the per-frame G/B staging, the
 state snapshots and any re-reads are overhead, not algorithm):
   whole path   8*D bytes per token-head (Q, K, V read; O written, bf16)
@@ -115,13 +121,21 @@ def main():
     for _ in range(args.warmup):
         call(False)
     torch.cuda.synchronize()
+    # throughput: K plain steps (no per-kernel events between the launches)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call(False)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    # per-kernel device time: the same K steps again, each launch bracketed by
+    # HIP events on the stream it runs on
     gdn.kernel_times(reset=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for _ in range(args.steps):
         call(True)
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    dt_ev = time.perf_counter() - t1
     ktimes = gdn.kernel_times(reset=True)
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -171,6 +185,7 @@ def main():
                           "frac": path_gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes,
                           "mfma_frac": path_flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
         "kernels_ms_per_step": kms,
+        "ms_per_step_with_kernel_events": dt_ev * 1e3 / args.steps,
     }
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)

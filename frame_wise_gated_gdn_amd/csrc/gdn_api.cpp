@@ -183,12 +183,31 @@ size_t frames_per_launch(const Plan& p, int T, size_t wb) {
 // at default priority and kept for the life of the process, with a small ring
 // of events.  An event is recorded again only after every wait on its
 // previous record has been enqueued (the enqueue order below guarantees it).
-constexpr int kStateSplit = 4;             // state/readout sub-ranges per gram range
-constexpr int kMinSplitFrames = 64;        // frames per sub-range at least
+constexpr int kStateSplit = 6;          // state/readout sub-ranges per gram range (at most)
+constexpr int kMinSplitFrames = 32;     // frames per sub-range at least
+constexpr double kStateGrow = 1.4;      // size ratio of consecutive sub-ranges
 struct SideStream {
   hipStream_t stream = nullptr;
-  hipEvent_t ev[2 * kStateSplit + 2] = {};
+  hipEvent_t ev[kStateSplit + 2] = {};
 };
+
+// Sub-range boundaries bnd[0] = 0 < ... < bnd[n] = tc of a gram range, sizes
+// growing by kStateGrow.  The state pass of the first sub-range runs alone, so
+// it is kept short; the state of sub-range i+1 runs next to the readout of
+// sub-range i, which is HBM-bound and takes longer per frame than the state
+// pass does, so the later sub-ranges can grow without stalling the readouts.
+// Returns n.
+int split_frames(int tc, int bnd[kStateSplit + 1]) {
+  const int n = std::max(1, std::min(kStateSplit, tc / kMinSplitFrames));
+  const double rn = std::pow(kStateGrow, n);
+  bnd[0] = 0;
+  for (int i = 1; i < n; ++i) {
+    const double frac = kStateGrow == 1.0 ? (double)i / n : (std::pow(kStateGrow, i) - 1.0) / (rn - 1.0);
+    bnd[i] = std::max(bnd[i - 1] + 1, (int)std::lround(tc * frac));
+  }
+  bnd[n] = tc;
+  return n;
+}
 thread_local std::vector<SideStream*> t_side;   // by device id
 
 hipError_t side_stream(SideStream** out) {
@@ -239,7 +258,8 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
   for (int t0 = 0; t0 < d->T && e == hipSuccess; t0 += (int)F) {
     failed_t0 = t0;
     const int tc = (int)std::min<size_t>(F, (size_t)(d->T - t0));
-    const int nsub = std::max(1, std::min(kStateSplit, tc / kMinSplitFrames));
+    int bnd[kStateSplit + 1];
+    const int nsub = split_frames(tc, bnd);
     gdn::GramArgs ga;
     ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
     ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
@@ -256,7 +276,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
     }
     // state sub-ranges (side stream), then their readouts (caller's stream)
     for (int i = 0; i < nsub && e == hipSuccess; ++i) {
-      const int f0 = (int)((long long)tc * i / nsub), f1 = (int)((long long)tc * (i + 1) / nsub);
+      const int f0 = bnd[i], f1 = bnd[i + 1];
       gdn::StateArgs sa;
       sa.gfr = gfr; sa.bfr = bfr; sa.gamma = x.gamma; sa.beta = x.beta;
       sa.state_src = (t0 == 0 && i == 0) ? x.state_in : hand;
@@ -268,7 +288,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
       if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
     }
     for (int i = 0; i < nsub && e == hipSuccess; ++i) {
-      const int f0 = (int)((long long)tc * i / nsub), f1 = (int)((long long)tc * (i + 1) / nsub);
+      const int f0 = bnd[i], f1 = bnd[i + 1];
       if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + i], 0);
       gdn::ReadoutArgs ro;
       ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = nullptr;
@@ -281,7 +301,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
   if (e != hipSuccess) {
     // keep the caller's stream ordered after anything already on the side stream
     if (ss) {
-      const int last = 2 * kStateSplit + 1;
+      const int last = kStateSplit + 1;
       if (hipEventRecord(ss->ev[last], ss->stream) == hipSuccess) (void)hipStreamWaitEvent(s, ss->ev[last], 0);
     }
     return fail(GDN_ERR_HIP, "kernel launch (frames from %d): %s", failed_t0, hipGetErrorString(e));

@@ -86,8 +86,16 @@ constexpr int kBufWord3 = 0x00020000;       // gfx9 buffer descriptor word 3 (ra
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
 }
+// Cache-policy bits of a buffer instruction: kNT marks data that is touched
+// once (Q, K, V, O, the per-frame B_t tiles) as streaming.  Under heavy read
+// traffic it measurably lowers the cost of the passes' own stores, which
+// otherwise compete with the streamed lines for L2 residency.
+constexpr int kNT = 2;
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
 }
 // LDS-only workgroup barrier: waits for this wave's LDS operations, not for
 // its outstanding global loads.

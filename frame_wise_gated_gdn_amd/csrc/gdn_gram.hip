@@ -150,7 +150,7 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
       const int tok = ch * 32 + u / UPR;
       const bool ok = p < 2 * NLD && ch < nch && tok < S;
       const uint32_t off = ok ? fbyte + (uint32_t)(ch * 32 * UPR + u) * 16u : kOOB;
-      X[i] = buf_load16(p < NLD ? krs : vrs, off);
+      X[i] = buf_load16_nt(p < NLD ? krs : vrs, off);
     }
   };
   auto stage = [&](int buf, const u32x4 (&X)[LPW]) {
@@ -327,7 +327,7 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
       const bool ok = valid && p < 2 * NLD && tok < S;
       // offset past the buffer when !ok, by arithmetic (no select to branch on)
       const uint32_t off = (uint32_t)(lch * 32 * UPR + u) * 16u | ((uint32_t)!ok << 31);
-      X[i] = buf_load16(p < NLD ? krs : vrs, off);
+      X[i] = buf_load16_nt(p < NLD ? krs : vrs, off);
     }
     const bool wrap = lch + 1 == nch;
     lch = wrap ? 0 : lch + 1;
@@ -365,7 +365,7 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
         isg ? make_rsrc((unsigned char*)a.gfr + fh * Sh::g_frame_bytes, (uint32_t)St::GB)
             : make_rsrc((unsigned char*)a.bfr + fh * Sh::b_frame_bytes, (uint32_t)St::BB);
     const uint32_t off = (uint32_t)((isg ? pp : pp - NGG) * 1024 + l * 16);
-    __builtin_amdgcn_raw_buffer_store_b128(v, ors, valid ? off : kOOB, 0, 2 /* nt */);
+    __builtin_amdgcn_raw_buffer_store_b128(v, ors, valid ? off : kOOB, 0, kNT);
   };
   const float c2 = a.kscale2, c1 = a.kscale;
 
@@ -525,7 +525,7 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
       Gr[r][i] = buf_load16(grs, (ok && q < NGL) ? (uint32_t)f * (uint32_t)gfb + q * 1024 + l * 16 : kOOB);
     }
     Bf[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                          brs, ok ? bbase + (uint32_t)f * (uint32_t)bfb : kOOB, 0, 0));
+                                          brs, ok ? bbase + (uint32_t)f * (uint32_t)bfb : kOOB, 0, kNT));
   };
   auto stage_g = [&](int slot, int r) {
 #pragma unroll

@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
   auto load_chunk = [&](int i, u32x4 (&X)[NLD]) {
     const int ch = w + kReadWaves * i;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) X[j] = buf_load16(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
+    for (int j = 0; j < NLD; ++j) X[j] = buf_load16_nt(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
   };
 
   // A operands: M_t^T rows (value column 16jb + n); k-step kc holds keys
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
       for (int j = 0; j < NLD; ++j) {
         const int u = 64 * j + l;
         const u32x4 y = *(const u32x4*)(os + (u / UPR) * RS + 8 * (u % UPR));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ors, i < NC ? unit_off(ch, u) : kOOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ors, i < NC ? unit_off(ch, u) : kOOB, 0, kNT);
       }
     }
   }
