@@ -546,18 +546,19 @@ __global__ __launch_bounds__(kReadWaves * 64) void gdn_readout_f32_kernel(Readou
 // bf16 readout.  One workgroup per (head, frame); every wave holds M_t^T as A
 // operands and walks 32-token chunks of the frame.  Q chunks are read with
 // fully coalesced 16-byte loads (a chunk is 32*D contiguous bf16), kept
-// kReadRing chunks ahead in registers, passed through ReLU and staged in the
+// RING chunks ahead in registers, passed through ReLU and staged in the
 // wave's LDS tile, from which the B operands (token n, 8 consecutive keys) are
 // read.  The O chunk is assembled in a second LDS tile and written back with
 // the same coalesced pattern.  Out-of-range lanes use an offset beyond the
 // buffer: their loads read zeros and their stores are dropped, so the loop is
 // branch-free and its wait counts are exact.
 // ----------------------------------------------------------------------------
-constexpr int kReadRing = 3;
-
 template <int D>
 struct ReadShape {
   static constexpr int NB = D / 16, NKC = (D + 31) / 32;
+  // Q chunks in flight per wave: at D = 128 the A operands alone take 128
+  // registers and a third chunk would spill
+  static constexpr int RING = D >= 128 ? 2 : 3;
   static constexpr int UPR = D / 8;              // 16-byte units per token row
   static constexpr int NLD = D / 16;             // 1 KB loads per 32-token chunk (= 32*UPR/64)
   static constexpr int RS = D + 8;               // LDS row stride (elements)
@@ -616,9 +617,10 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
                                          : u32x2{0u, 0u};
       A[jb][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
-  u32x4 X[kReadRing][NLD];
+  constexpr int RING = Sh::RING;
+  u32x4 X[RING][NLD];
 #pragma unroll
-  for (int r = 0; r < kReadRing; ++r) load_chunk(r, X[r]);
+  for (int r = 0; r < RING; ++r) load_chunk(r, X[r]);
   // The snapshot loads were issued first: one use of the last of them makes
   // the compiler wait for all of them here, once, instead of inside the loop.
   asm volatile("" ::"v"(A[NB - 1][NKC - 1]));
@@ -640,9 +642,9 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
     if (l == 0) a.norms[(size_t)bh * T + t] = sqrtf(sq);
   }
 
-  for (int base = 0; base < NC; base += kReadRing) {
+  for (int base = 0; base < NC; base += RING) {
 #pragma unroll
-    for (int r = 0; r < kReadRing; ++r) {
+    for (int r = 0; r < RING; ++r) {
       const int i = base + r;
       const int ch = w + kReadWaves * i;
       // stage ReLU(Q) of the chunk (row-major, padded rows)
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
         const int u = 64 * j + l;
         *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(X[r][j]);
       }
-      load_chunk(i + kReadRing, X[r]);
+      load_chunk(i + RING, X[r]);
       wave_lds_sync();
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
