@@ -5,7 +5,9 @@ One step = one gdn_frame_forward call over the whole minute-scale 720p-shaped
 workload (B1 H20 T961 S880 D112, bf16 I/O, fp32 state, ERASE mode), inputs
 already resident in HBM.  Prints ONE JSON line with tokens/s (B*H*T*S per
 second), the roofline of the dominant kernel, the whole-path roofline and the
-oracle's CPU rate on a bounded sample.
+oracle's CPU rate on a bounded sample.  A `streaming` field adds the
+chunk-causal rollout check: the short-clip shape (B1 H16 T81 S880 D64) fed 4
+frames per gdn_frame_step call, its per-chunk latency and back-to-back rate.
 
 The default bf16 path is the Gram pipeline (gram pass, serial state pass,
 readout); --path direct times the single-pass recurrence instead.
@@ -85,12 +87,54 @@ def cpu_baseline(w, inp, heads: int):
                       f"{dt:.1f} s wall, fp64, OpenMP {threads} threads"}
 
 
+def streaming_latency(gdn, wl, torch, dev, reps: int):
+    """Chunk-causal rollout of the short-clip shape, 4 frames per gdn_frame_step call
+    with the state committed in place: per-chunk latency (enqueue to completion,
+    one chunk at a time) and the per-chunk time of back-to-back chunks."""
+    w = wl.CHUNKED
+    inp = wl.generate(w, device=dev)
+    T, c = w.T, w.chunk
+    chunks = [tuple(inp[n][:, :, t0:min(T, t0 + c)].contiguous() for n in ("q", "k", "v", "gamma", "beta"))
+              for t0 in range(0, T, c)]
+    outs = [torch.empty_like(ch[0]) for ch in chunks]
+    state = torch.zeros((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    desc = gdn.make_desc(w.B, w.H, c, w.S, w.D, w.dtype, w.beta_mode)
+    ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
+
+    def rollout(sync_each):
+        state.zero_()
+        lat = []
+        for ch, o in zip(chunks, outs):
+            t0 = time.perf_counter()
+            gdn.frame_step(*ch, state, beta_mode=w.beta_mode, out=o, commit="inplace", workspace=ws)
+            if sync_each:
+                torch.cuda.synchronize()
+                if ch[0].shape[2] == c:
+                    lat.append(time.perf_counter() - t0)
+        return lat
+
+    rollout(True)
+    lat = sorted(x for _ in range(reps) for x in rollout(True))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rollout(False)
+    torch.cuda.synchronize()
+    per_chunk = (time.perf_counter() - t0) / (reps * len(chunks))
+    return {"workload": w.name, "frames_per_chunk": c, "chunks_per_rollout": len(chunks), "rollouts": reps,
+            "latency_us_median": lat[len(lat) // 2] * 1e6, "latency_us_p90": lat[int(len(lat) * 0.9)] * 1e6,
+            "back_to_back_us_per_chunk": per_chunk * 1e6,
+            "back_to_back_tokens_per_s": w.B * w.H * w.T * w.S / (per_chunk * len(chunks))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=12, help="oracle heads timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--stream-reps", type=int, default=5,
+                    help="rollouts of the chunk-causal streaming latency check (0 = skip)")
     ap.add_argument("--path", choices=("auto", "direct"), default="auto",
                     help="bf16 path: Gram pipeline (auto) or single-pass recurrence (direct)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -187,6 +231,8 @@ def main():
         "kernels_ms_per_step": kms,
         "ms_per_step_with_kernel_events": dt_ev * 1e3 / args.steps,
     }
+    if args.stream_reps > 0:
+        rec["streaming"] = streaming_latency(gdn, wl, torch, dev, args.stream_reps)
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(rec), flush=True)
