@@ -8,6 +8,9 @@ second), the roofline of the dominant kernel, the whole-path roofline and the
 oracle's CPU rate on a bounded sample.  A `streaming` field adds the
 chunk-causal rollout check: the short-clip shape (B1 H16 T81 S880 D64) fed 4
 frames per gdn_frame_step call, its per-chunk latency and back-to-back rate.
+A `variants` field times the same 720p-shaped step with OCP E4M3 Q, K, V, O
+(the low-precision I/O variant, 4*D bytes per token-head); the headline
+`value` stays the bf16 step.
 
 The default bf16 path is the Gram pipeline (gram pass, serial state pass,
 readout); --path direct times the single-pass recurrence instead.
@@ -127,12 +130,47 @@ def streaming_latency(gdn, wl, torch, dev, reps: int):
             "back_to_back_tokens_per_s": w.B * w.H * w.T * w.S / (per_chunk * len(chunks))}
 
 
+def fp8_variant(gdn, wl, torch, dev, steps: int, warmup: int):
+    """The same 720p-shaped step with OCP E4M3 Q, K, V and O (the low-precision
+    I/O variant): 4*D bytes per token-head instead of 8*D."""
+    w = wl.MINUTE_720P.with_(dtype="fp8")
+    inp = wl.generate(w, device=dev)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode)
+    ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["q"])
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    call = lambda timed: gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
+                                           beta_mode=w.beta_mode, out=out, state_out=st, workspace=ws,
+                                           time_kernels=timed)
+    for _ in range(warmup):
+        call(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call(False)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gdn.kernel_times(reset=True)
+    for _ in range(steps):
+        call(True)
+    torch.cuda.synchronize()
+    kms = {name: t / steps for name, (t, n) in gdn.kernel_times(reset=True).items() if n > 0}
+    path_bytes = w.B * w.H * w.T * w.S * 4 * w.D
+    gbs = path_bytes / (ms * 1e-3) / 1e9
+    return {"io_dtype": "fp8_e4m3 (OCP)", "workload": w.name, "value": w.tokens / (ms * 1e-3),
+            "unit": "tokens/s", "ms_per_step": ms, "kernels_ms_per_step": kms,
+            "path_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=12, help="oracle heads timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-fp8", dest="fp8", action="store_false",
+                    help="skip the E4M3 I/O variant of the step")
     ap.add_argument("--stream-reps", type=int, default=5,
                     help="rollouts of the chunk-causal streaming latency check (0 = skip)")
     ap.add_argument("--path", choices=("auto", "direct"), default="auto",
@@ -233,6 +271,8 @@ def main():
     }
     if args.stream_reps > 0:
         rec["streaming"] = streaming_latency(gdn, wl, torch, dev, args.stream_reps)
+    if args.fp8 and args.path == "auto":
+        rec["variants"] = {"fp8_e4m3_io": fp8_variant(gdn, wl, torch, dev, args.steps, args.warmup)}
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(rec), flush=True)

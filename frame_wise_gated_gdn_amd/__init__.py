@@ -5,7 +5,7 @@ The recurrence runs in hand-written gfx950 HIP kernels behind the C ABI of
 ctypes binding and the seeded synthetic workloads.  PyTorch only provides
 device memory and streams.
 """
-from .binding import (ABI_VERSION, BF16, ERASE, F32, WRITE, Desc, GDNError, check_args,  # noqa: F401
+from .binding import (ABI_VERSION, BF16, ERASE, F32, FP8, WRITE, Desc, GDNError, check_args,  # noqa: F401
                       frame_forward, frame_step, kernel_times, lib, make_desc, workspace_min_size,
                       workspace_size)
 

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdn.so")
 
 ABI_VERSION = 1
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2          # gdn_dtype; FP8 = OCP E4M3
 ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
 FLAG_DIRECT = 0x2
@@ -80,7 +80,7 @@ def lib() -> ctypes.CDLL:
 
 def make_desc(B, H, T, S, D, io_dtype, beta_mode="erase", flags=0, abi_version=ABI_VERSION) -> Desc:
     mode = {"erase": ERASE, "write": WRITE}.get(beta_mode, beta_mode)
-    dt = {"bf16": BF16, "f32": F32}.get(io_dtype, io_dtype)
+    dt = {"bf16": BF16, "f32": F32, "fp8": FP8}.get(io_dtype, io_dtype)
     return Desc(abi_version, B, H, T, S, D, dt, mode, flags)
 
 
@@ -134,8 +134,10 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
         io = BF16
     elif q.dtype == torch.float32:
         io = F32
+    elif q.dtype == torch.float8_e4m3fn:
+        io = FP8
     else:
-        raise TypeError("q, k, v must be bfloat16 or float32")
+        raise TypeError("q, k, v must be bfloat16, float32 or float8_e4m3fn")
     for name, t in (("k", k), ("v", v)):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{name} must match q in shape and dtype")
@@ -168,7 +170,7 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
 def frame_forward(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None, state_out=None,
                   norms=None, want_state=True, want_norms=False, workspace=None, stream=None,
                   time_kernels=False, path="auto"):
-    """Whole-sequence forward.  q, k, v [B,H,T,S,D] (bf16 or fp32), gamma/beta [B,H,T] fp32,
+    """Whole-sequence forward.  q, k, v [B,H,T,S,D] (bf16, fp32 or float8_e4m3fn), gamma/beta [B,H,T] fp32,
     state [B,H,D,D] fp32 or None (zeros).  path="direct" selects the single-pass
     recurrence for bf16 (GDN_FLAG_DIRECT).  Returns (o, state_out, norms)."""
     import torch

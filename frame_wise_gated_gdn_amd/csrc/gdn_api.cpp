@@ -37,7 +37,7 @@ using gdn::kMaxFramesPerLaunch;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  bool gram;                      // bf16 Gram pipeline (else the single-pass recurrence)
+  bool gram;                      // Gram pipeline, bf16 or e4m3 I/O (else the single-pass recurrence)
   size_t bh, esz, nb;
   size_t io_bytes, gb_bytes, state_bytes;
   size_t carrier, snap_frame, norm_frame, gfr_frame, bfr_frame;
@@ -47,14 +47,15 @@ struct Plan {
 Plan make_plan(const gdn_desc* d) {
   Plan p;
   p.bh = (size_t)d->B * (size_t)d->H;
-  p.esz = d->io_dtype == GDN_BF16 ? 2 : 4;
+  p.esz = d->io_dtype == GDN_FP8_E4M3 ? 1 : d->io_dtype == GDN_BF16 ? 2 : 4;
   p.nb = (size_t)d->D / 16;
   p.io_bytes = p.bh * (size_t)d->T * (size_t)d->S * (size_t)d->D * p.esz;
   p.gb_bytes = p.bh * (size_t)d->T * 4;
   p.state_bytes = p.bh * (size_t)d->D * (size_t)d->D * 4;
   p.carrier = round_up(p.state_bytes);
-  p.gram = d->io_dtype == GDN_BF16 && !(d->flags & GDN_FLAG_DIRECT);
-  p.snap_frame = p.bh * (size_t)d->D * (size_t)d->D * p.esz;
+  p.gram = d->io_dtype != GDN_F32 && !(d->flags & GDN_FLAG_DIRECT);
+  // state snapshots: fp32 for fp32 I/O, else bf16
+  p.snap_frame = p.bh * (size_t)d->D * (size_t)d->D * (d->io_dtype == GDN_F32 ? 4 : 2);
   // per-frame staging: the single-pass recurrence writes fp32 norm partials,
   // the Gram pipeline writes G_t and B_t (the readout takes norms from the
   // snapshots)
@@ -73,12 +74,14 @@ gdn_status check_desc(const gdn_desc* d) {
   if (!d) return fail(GDN_ERR_NULL, "desc is NULL");
   if (d->abi_version != GDN_ABI_VERSION)
     return fail(GDN_ERR_ABI, "desc.abi_version %d != library ABI %d", d->abi_version, GDN_ABI_VERSION);
-  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16)
-    return fail(GDN_ERR_DTYPE, "io_dtype %d is not GDN_F32 or GDN_BF16", d->io_dtype);
+  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16 && d->io_dtype != GDN_FP8_E4M3)
+    return fail(GDN_ERR_DTYPE, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_FP8_E4M3", d->io_dtype);
   if (d->beta_mode != GDN_BETA_ERASE && d->beta_mode != GDN_BETA_WRITE)
     return fail(GDN_ERR_DTYPE, "beta_mode %d is not GDN_BETA_ERASE or GDN_BETA_WRITE", d->beta_mode);
   if (d->flags & ~(GDN_FLAG_TIME_KERNELS | GDN_FLAG_DIRECT))
     return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if ((d->flags & GDN_FLAG_DIRECT) && d->io_dtype == GDN_FP8_E4M3)
+    return fail(GDN_ERR_UNSUPPORTED, "GDN_FLAG_DIRECT is for bf16 I/O; e4m3 I/O runs the Gram pipeline only");
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->S < 1 || d->D < 1)
     return fail(GDN_ERR_SHAPE, "B=%d H=%d T=%d S=%d D=%d: every size must be >= 1", d->B, d->H, d->T, d->S, d->D);
   if (d->D % 16 != 0 || d->D > 128)
@@ -264,6 +267,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
     ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
     ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
     ga.kscale = (float)c; ga.kscale2 = (float)(c * c);
+    ga.fp8 = d->io_dtype == GDN_FP8_E4M3;
     e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(d->D, ga, s); });
     hipStream_t st = s;
     if (e == hipSuccess && nsub > 1) {
@@ -293,7 +297,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
       gdn::ReadoutArgs ro;
       ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = nullptr;
       ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0 + f0; ro.Tc = f1 - f0;
-      ro.Fs = tc; ro.f0 = f0;
+      ro.Fs = tc; ro.f0 = f0; ro.fp8 = d->io_dtype == GDN_FP8_E4M3;
       if (e == hipSuccess)
         e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_readout(d->D, true, ro, s); });
     }
@@ -342,7 +346,7 @@ gdn_status run_direct(const gdn_desc* d, const Plan& p, const Ptrs& x, void* wor
     gdn::ReadoutArgs ro;
     ro.q = x.q; ro.o = x.o; ro.snap = snap; ro.norms = x.norms; ro.norm_part = ra.norm_part;
     ro.BH = (int)p.bh; ro.T = d->T; ro.S = d->S; ro.t0 = t0; ro.Tc = tc;
-    ro.Fs = tc; ro.f0 = 0;
+    ro.Fs = tc; ro.f0 = 0; ro.fp8 = 0;
     hipError_t e = launch_timed(timed, GDN_KERNEL_RECURRENCE, s,
                                 [&] { return gdn::launch_recurrence(d->D, bf16, ra, s); });
     if (e == hipSuccess)

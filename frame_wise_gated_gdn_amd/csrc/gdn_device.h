@@ -25,6 +25,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -71,6 +72,25 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// OCP e4m3 (the "fn" variant: exponent bias 7, no infinities, 0x7F and 0xFF
+// are NaN).  v_cvt_pk_f32_fp8 decodes two bytes exactly, and every e4m3 value
+// is also exact in bf16, so eight bytes become eight bf16 with no rounding.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 x) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[0], true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[1], true);
+  return u32x4{pack_bf16(a[0], a[1]), pack_bf16(b[0], b[1]), pack_bf16(c[0], c[1]), pack_bf16(d[0], d[1])};
+}
+// Four floats to four e4m3 bytes, in order: round to nearest even, and a
+// magnitude past the rounding range of the largest finite value (448)
+// becomes NaN (v_cvt_pk_fp8_f32).
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(f32x4 v) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], p, true);
+  return (uint32_t)p;
+}
+
 // XCD-aware unit for this workgroup: units are split into 8 contiguous ranges,
 // range x is served by the workgroups that land on XCD x (ids = x mod 8).
 __device__ __forceinline__ int xcd_unit(int units) {
@@ -97,6 +117,30 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
 }
+// Element format of Q, K, V and O.  The kernels stage every operand as bf16
+// in LDS; they load a tensor in units of 8 elements per lane -- 16 bytes of
+// bf16 or 8 bytes of e4m3 -- and convert the unit on its way to LDS.
+template <bool FP8>
+struct IoFmt;
+template <>
+struct IoFmt<false> {
+  static constexpr uint32_t ebytes = 2;
+  static constexpr uint32_t unit_bytes = 16;
+  using raw = u32x4;
+  __device__ static __forceinline__ raw load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) { return buf_load16_nt(r, off); }
+  __device__ static __forceinline__ u32x4 to_bf16(raw x) { return x; }
+};
+template <>
+struct IoFmt<true> {
+  static constexpr uint32_t ebytes = 1;
+  static constexpr uint32_t unit_bytes = 8;
+  using raw = u32x2;
+  __device__ static __forceinline__ raw load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNT));
+  }
+  __device__ static __forceinline__ u32x4 to_bf16(raw x) { return fp8x8_to_bf16x8(x); }
+};
+
 // LDS-only workgroup barrier: waits for this wave's LDS operations, not for
 // its outstanding global loads.
 __device__ __forceinline__ void lds_barrier() {

@@ -124,36 +124,39 @@ constexpr uint32_t gram_ymask(int NB, int b0, int b1) {
   return m;
 }
 
-template <int D, int W>
+template <int D, bool FP8, int W>
 __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem, int bh, int tl) {
   using Sh = GramShape<D>;
+  using IO = IoFmt<FP8>;
   constexpr int NB = Sh::NB, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, RS = Sh::RS;
   constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT;
   constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
   constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
   const int l = lane_id(), g = l >> 4, n = l & 15;
   const int S = a.S, T = a.T, t = a.t0 + tl;
-  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + (size_t)bh * T * S * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + (size_t)bh * T * S * D, head_bytes);
-  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * 2u;
+  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * IO::ebytes;
+  const size_t head0 = (size_t)bh * T * S * D * IO::ebytes;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc((const unsigned char*)a.k + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const unsigned char*)a.v + head0, head_bytes);
+  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * IO::ebytes;
   const int nch = (S + 31) / 32;
   const int nit = (nch + kGramRing - 1) / kGramRing * kGramRing;
+  using raw = typename IO::raw;
 
   // piece p of a chunk: p < NLD are keys, NLD <= p < 2 NLD values; lane l of
-  // piece p carries 16-byte unit 64 (p mod NLD) + l of the chunk.
-  auto load_chunk = [&](int ch, u32x4 (&X)[LPW]) {
+  // piece p carries 8-element unit 64 (p mod NLD) + l of the chunk.
+  auto load_chunk = [&](int ch, raw (&X)[LPW]) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int p = W + NW * i;
       const int u = 64 * (p % NLD) + l;
       const int tok = ch * 32 + u / UPR;
       const bool ok = p < 2 * NLD && ch < nch && tok < S;
-      const uint32_t off = ok ? fbyte + (uint32_t)(ch * 32 * UPR + u) * 16u : kOOB;
-      X[i] = buf_load16_nt(p < NLD ? krs : vrs, off);
+      const uint32_t off = ok ? fbyte + (uint32_t)(ch * 32 * UPR + u) * IO::unit_bytes : kOOB;
+      X[i] = IO::load_nt(p < NLD ? krs : vrs, off);
     }
   };
-  auto stage = [&](int buf, const u32x4 (&X)[LPW]) {
+  auto stage = [&](int buf, const raw (&X)[LPW]) {
     uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
     uint16_t* vt = kt + 32 * RS;
 #pragma unroll
@@ -162,7 +165,8 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
       if (p < 2 * NLD) {
         const int u = 64 * (p % NLD) + l;
         uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
-        *(u32x4*)dst = p < NLD ? relu8(X[i]) : X[i];
+        const u32x4 x = IO::to_bf16(X[i]);
+        *(u32x4*)dst = p < NLD ? relu8(x) : x;
       }
     }
   };
@@ -178,7 +182,7 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
 #pragma unroll
   for (int i = 0; i < NMB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 R[kGramRing][LPW];
+  raw R[kGramRing][LPW];
 #pragma unroll
   for (int r = 0; r < kGramRing; ++r) load_chunk(r, R[r]);
 
@@ -232,17 +236,16 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   });
 }
 
-template <int D>
-__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_bf16_kernel(GramArgs a) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_kernel(GramArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int fh = blockIdx.x;   // over BH * Tc
   const int bh = fh / a.Tc, tl = fh % a.Tc;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int NW = GramShape<D>::NW;
-  if (w == 0) gram_wave<D, 0>(a, smem, bh, tl);
-  if constexpr (NW > 1) if (w == 1) gram_wave<D, 1>(a, smem, bh, tl);
-  if constexpr (NW > 2) if (w == 2) gram_wave<D, 2>(a, smem, bh, tl);
-  if constexpr (NW > 3) if (w == 3) gram_wave<D, 3>(a, smem, bh, tl);
+  static_for<GramShape<D>::NW>([&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    if (w == W) gram_wave<D, FP8, W>(a, smem, bh, tl);
+  });
 }
 
 // ----------------------------------------------------------------------------
@@ -285,10 +288,12 @@ constexpr bool gram_stream_fits() {
   return 2 * GramStream<D>::lds_bytes <= 160 * 1024;
 }
 
-template <int D, int W>
+template <int D, bool FP8, int W>
 __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned char* smem) {
   using Sh = GramShape<D>;
   using St = GramStream<D>;
+  using IO = IoFmt<FP8>;
+  using raw = typename IO::raw;
   constexpr int NB = Sh::NB, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, RS = Sh::RS;
   constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT, NGG = St::NGG, NP = St::NP;
   constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
@@ -300,7 +305,7 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
   const int nch = (S + 31) / 32;
   const int total = nmine * nch;
   const int nit = (total + kGramRing - 1) / kGramRing * kGramRing;
-  const uint32_t frame_bytes = (uint32_t)S * D * 2u;
+  const uint32_t frame_bytes = (uint32_t)S * D * IO::ebytes;
   unsigned char* stage_buf = smem + St::stage_off;
 
   // Uniform conditions that decide whether a memory operation is real are
@@ -312,13 +317,13 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
     return x;
   };
   int lk = 0, lch = 0;   // next chunk to load: frame lk of this workgroup, chunk lch
-  auto load_next = [&](u32x4 (&X)[LPW]) {
+  auto load_next = [&](raw (&X)[LPW]) {
     const int kk = lk < nmine ? lk : nmine - 1;          // a valid frame for the addresses
     const bool valid = vgpr(lk) < nmine;
     const int fh = wg + kk * G, bh = fh / Tc, tl = fh - bh * Tc;
-    const size_t fe = ((size_t)bh * T + a.t0 + tl) * (size_t)S * D;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + fe, frame_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + fe, frame_bytes);
+    const size_t fe = ((size_t)bh * T + a.t0 + tl) * (size_t)S * D * IO::ebytes;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const unsigned char*)a.k + fe, frame_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const unsigned char*)a.v + fe, frame_bytes);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int p = W + NW * i;
@@ -326,14 +331,14 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
       const int tok = lch * 32 + u / UPR;
       const bool ok = valid && p < 2 * NLD && tok < S;
       // offset past the buffer when !ok, by arithmetic (no select to branch on)
-      const uint32_t off = (uint32_t)(lch * 32 * UPR + u) * 16u | ((uint32_t)!ok << 31);
-      X[i] = buf_load16_nt(p < NLD ? krs : vrs, off);
+      const uint32_t off = (uint32_t)(lch * 32 * UPR + u) * IO::unit_bytes | ((uint32_t)!ok << 31);
+      X[i] = IO::load_nt(p < NLD ? krs : vrs, off);
     }
     const bool wrap = lch + 1 == nch;
     lch = wrap ? 0 : lch + 1;
     lk += wrap ? 1 : 0;
   };
-  auto stage = [&](int buf, const u32x4 (&X)[LPW]) {
+  auto stage = [&](int buf, const raw (&X)[LPW]) {
     uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
     uint16_t* vt = kt + 32 * RS;
 #pragma unroll
@@ -342,7 +347,8 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
       if (p < 2 * NLD) {
         const int u = 64 * (p % NLD) + l;
         uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
-        *(u32x4*)dst = p < NLD ? relu8(X[i]) : X[i];
+        const u32x4 x = IO::to_bf16(X[i]);
+        *(u32x4*)dst = p < NLD ? relu8(x) : x;
       }
     }
   };
@@ -373,7 +379,7 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
 #pragma unroll
   for (int i = 0; i < NMB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 R[kGramRing][LPW];
+  raw R[kGramRing][LPW];
 #pragma unroll
   for (int r = 0; r < kGramRing; ++r) load_next(R[r]);
 
@@ -429,13 +435,13 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
   for (int p = W; p < NP; p += NW) store_piece(nmine - 1, p);
 }
 
-template <int D>
-__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_stream_bf16_kernel(GramArgs a) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_stream_kernel(GramArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   static_for<GramShape<D>::NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    if (w == W) gram_stream_wave<D, W>(a, smem);
+    if (w == W) gram_stream_wave<D, FP8, W>(a, smem);
   });
 }
 
@@ -617,21 +623,21 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
 // ----------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------
-template <int D>
-static hipError_t launch_gram_t(const GramArgs& ga, hipStream_t stream) {
+template <int D, bool FP8>
+static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
   static bool attr_set = false;   // benign race: every setter writes the same value
   static int slots = 0;            // resident workgroups of the streaming kernel on the device
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_bf16_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gdn_gram_stream_bf16_kernel<D>,
+      e = hipFuncSetAttribute((const void*)gdn_gram_stream_kernel<D, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramStream<D>::lds_bytes);
     int dev = 0, cus = 0, per_cu = 0;
     if (e == hipSuccess) e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)gdn_gram_stream_bf16_kernel<D>,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)gdn_gram_stream_kernel<D, FP8>,
                                                        GramShape<D>::NW * 64, GramStream<D>::lds_bytes);
     if (e != hipSuccess) return e;
     slots = std::max(1, per_cu) * cus;
@@ -642,13 +648,18 @@ static hipError_t launch_gram_t(const GramArgs& ga, hipStream_t stream) {
   if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {
     // persistent: one workgroup per resident slot
     const int grid = (int)std::min<long long>(nfh, slots);
-    hipLaunchKernelGGL((gdn_gram_stream_bf16_kernel<D>), dim3(grid), dim3(GramShape<D>::NW * 64),
+    hipLaunchKernelGGL((gdn_gram_stream_kernel<D, FP8>), dim3(grid), dim3(GramShape<D>::NW * 64),
                        GramStream<D>::lds_bytes, stream, ga);
   } else {
-    hipLaunchKernelGGL((gdn_gram_bf16_kernel<D>), dim3((unsigned)nfh), dim3(GramShape<D>::NW * 64),
+    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8>), dim3((unsigned)nfh), dim3(GramShape<D>::NW * 64),
                        GramShape<D>::lds_bytes, stream, ga);
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_gram_t(const GramArgs& ga, hipStream_t stream) {
+  return ga.fp8 ? launch_gram_io<D, true>(ga, stream) : launch_gram_io<D, false>(ga, stream);
 }
 
 template <int D>

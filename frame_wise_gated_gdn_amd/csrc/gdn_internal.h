@@ -36,16 +36,18 @@ struct ReadoutArgs {
   float* norms;             // [BH][T] or nullptr
   int BH, T, S, t0, Tc;
   int Fs, f0;               // snapshots (and norm partials) hold [BH][Fs] frames from f0
+  int fp8;                  // 1: Q and O are OCP e4m3 bytes (bf16 snapshots only)
 };
 
-// Gram pass (bf16 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
+// Gram pass (bf16 or e4m3 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
 struct GramArgs {
-  const void* k;            // [BH][T][S][D] bf16
-  const void* v;            // [BH][T][S][D] bf16
+  const void* k;            // [BH][T][S][D] bf16, or OCP e4m3 when fp8
+  const void* v;            // [BH][T][S][D] as k
   void* gfr;                // [BH][Tc] x gram_frame_bytes(D): G as state-pass A operands
   void* bfr;                // [BH][Tc] x input_frame_bytes(D): B in accumulator layout
   int BH, T, S, t0, Tc;
   float kscale, kscale2;    // 1/sqrt(D*S) and 1/(D*S), each rounded once to fp32
+  int fp8;                  // 1: K and V are OCP e4m3 bytes
 };
 
 // State pass (bf16 I/O): the serial frame loop over G and B.

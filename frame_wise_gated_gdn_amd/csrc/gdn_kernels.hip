@@ -566,10 +566,13 @@ struct ReadShape {
   static constexpr size_t lds_bytes = (size_t)kReadWaves * 2 * tile_bytes;
 };
 
-template <int D>
-__global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(ReadoutArgs a) {
+template <int D, bool FP8>
+__global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_kernel(ReadoutArgs a) {
   using Sh = ReadShape<D>;
+  using IO = IoFmt<FP8>;
+  using raw = typename IO::raw;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, UPR = Sh::UPR, NLD = Sh::NLD, RS = Sh::RS;
+  constexpr int RS8 = D + 8;                       // row stride (bytes) of the e4m3 O tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int frame = blockIdx.x;                    // over BH * Tc
   const int bh = frame / a.Tc, tl = frame % a.Tc, t = a.t0 + tl;
@@ -578,10 +581,11 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
   uint16_t* const qs = (uint16_t*)(smem + (size_t)w * 2 * Sh::tile_bytes);
   uint16_t* const os = qs + 32 * RS;
   const int S = a.S, T = a.T;
-  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const uint16_t*)a.q + (size_t)bh * T * S * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc((uint16_t*)a.o + (size_t)bh * T * S * D, head_bytes);
-  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * 2u;   // frame's first byte in the head
+  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * IO::ebytes;
+  const size_t head0 = (size_t)bh * T * S * D * IO::ebytes;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const unsigned char*)a.q + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc((unsigned char*)a.o + head0, head_bytes);
+  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * IO::ebytes;   // frame's first byte in the head
   const int nchunk = (S + 31) / 32;
   const int NC = (nchunk + kReadWaves - 1) / kReadWaves;     // chunk slots per wave
   const size_t sf = (size_t)bh * a.Fs + a.f0 + tl;           // staging frame of (head, frame)
@@ -592,15 +596,15 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
     a.norms[(size_t)bh * T + t] = sqrtf(sq);
   }
 
-  // byte offset of 16-byte unit u of a chunk (tokens past S -> beyond the buffer)
+  // byte offset of 8-element unit u of a chunk (tokens past S -> beyond the buffer)
   auto unit_off = [&](int ch, int u) -> uint32_t {
     const int tok = ch * 32 + u / UPR;
-    return (ch < nchunk && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * 16u : kOOB;
+    return (ch < nchunk && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * IO::unit_bytes : kOOB;
   };
-  auto load_chunk = [&](int i, u32x4 (&X)[NLD]) {
+  auto load_chunk = [&](int i, raw (&X)[NLD]) {
     const int ch = w + kReadWaves * i;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) X[j] = buf_load16_nt(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
+    for (int j = 0; j < NLD; ++j) X[j] = IO::load_nt(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
   };
 
   // A operands: M_t^T rows (value column 16jb + n); k-step kc holds keys
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
       A[jb][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   constexpr int RING = Sh::RING;
-  u32x4 X[RING][NLD];
+  raw X[RING][NLD];
 #pragma unroll
   for (int r = 0; r < RING; ++r) load_chunk(r, X[r]);
   // The snapshot loads were issued first: one use of the last of them makes
@@ -651,7 +655,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int u = 64 * j + l;
-        *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(X[r][j]);
+        *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(IO::to_bf16(X[r][j]));
       }
       load_chunk(i + RING, X[r]);
       wave_lds_sync();
@@ -671,16 +675,26 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_bf16_kernel(Re
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kc = 0; kc < NKC; ++kc) acc = mfma_bf16(A[jb][kc], B[kc], acc);
-          const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-          *(u32x2*)(os + (16 * half + n) * RS + 16 * jb + 4 * g) = pk;
+          if constexpr (FP8) {
+            // one rounding, fp32 -> e4m3
+            *(uint32_t*)((unsigned char*)os + (16 * half + n) * RS8 + 16 * jb + 4 * g) = f32x4_to_fp8x4(acc);
+          } else {
+            const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+            *(u32x2*)(os + (16 * half + n) * RS + 16 * jb + 4 * g) = pk;
+          }
         }
       }
       wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int u = 64 * j + l;
-        const u32x4 y = *(const u32x4*)(os + (u / UPR) * RS + 8 * (u % UPR));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ors, i < NC ? unit_off(ch, u) : kOOB, 0, kNT);
+        if constexpr (FP8) {
+          const u32x2 y = *(const u32x2*)((const unsigned char*)os + (u / UPR) * RS8 + 8 * (u % UPR));
+          __builtin_amdgcn_raw_buffer_store_b64(y, ors, i < NC ? unit_off(ch, u) : kOOB, 0, kNT);
+        } else {
+          const u32x4 y = *(const u32x4*)(os + (u / UPR) * RS + 8 * (u % UPR));
+          __builtin_amdgcn_raw_buffer_store_b128(y, ors, i < NC ? unit_off(ch, u) : kOOB, 0, kNT);
+        }
       }
     }
   }
@@ -728,8 +742,11 @@ static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
   if (!attr_set) {
     hipError_t e;
     if constexpr (BF16) {
-      e = hipFuncSetAttribute((const void*)gdn_readout_bf16_kernel<D>,
+      e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
     } else {
       e = hipFuncSetAttribute((const void*)gdn_readout_f32_kernel<D>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
@@ -738,8 +755,13 @@ static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
     attr_set = true;
   }
   if constexpr (BF16) {
-    hipLaunchKernelGGL((gdn_readout_bf16_kernel<D>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
-                       ReadShape<D>::lds_bytes, stream, ro);
+    // bf16 snapshots: bf16 or e4m3 Q and O
+    if (ro.fp8)
+      hipLaunchKernelGGL((gdn_readout_kernel<D, true>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
+                         ReadShape<D>::lds_bytes, stream, ro);
+    else
+      hipLaunchKernelGGL((gdn_readout_kernel<D, false>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
+                         ReadShape<D>::lds_bytes, stream, ro);
   } else {
     hipLaunchKernelGGL((gdn_readout_f32_kernel<D>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
                        (size_t)D * (D + 1) * 4, stream, ro);

@@ -17,7 +17,8 @@ Draw recipe (fixed; changing it changes every stored expectation):
       seed * 1_000_003 + stream_id,
     stream_id = tensor_index * B*H + b*H + h, tensor_index Q=0 K=1 V=2 gamma=3 beta=4;
   * Q, K, V: fp32 ``randn`` of shape [T, S, D] times the tensor's std, then
-    rounded to nearest-even bf16 when the I/O dtype is bf16;
+    rounded to nearest-even bf16, or to the nearest OCP E4M3 value (ties to
+    even), when the I/O dtype is bf16 or fp8;
   * gamma, beta: fp32 ``rand`` of shape [T], mapped affinely onto [lo, hi].
 CPU and GPU generators give different streams: a test draws on one device and
 hands the same values to both sides.
@@ -40,7 +41,7 @@ class Workload:
     T: int
     S: int
     D: int
-    dtype: str = "bf16"                 # I/O dtype of q, k, v, o: "bf16" or "f32"
+    dtype: str = "bf16"                 # I/O dtype of q, k, v, o: "bf16", "f32" or "fp8" (OCP E4M3)
     gamma: Tuple[float, float] = (0.9, 1.0)
     beta: Tuple[float, float] = (0.0, 1.0)
     q_std: float = 1.0
@@ -55,7 +56,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}[self.dtype]
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -115,8 +116,11 @@ def generate(w: Workload, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor
 
 
 def to_numpy_io(x: torch.Tensor):
-    """Host copy in the oracle's input convention: float32, or uint16 bf16 bits."""
+    """Host copy in the oracle's input convention: float32, uint16 bf16 bits or
+    uint8 E4M3 codes."""
     x = x.detach().to("cpu").contiguous()
     if x.dtype == torch.bfloat16:
         return x.view(torch.int16).numpy().view("uint16")
+    if x.dtype == torch.float8_e4m3fn:
+        return x.view(torch.uint8).numpy()
     return x.numpy()

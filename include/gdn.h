@@ -22,7 +22,7 @@
  * fp32 scalars, one per (batch, head, frame).
  *
  * Layouts (all row-major, innermost last; every pointer is a DEVICE pointer):
- *   q, k, v, o     [B][H][T][S][D]  io_dtype (bf16 or fp32)
+ *   q, k, v, o     [B][H][T][S][D]  io_dtype (bf16, fp32 or OCP e4m3)
  *   gamma, beta    [B][H][T]        fp32
  *   state_in/out   [B][H][D][D]     fp32, indexed [key][value]
  *   state_norms    [B][H][T]        fp32, Frobenius norm of the post-update state
@@ -59,7 +59,15 @@ extern "C" {
 
 #define GDN_ABI_VERSION 1
 
-typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+/*
+ * Element type of q, k, v and o.  GDN_FP8_E4M3 is the OCP 8-bit float E4M3
+ * ("fn": exponent bias 7, no infinities, 0x7F/0xFF NaN), a low-precision I/O
+ * variant of the same computation (after the 4-bit NVFP4 deployment the
+ * SANA-WM news article describes): inputs are decoded exactly, the Gram
+ * pipeline runs as for bf16, and o is rounded once from fp32 to the nearest
+ * e4m3 (ties to even; magnitudes past 448's rounding range become NaN).
+ */
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
 
 typedef enum gdn_beta_mode {
   GDN_BETA_ERASE = 0, /* M = gM + Kf^T (V - b Kf gM): beta scales the correction */
@@ -73,7 +81,7 @@ typedef enum gdn_status {
   GDN_ERR_DTYPE = 3,       /* io_dtype or beta_mode not one of the enums */
   GDN_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
   GDN_ERR_ALIAS = 5,       /* forbidden overlap between buffers */
-  GDN_ERR_UNSUPPORTED = 6, /* D not in {16, 32, ..., 128}, or unknown flags */
+  GDN_ERR_UNSUPPORTED = 6, /* D not in {16, 32, ..., 128}, unknown flags, or DIRECT with e4m3 */
   GDN_ERR_ABI = 7,         /* desc->abi_version != GDN_ABI_VERSION */
   GDN_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than one frame needs */
   GDN_ERR_HIP = 9          /* a HIP runtime call failed (message in gdn_last_error) */
@@ -82,7 +90,7 @@ typedef enum gdn_status {
 /* Record device time per kernel on `stream` (read back with gdn_kernel_times). */
 #define GDN_FLAG_TIME_KERNELS 0x1u
 /*
- * bf16 I/O only: run the single-pass recurrence (keys and values streamed by
+ * bf16 I/O only (GDN_ERR_UNSUPPORTED with e4m3): run the single-pass recurrence (keys and values streamed by
  * every value-column tile of the state, the state product in the same sweep)
  * instead of the default Gram pipeline (frame-parallel G_t = Kf^T Kf and
  * B_t = Kf^T V, then a serial D x D state pass).  Slower; needs no G/B
@@ -117,7 +125,7 @@ const char* gdn_last_error(void);
 
 /*
  * Workspace bytes the library would like for `d` (all T frames staged at once,
- * capped at 1024 frames; the bf16 path stages G_t, B_t and a bf16 state
+ * capped at 1024 frames; the bf16 and e4m3 paths stage G_t, B_t and a bf16 state
  * snapshot per frame, about 3*D*D*2 bytes per head and frame); 0 if `d` is
  * invalid.  Any workspace of at
  * least gdn_workspace_min_size(d) bytes works: a smaller one makes the library

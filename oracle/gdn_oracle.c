@@ -43,8 +43,9 @@
  * whatever the thread count, so the result is bitwise reproducible.  Memory is
  * O(S*D + D*D) per head and does not grow with T.
  *
- * Inputs are read exactly: fp32 values, or bf16 bit patterns widened to fp32
- * (exact) and then to double (exact).
+ * Inputs are read exactly: fp32 values, bf16 bit patterns widened to fp32
+ * (exact) and then to double (exact), or OCP 8-bit E4M3 codes decoded from
+ * the format's definition (see e4m3_value).
  */
 #include <math.h>
 #include <stdint.h>
@@ -66,8 +67,24 @@ static int omp_get_max_threads(void) { return 1; }
 #define ORACLE_MUTANT 0
 #endif
 
+/* OCP 8-bit float E4M3 ("fn" variant): sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the
+ * all-ones code (exponent 15, mantissa 7) is NaN; there is no infinity. */
+static double e4m3_value(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double x;
+  if (e == 15 && m == 7)
+    x = NAN;
+  else if (e == 0)
+    x = ldexp((double)m, -9);
+  else
+    x = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -x : x;
+}
+
 static double widen(const void* p, int io_dtype, size_t idx) {
   if (io_dtype == 0) return (double)((const float*)p)[idx];
+  if (io_dtype == 2) return e4m3_value(((const uint8_t*)p)[idx]);
   uint32_t u = ((uint32_t)((const uint16_t*)p)[idx]) << 16;
   float f;
   memcpy(&f, &u, sizeof f);
@@ -78,10 +95,15 @@ static double relu(double x) { return x > 0.0 ? x : 0.0; }
 
 int oracle_abi_version(void) { return 1; }
 
+/* The E4M3 decoder on its own, for the tests that pin it: n codes -> doubles. */
+void oracle_e4m3_decode(const uint8_t* codes, double* out, int n) {
+  for (int i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+}
+
 /*
  * One head.
  *   T, S, D      frames, tokens per frame, head dim (>= 1 each)
- *   io_dtype     0 = fp32 inputs, 1 = bf16 bit patterns (uint16)
+ *   io_dtype     0 = fp32 inputs, 1 = bf16 bit patterns (uint16), 2 = E4M3 codes (uint8)
  *   beta_mode    0 = ERASE, 1 = WRITE
  *   q, k, v      [T][S][D] for this head, row-major
  *   gamma, beta  [T] fp32
@@ -96,7 +118,7 @@ int oracle_gdn_head(int T, int S, int D, int io_dtype, int beta_mode,
                     const float* gamma, const float* beta,
                     const double* state_in, double* out, double* state_out,
                     double* norms, int threads) {
-  if (T < 0 || S < 1 || D < 1 || (io_dtype != 0 && io_dtype != 1) ||
+  if (T < 0 || S < 1 || D < 1 || io_dtype < 0 || io_dtype > 2 ||
       (beta_mode != 0 && beta_mode != 1))
     return ORACLE_ERR_ARG;
   if (T > 0 && (!q || !k || !v || !gamma || !beta)) return ORACLE_ERR_ARG;

@@ -4,8 +4,8 @@ Only the tests, the package's smoke check and the CPU-baseline leg of the
 benchmark may import this module.  It loads ``liboracle_gdn.so`` built from
 ``gdn_oracle.c`` with the host C compiler and never touches the HIP library.
 
-Arrays are numpy.  bf16 tensors travel as ``uint16`` bit patterns; fp32 as
-``float32``.  Layouts: q, k, v, o are [B, H, T, S, D]; gamma, beta [B, H, T];
+Arrays are numpy.  bf16 tensors travel as ``uint16`` bit patterns, OCP E4M3
+tensors as ``uint8`` codes, fp32 as ``float32``.  Layouts: q, k, v, o are [B, H, T, S, D]; gamma, beta [B, H, T];
 states [B, H, D, D] indexed [key][value].
 
 The recurrence itself is documented in ``gdn_oracle.c`` (source: the SANA-WM
@@ -57,6 +57,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int]
+    lib.oracle_e4m3_decode.restype = None
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     _libs[path] = lib
     return lib
 
@@ -67,7 +69,7 @@ def _ptr(a: Optional[np.ndarray]):
 
 def head(q, k, v, gamma, beta, state_in=None, beta_mode="erase", want_out=True,
          want_norms=False, threads: int = 0, lib_path: str = LIB):
-    """One head: q, k, v [T, S, D] (float32 or uint16 bf16 bits), gamma/beta [T].
+    """One head: q, k, v [T, S, D] (float32, uint16 bf16 bits or uint8 E4M3 codes), gamma/beta [T].
 
     Returns (out [T,S,D] float64 or None, state_out [D,D] float64, norms [T] or None).
     """
@@ -83,8 +85,10 @@ def head(q, k, v, gamma, beta, state_in=None, beta_mode="erase", want_out=True,
         io = 0
     elif q.dtype == np.uint16:
         io = 1
+    elif q.dtype == np.uint8:
+        io = 2
     else:
-        raise TypeError("inputs must be float32 or uint16 (bf16 bit patterns)")
+        raise TypeError("inputs must be float32, uint16 (bf16 bit patterns) or uint8 (E4M3 codes)")
     T, S, D = q.shape
     g = np.ascontiguousarray(gamma, dtype=np.float32).reshape(T)
     b = np.ascontiguousarray(beta, dtype=np.float32).reshape(T)
@@ -126,3 +130,40 @@ def forward(q, k, v, gamma, beta, state_in=None, beta_mode="erase", want_out=Tru
 def bf16_bits_to_f64(x: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns (uint16) to float64."""
     return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray, lib_path: str = LIB) -> np.ndarray:
+    """Exact values of OCP E4M3 codes (uint8), decoded by the oracle's C decoder."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    load(lib_path).oracle_e4m3_decode(_ptr(c), _ptr(out), int(c.size))
+    return out
+
+
+def _e4m3_grid() -> np.ndarray:
+    """Values of the non-negative finite E4M3 codes 0x00..0x7E, in code order
+    (which is also increasing value order)."""
+    return e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+
+
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """E4M3 code (uint8) nearest to each double, ties to the even code.
+
+    The grid is that of the format (OCP 8-bit float E4M3, "fn" variant): the
+    126 non-negative finite values, 448 the largest.  A magnitude past 464,
+    half-way to the first value the format lacks (480), has no nearest code and
+    gives NaN; NaN gives NaN.  The sign goes to the top bit, so -0.0 is 0x80.
+    This is the rounding used for an E4M3 output: one rounding of the exact
+    value to the format.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    grid = _e4m3_grid()
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, len(grid) - 1)   # first grid value >= a
+    lo = np.clip(hi - 1, 0, len(grid) - 1)
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a > 464.0, 0x7F, code).astype(np.uint8)
+    code = np.where(np.isnan(x), 0x7F, code).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)

@@ -60,7 +60,7 @@ def args_ok(gdn, d):
 
 
 def test_valid_arguments_pass(gdn):
-    for dt in ("bf16", "f32"):
+    for dt in ("bf16", "f32", "fp8"):
         for D in range(16, 129, 16):
             d = gdn.make_desc(2, 3, 5, 17, D, dt)
             assert gdn.check_args(d, **args_ok(gdn, d)) == 0, gdn.lib().gdn_last_error()
@@ -75,6 +75,9 @@ def test_abi_and_enum_errors(gdn):
     assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 3
     d = gdn.make_desc(1, 2, 3, 16, 16, "bf16", flags=0x80)
     assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))) == 6
+    # the single-pass recurrence has no E4M3 form
+    d = gdn.make_desc(1, 2, 3, 16, 16, "fp8", flags=gdn.binding.FLAG_DIRECT)
+    assert gdn.check_args(d, **args_ok(gdn, gdn.make_desc(1, 2, 3, 16, 16, "fp8"))) == 6
     assert gdn.lib().gdn_check_args(None, *([None] * 10), 0, 0) == 1
 
 

@@ -1,7 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the double-precision oracle.
 
 Bar (relative Frobenius error over the compared tensor): 1e-4 for fp32 I/O,
-2e-2 for bf16 I/O, the same for the final state.  Chunked streaming must equal
+2e-2 for bf16 I/O, the same for the final state; E4M3 I/O adds its own output
+rounding to the bf16 bar (see FP8_TOL).  Chunked streaming must equal
 the one-shot forward bitwise, and the result must not depend on the workspace
 size or on the run.  bf16 I/O has two paths: the default Gram pipeline
 (path="auto") and the single-pass recurrence (path="direct"); both are held to
@@ -361,6 +362,90 @@ def test_device_argument_errors(env):
     assert e.value.status == 4
 
 
+# ------------------------------------------------------------------ OCP E4M3 I/O
+# O is rounded once from fp32 to E4M3.  For a normal value that rounding moves
+# it by at most half a unit in the last place, 2^-4 of its magnitude, so the
+# relative Frobenius error against the exact result is at most 2^-4 plus the
+# error of the fp32 value before rounding (the same Gram pipeline as bf16 I/O,
+# held to 2e-2).  The codes are also compared with the exact result rounded the
+# same way.  The fp32 value before rounding carries an absolute error of about
+# eps * rms(O) on every element (it comes from the bf16 copies of the state and
+# of G, B, which all elements share); where |O| is at least a quarter of
+# rms(O), one code step (>= 2^-4 |O|) is larger than that error for any eps
+# up to 1.5e-2, so there the codes can differ only where the two values
+# straddle a rounding midpoint, and then by one code.  Near zero the steps are
+# finer than that error and only the Frobenius bound applies.
+FP8_TOL = 2.0 ** -4 + 2e-2
+
+
+def code_order(c):
+    """E4M3 codes in value order (sign-magnitude byte -> signed integer)."""
+    c = np.asarray(c).astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c)
+
+
+def check_fp8(env, out, st, ref, max_mismatch=0.1):
+    torch, gdn, wl, go = env
+    worst = (0.0, 0.0)
+    for (b, h), (o_ref, s_ref, _) in ref.items():
+        codes = out[b, h].view(torch.uint8).cpu().numpy()
+        got = go.e4m3_to_f64(codes)
+        assert np.isfinite(got).all(), f"head {(b, h)}: non-finite output"
+        eo = rel(got, o_ref)
+        assert eo < FP8_TOL, f"head {(b, h)}: output rel err {eo:.3e}"
+        d = np.abs(code_order(codes) - code_order(go.round_e4m3(o_ref)))
+        frac = float(np.count_nonzero(d)) / d.size
+        big = np.abs(o_ref) >= 0.25 * np.sqrt(np.mean(o_ref ** 2))
+        print(f"head {(b, h)}: rel {eo:.3e}, codes off {frac:.4f}, max step {d.max()} "
+              f"(|O| >= rms/4: {d[big].max() if big.any() else 0})")
+        assert not big.any() or d[big].max() <= 1, f"head {(b, h)}: a large output is >1 code off"
+        assert frac < max_mismatch, f"head {(b, h)}: {frac:.3f} of the codes differ"
+        es = rel(to_f64(torch, st[b, h]), s_ref)
+        assert es < TOL["bf16"], f"head {(b, h)}: state rel err {es:.3e}"
+        worst = (max(worst[0], eo), max(worst[1], frac))
+    print(f"worst output rel err {worst[0]:.3e}, worst code mismatch fraction {worst[1]:.4f}")
+
+
+@pytest.mark.parametrize("B,H,T,S,D", [(1, 2, 7, 100, 16), (1, 2, 5, 880, 64), (1, 3, 6, 300, 112),
+                                        (1, 2, 5, 400, 112), (2, 2, 4, 200, 128), (1, 2, 9, 1000, 48)])
+def test_fp8_io_parity(env, B, H, T, S, D):
+    """E4M3 Q, K, V, O: per-frame and persistent gram kernels, ragged chunks, both beta modes."""
+    torch, gdn, wl, go = env
+    w = wl.Workload("fp8", B, H, T, S, D, dtype="fp8", gamma=(0.8, 1.0), beta=(0.0, 1.0))
+    inp = gen(env, w)
+    for mode in ("erase", "write"):
+        out, st, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], beta_mode=mode)
+        torch.cuda.synchronize()
+        assert out.dtype == torch.float8_e4m3fn
+        check_fp8(env, out, st, run_oracle(env, inp, mode=mode))
+
+
+def test_fp8_chunked_rollout_equals_one_shot_bitwise(env):
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.CHUNKED.with_(H=4, T=13, dtype="fp8"))
+    o1, st1, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    B, H, T, S, D = inp["q"].shape
+    state = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
+    outs = []
+    for t0 in range(0, T, 4):
+        sl = slice(t0, min(T, t0 + 4))
+        o, _, _ = gdn.frame_step(*(inp[n][:, :, sl].contiguous() for n in ("q", "k", "v", "gamma", "beta")),
+                                 state, commit="inplace")
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2).view(torch.uint8), o1.view(torch.uint8))
+    assert torch.equal(state, st1)
+    check_fp8(env, o1, st1, run_oracle(env, inp, heads=[(0, 0), (0, 3)]))
+
+
+def test_fp8_direct_path_is_rejected(env):
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.Workload("fp8d", 1, 1, 2, 16, 16, dtype="fp8"))
+    with pytest.raises(gdn.GDNError) as e:
+        gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], path="direct")
+    assert e.value.status == 6
+
+
 # ------------------------------------------------------------------ full-size workloads
 def test_minute_720p_sampled_heads(env):
     """The benchmarked launch (B1 H20 T961 S880 D112, one call); oracle on sampled heads."""
@@ -405,3 +490,13 @@ def test_stress_shape_stable_and_sampled_parity(env):
         a2 = g_t * float(torch.max(torch.abs(1 - b_t * lam)))
         n_bound = a2 * n_bound + float(torch.linalg.norm(kf.T @ vv[t].double()))
         assert norms[t] <= n_bound * (1 + 2e-2), t
+
+
+def test_fp8_minute_720p_sampled_heads(env):
+    """The 720p-shaped launch with E4M3 Q, K, V, O; oracle on sampled heads."""
+    torch, gdn, wl, go = env
+    w = wl.MINUTE_720P.with_(dtype="fp8")
+    inp = wl.generate(w, device="cuda")
+    out, st, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    torch.cuda.synchronize()
+    check_fp8(env, out, st, run_oracle(env, inp, heads=[(0, 0), (0, 19)]))

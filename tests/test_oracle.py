@@ -251,6 +251,64 @@ def test_bf16_inputs_are_widened_exactly(oracle):
     assert np.array_equal(o_bits, o_f) and np.array_equal(s_bits, s_f)
 
 
+# ---------------------------------------------------------------- OCP E4M3 (8-bit float) I/O
+def test_e4m3_decode_closed_forms(oracle):
+    """The oracle's E4M3 decoder against values fixed by the format definition
+    (sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals m/8 * 2^-6,
+    0x7F / 0xFF NaN) and against torch's float8_e4m3fn on all 256 codes."""
+    import torch
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+             0x3C: 1.5, 0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    got = oracle.e4m3_to_f64(np.array(list(fixed), np.uint8))
+    assert np.array_equal(got, np.array(list(fixed.values())))
+    z = oracle.e4m3_to_f64(np.array([0x80], np.uint8))
+    assert z[0] == 0.0 and np.signbit(z[0])
+    assert np.isnan(oracle.e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+    codes = np.arange(256, dtype=np.uint8)
+    lib_vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    mine = oracle.e4m3_to_f64(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(lib_vals))
+    ok = ~np.isnan(mine)
+    assert np.array_equal(mine[ok], lib_vals[ok])
+
+
+def test_e4m3_rounding_ties_overflow_and_library(oracle):
+    """Rounding to E4M3: ties go to the even code, 464 (half-way from 448 to the
+    missing 480) rounds down to 448 and anything above it is NaN, the
+    subnormal tie 2^-10 goes to +0; and it agrees with torch's float32 ->
+    float8_e4m3fn cast on every midpoint of the grid, its neighbours and
+    random values."""
+    import torch
+    r = lambda *x: oracle.round_e4m3(np.array(x, np.float64))
+    assert r(1.0625).tolist() == [0x38]           # tie between 1.0 (m=0) and 1.125 (m=1)
+    assert r(1.1875).tolist() == [0x3A]           # tie between 1.125 and 1.25 -> 1.25 (m=2)
+    assert r(464.0, 465.0, 1e9, -500.0).tolist() == [0x7E, 0x7F, 0x7F, 0xFF]
+    assert r(2.0 ** -10, 3 * 2.0 ** -10, -0.0).tolist() == [0x00, 0x02, 0x80]
+    assert r(float("nan")).tolist() == [0x7F]
+    grid = oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (grid[1:] + grid[:-1]) / 2
+    rng = np.random.default_rng(5)
+    x = np.concatenate([mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf), grid,
+                        rng.standard_normal(5000) * 4, -mids]).astype(np.float32)
+    lib_codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.round_e4m3(x.astype(np.float64)), lib_codes)
+
+
+def test_e4m3_inputs_are_decoded_exactly(oracle):
+    """E4M3 codes and their exact values passed as float32 give the same bits."""
+    rng = np.random.default_rng(17)
+    T, S, D = 3, 24, 16
+    codes = [rng.integers(0, 256, (T, S, D), dtype=np.uint8) for _ in range(3)]
+    for c in codes:
+        c[(c & 0x7F) == 0x7F] = 0x38                # no NaN codes
+    g = np.full(T, 0.9, np.float32)
+    b = np.full(T, 0.5, np.float32)
+    o_c, s_c, _ = oracle.head(*codes, g, b)
+    as_f32 = [oracle.e4m3_to_f64(c).astype(np.float32) for c in codes]
+    o_f, s_f, _ = oracle.head(*as_f32, g, b)
+    assert np.array_equal(o_c, o_f) and np.array_equal(s_c, s_f)
+
+
 # ---------------------------------------------------------------- P10 / P11 / P12
 @pytest.mark.parametrize("S,D,kstd,beta", [(880, 64, 1.0, 1.0), (880, 112, 1.0, 1.0),
                                            (3600, 128, 2.0, 1.0), (16, 16, 1.0, 1.0)])
