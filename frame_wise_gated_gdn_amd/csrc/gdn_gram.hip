@@ -124,11 +124,16 @@ constexpr uint32_t gram_ymask(int NB, int b0, int b1) {
   return m;
 }
 
-template <int D, bool FP8, int W>
+// NW waves share a frame's output blocks and its loads (GramShape<D>::NW, or
+// twice that for launches too small to fill the GPU, where the time of one
+// workgroup is the latency of the whole launch).  Every block is accumulated
+// over the chunks in the same order whatever NW is, so the bits do not change.
+template <int D, bool FP8, int NW, int W>
 __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem, int bh, int tl) {
   using Sh = GramShape<D>;
   using IO = IoFmt<FP8>;
-  constexpr int NB = Sh::NB, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, RS = Sh::RS;
+  constexpr int NB = Sh::NB, UPR = Sh::UPR, NLD = Sh::NLD, RS = Sh::RS;
+  constexpr int LPW = (2 * NLD + NW - 1) / NW;        // pieces loaded per wave per chunk
   constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT;
   constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
   constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
@@ -236,15 +241,15 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   });
 }
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_gram_kernel(GramArgs a) {
+template <int D, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gram_kernel(GramArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int fh = blockIdx.x;   // over BH * Tc
   const int bh = fh / a.Tc, tl = fh % a.Tc;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  static_for<GramShape<D>::NW>([&](auto wc) {
+  static_for<NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    if (w == W) gram_wave<D, FP8, W>(a, smem, bh, tl);
+    if (w == W) gram_wave<D, FP8, NW, W>(a, smem, bh, tl);
   });
 }
 
@@ -625,15 +630,20 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
 // ----------------------------------------------------------------------------
 template <int D, bool FP8>
 static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
+  constexpr int NW = GramShape<D>::NW;
   static bool attr_set = false;   // benign race: every setter writes the same value
   static int slots = 0;            // resident workgroups of the streaming kernel on the device
+  static int cus = 0;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8>,
+    hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8, 2 * NW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gdn_gram_stream_kernel<D, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramStream<D>::lds_bytes);
-    int dev = 0, cus = 0, per_cu = 0;
+    int dev = 0, per_cu = 0;
     if (e == hipSuccess) e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
@@ -645,13 +655,18 @@ static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
   }
   const long long nfh = (long long)ga.BH * ga.Tc;
   const int nch = (ga.S + 31) / 32;
-  if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {
+  if (nfh <= 2 * cus) {
+    // at most two frames per CU (a short streaming chunk): one workgroup per
+    // frame with twice the waves, so that the launch takes half as long
+    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, 2 * NW>), dim3((unsigned)nfh), dim3(2 * NW * 64),
+                       GramShape<D>::lds_bytes, stream, ga);
+  } else if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {
     // persistent: one workgroup per resident slot
     const int grid = (int)std::min<long long>(nfh, slots);
     hipLaunchKernelGGL((gdn_gram_stream_kernel<D, FP8>), dim3(grid), dim3(GramShape<D>::NW * 64),
                        GramStream<D>::lds_bytes, stream, ga);
   } else {
-    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8>), dim3((unsigned)nfh), dim3(GramShape<D>::NW * 64),
+    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, NW>), dim3((unsigned)nfh), dim3(NW * 64),
                        GramShape<D>::lds_bytes, stream, ga);
   }
   return hipGetLastError();

@@ -563,11 +563,15 @@ struct ReadShape {
   static constexpr int NLD = D / 16;             // 1 KB loads per 32-token chunk (= 32*UPR/64)
   static constexpr int RS = D + 8;               // LDS row stride (elements)
   static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
-  static constexpr size_t lds_bytes = (size_t)kReadWaves * 2 * tile_bytes;
+  // per wave: a Q tile and an O tile
+  static constexpr size_t lds_bytes(int waves) { return (size_t)waves * 2 * tile_bytes; }
 };
 
-template <int D, bool FP8>
-__global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_kernel(ReadoutArgs a) {
+// RW waves per workgroup split the frame's chunks: kReadWaves, or twice that
+// for launches with fewer frames than CUs.  Every output element is computed
+// the same way whatever RW is.
+template <int D, bool FP8, int RW>
+__global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_kernel(ReadoutArgs a) {
   using Sh = ReadShape<D>;
   using IO = IoFmt<FP8>;
   using raw = typename IO::raw;
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_kernel(Readout
   const __amdgpu_buffer_rsrc_t ors = make_rsrc((unsigned char*)a.o + head0, head_bytes);
   const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * IO::ebytes;   // frame's first byte in the head
   const int nchunk = (S + 31) / 32;
-  const int NC = (nchunk + kReadWaves - 1) / kReadWaves;     // chunk slots per wave
+  const int NC = (nchunk + RW - 1) / RW;                     // chunk slots per wave
   const size_t sf = (size_t)bh * a.Fs + a.f0 + tl;           // staging frame of (head, frame)
 
   if (a.norms && a.norm_part && tid == 0) {
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_kernel(Readout
     return (ch < nchunk && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * IO::unit_bytes : kOOB;
   };
   auto load_chunk = [&](int i, raw (&X)[NLD]) {
-    const int ch = w + kReadWaves * i;
+    const int ch = w + RW * i;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) X[j] = IO::load_nt(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
   };
@@ -650,7 +654,7 @@ __global__ __launch_bounds__(kReadWaves * 64, 2) void gdn_readout_kernel(Readout
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       const int i = base + r;
-      const int ch = w + kReadWaves * i;
+      const int ch = w + RW * i;
       // stage ReLU(Q) of the chunk (row-major, padded rows)
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
@@ -738,32 +742,46 @@ static hipError_t launch_recurrence_t(const RecurArgs& ra, hipStream_t stream) {
 
 template <int D, bool BF16>
 static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
+  constexpr int RW = kReadWaves;
   static bool attr_set = false;
+  static int cus = 0;
   if (!attr_set) {
     hipError_t e;
     if constexpr (BF16) {
-      e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes);
+      const void* fns[4] = {(const void*)gdn_readout_kernel<D, false, RW>, (const void*)gdn_readout_kernel<D, true, RW>,
+                            (const void*)gdn_readout_kernel<D, false, 2 * RW>,
+                            (const void*)gdn_readout_kernel<D, true, 2 * RW>};
+      const size_t lds[4] = {ReadShape<D>::lds_bytes(RW), ReadShape<D>::lds_bytes(RW),
+                             ReadShape<D>::lds_bytes(2 * RW), ReadShape<D>::lds_bytes(2 * RW)};
+      e = hipSuccess;
+      for (int i = 0; i < 4 && e == hipSuccess; ++i)
+        e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i]);
     } else {
       e = hipFuncSetAttribute((const void*)gdn_readout_f32_kernel<D>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
     }
+    int dev = 0;
+    if (e == hipSuccess) e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  const unsigned grid = (unsigned)(ro.BH * ro.Tc);
   if constexpr (BF16) {
-    // bf16 snapshots: bf16 or e4m3 Q and O
-    if (ro.fp8)
-      hipLaunchKernelGGL((gdn_readout_kernel<D, true>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
-                         ReadShape<D>::lds_bytes, stream, ro);
-    else
-      hipLaunchKernelGGL((gdn_readout_kernel<D, false>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
-                         ReadShape<D>::lds_bytes, stream, ro);
+    // bf16 snapshots: bf16 or e4m3 Q and O; a launch with fewer frames than
+    // CUs (a short streaming chunk) takes twice the waves per frame
+    const bool wide = (int)grid < cus;
+    const size_t lds = ReadShape<D>::lds_bytes(wide ? 2 * RW : RW);
+    const dim3 block(wide ? 2 * RW * 64 : RW * 64);
+    if (ro.fp8) {
+      if (wide) hipLaunchKernelGGL((gdn_readout_kernel<D, true, 2 * RW>), dim3(grid), block, lds, stream, ro);
+      else hipLaunchKernelGGL((gdn_readout_kernel<D, true, RW>), dim3(grid), block, lds, stream, ro);
+    } else {
+      if (wide) hipLaunchKernelGGL((gdn_readout_kernel<D, false, 2 * RW>), dim3(grid), block, lds, stream, ro);
+      else hipLaunchKernelGGL((gdn_readout_kernel<D, false, RW>), dim3(grid), block, lds, stream, ro);
+    }
   } else {
-    hipLaunchKernelGGL((gdn_readout_f32_kernel<D>), dim3(ro.BH * ro.Tc), dim3(kReadWaves * 64),
+    hipLaunchKernelGGL((gdn_readout_f32_kernel<D>), dim3(grid), dim3(kReadWaves * 64),
                        (size_t)D * (D + 1) * 4, stream, ro);
   }
   return hipGetLastError();
