@@ -179,7 +179,7 @@ def main():
                     help="also run one 1 GiB device copy (for rocprofv3 counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the path shards "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards "
               "by (batch, head) with no communication, so N GPUs would each run their own heads.",
               file=sys.stderr)
         sys.exit(2)
