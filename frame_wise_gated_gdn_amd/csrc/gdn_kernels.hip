@@ -655,13 +655,18 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
     for (int r = 0; r < RING; ++r) {
       const int i = base + r;
       const int ch = w + RW * i;
+      // the loop is unrolled by RING: slots past NC only keep the loads going
+      const bool live = i < NC;
       // stage ReLU(Q) of the chunk (row-major, padded rows)
+      if (live) {
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int u = 64 * j + l;
-        *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(IO::to_bf16(X[r][j]));
+        for (int j = 0; j < NLD; ++j) {
+          const int u = 64 * j + l;
+          *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(IO::to_bf16(X[r][j]));
+        }
       }
       load_chunk(i + RING, X[r]);
+      if (!live) continue;
       wave_lds_sync();
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
