@@ -438,6 +438,46 @@ def test_fp8_chunked_rollout_equals_one_shot_bitwise(env):
     check_fp8(env, o1, st1, run_oracle(env, inp, heads=[(0, 0), (0, 3)]))
 
 
+@pytest.mark.parametrize("S,D", [(96, 64), (880, 112)])
+def test_fp8_inputs_run_the_bf16_pipeline_bitwise(env, S, D):
+    """Every E4M3 value is exact in bf16, so E4M3 inputs and the same values as
+    bf16 must give bitwise the same final state and state norms (the decode
+    feeds the identical bf16 tiles); the outputs differ only in their last
+    rounding (e4m3 against bf16 of the same fp32 value)."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.Workload("fp8eq", 1, 3, 6, S, D, dtype="fp8", gamma=(0.8, 1.0), beta=(0.2, 1.0)))
+    as_bf16 = {n: (inp[n].to(torch.bfloat16) if n in ("q", "k", "v") else inp[n]) for n in inp}
+    m0 = torch.randn((1, 3, D, D), generator=torch.Generator().manual_seed(4)).cuda() * 0.1
+    for mode in ("erase", "write"):
+        o8, s8, n8 = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], state=m0,
+                                       beta_mode=mode, want_norms=True)
+        ob, sb, nb = gdn.frame_forward(as_bf16["q"], as_bf16["k"], as_bf16["v"], as_bf16["gamma"],
+                                       as_bf16["beta"], state=m0, beta_mode=mode, want_norms=True)
+        torch.cuda.synchronize()
+        assert torch.equal(s8, sb) and torch.equal(n8, nb)
+        # both outputs are one rounding of the same fp32 values
+        d = (o8.float() - ob.float()).abs()
+        assert bool((d <= ob.float().abs() * 2.0 ** -4 + 2.0 ** -10).all())
+
+
+def test_fp8_initial_state_norms_and_peek(env):
+    torch, gdn, wl, go = env
+    w = wl.Workload("fp8st", 1, 2, 5, 200, 64, dtype="fp8", gamma=(0.8, 1.0), beta=(0.0, 1.0))
+    inp = gen(env, w)
+    m0 = torch.randn((1, 2, 64, 64), generator=torch.Generator().manual_seed(6)).cuda() * 0.1
+    keep = m0.clone()
+    o, _, nm = gdn.frame_step(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], m0, commit="peek")
+    o2, s2, n2 = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], state=m0,
+                                   want_norms=True)
+    torch.cuda.synchronize()
+    assert torch.equal(m0, keep)
+    assert torch.equal(o.view(torch.uint8), o2.view(torch.uint8))
+    ref = run_oracle(env, inp, state=m0, want_norms=True)
+    check_fp8(env, o2, s2, ref)
+    for (b, h), (_, _, n_ref) in ref.items():
+        assert rel(to_f64(torch, n2[b, h]), n_ref) < TOL["bf16"]
+
+
 def test_fp8_direct_path_is_rejected(env):
     torch, gdn, wl, go = env
     inp = gen(env, wl.Workload("fp8d", 1, 1, 2, 16, 16, dtype="fp8"))
