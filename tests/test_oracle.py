@@ -424,3 +424,83 @@ def test_pins_catch_planted_mistakes(oracle):
             oracle.build(path, mutant=mutant)
             passed = set(_pin_battery(path, oracle))
             assert passed != full, f"planted mistake {mutant} passes every pin"
+
+
+# ---------------------------------------------------------------- backward (reference gradients)
+def _bw_inputs(rng, T, S, D, mode_beta=(0.1, 1.0)):
+    def away_from_zero(x):
+        return np.where(np.abs(x) < 1e-2, np.sign(x + 1e-12) * 1e-2, x)
+    q = away_from_zero(rng.standard_normal((T, S, D)))
+    k = away_from_zero(rng.standard_normal((T, S, D)))
+    v = rng.standard_normal((T, S, D))
+    g = rng.uniform(0.6, 1.0, T)
+    b = rng.uniform(*mode_beta, T)
+    m0 = 0.3 * rng.standard_normal((D, D))
+    do = rng.standard_normal((T, S, D))
+    ds = rng.standard_normal((D, D))
+    return q, k, v, g, b, m0, do, ds
+
+
+def _loss_affine(q, k, v, g, b, m0, do, ds, mode):
+    """L = sum_t <dO_t, O_t> + <dS, M_T>, with the forward in the affine
+    (transition-matrix) form of refs.py -- not the residual form the
+    reference gradients differentiate."""
+    out, mt = refs.affine_form(q, k, v, g, b, m0=m0, mode=mode)
+    return float(np.sum(do * out) + np.sum(ds * mt))
+
+
+@pytest.mark.parametrize("mode", ["erase", "write"])
+@pytest.mark.parametrize("shape", [(3, 6, 4), (2, 9, 8)])
+def test_backward_matches_finite_differences(mode, shape):
+    """Every gradient against a central difference of the loss along a random
+    direction (step 1e-6, keys and queries kept 1e-2 away from ReLU's kink)."""
+    from oracle import gdn_backward
+    rng = np.random.default_rng(21)
+    T, S, D = shape
+    q, k, v, g, b, m0, do, ds = _bw_inputs(rng, T, S, D)
+    grads = gdn_backward.backward_head(q, k, v, g, b, do, d_state_out=ds, state_in=m0, beta_mode=mode)
+    args = {"q": q, "k": k, "v": v, "gamma": g, "beta": b, "state_in": m0}
+    names = {"q": "dq", "k": "dk", "v": "dv", "gamma": "dgamma", "beta": "dbeta", "state_in": "dstate_in"}
+    eps = 1e-6
+    for name, x in args.items():
+        d = rng.standard_normal(x.shape)
+        plus = dict(args, **{name: x + eps * d})
+        minus = dict(args, **{name: x - eps * d})
+        lp = _loss_affine(plus["q"], plus["k"], plus["v"], plus["gamma"], plus["beta"], plus["state_in"], do, ds, mode)
+        lm = _loss_affine(minus["q"], minus["k"], minus["v"], minus["gamma"], minus["beta"], minus["state_in"], do, ds,
+                          mode)
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(grads[names[name]] * d))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_state_gradient_is_the_exact_adjoint():
+    """O and M_T are affine in the initial state, so the loss changes by exactly
+    <dL/dM_0, delta> for any (large) delta."""
+    from oracle import gdn_backward
+    rng = np.random.default_rng(22)
+    q, k, v, g, b, m0, do, ds = _bw_inputs(rng, 4, 7, 8)
+    grads = gdn_backward.backward_head(q, k, v, g, b, do, d_state_out=ds, state_in=m0)
+    delta = rng.standard_normal(m0.shape)
+    l0 = _loss_affine(q, k, v, g, b, m0, do, ds, "erase")
+    l1 = _loss_affine(q, k, v, g, b, m0 + delta, do, ds, "erase")
+    assert abs((l1 - l0) - np.sum(grads["dstate_in"] * delta)) <= 1e-10 * max(1.0, abs(l1 - l0))
+
+
+def test_backward_linear_attention_closed_form():
+    """beta = 0, gamma = 1 is cumulative linear attention, whose gradients are
+    sums over frames: dV_tau = Kf_tau sum_{t >= tau} Qf_t^T dO_t and
+    dQ_t = (dO_t (sum_{tau <= t} Kf_tau^T V_tau)^T) * [Q_t > 0]."""
+    from oracle import gdn_backward
+    rng = np.random.default_rng(23)
+    T, S, D = 4, 5, 6
+    q, k, v, _, _, _, do, _ = _bw_inputs(rng, T, S, D)
+    g, b = np.ones(T), np.zeros(T)
+    grads = gdn_backward.backward_head(q, k, v, g, b, do)
+    qf, kf = refs.feat(q, k, S, D)
+    for tau in range(T):
+        acc = sum(qf[t].T @ do[t] for t in range(tau, T))
+        assert np.allclose(grads["dv"][tau], kf[tau] @ acc, rtol=1e-12, atol=1e-12)
+    for t in range(T):
+        m = sum(kf[tau].T @ v[tau] for tau in range(t + 1))
+        assert np.allclose(grads["dq"][t], (do[t] @ m.T) * (q[t] > 0), rtol=1e-12, atol=1e-12)
