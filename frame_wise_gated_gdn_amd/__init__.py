@@ -6,8 +6,8 @@ ctypes binding and the seeded synthetic workloads.  PyTorch only provides
 device memory and streams.
 """
 from .binding import (ABI_VERSION, BF16, ERASE, F32, FP8, WRITE, Desc, GDNError, check_args,  # noqa: F401
-                      frame_forward, frame_step, kernel_times, lib, make_desc, workspace_min_size,
-                      workspace_size)
+                      backward_workspace_size, frame_backward, frame_forward, frame_step, kernel_times, lib,
+                      make_desc, workspace_min_size, workspace_size)
 
-__all__ = ["frame_forward", "frame_step", "GDNError", "workspace_size", "workspace_min_size",
+__all__ = ["frame_forward", "frame_step", "frame_backward", "backward_workspace_size", "GDNError", "workspace_size", "workspace_min_size",
            "kernel_times", "check_args", "make_desc", "lib"]

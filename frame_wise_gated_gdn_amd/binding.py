@@ -19,14 +19,14 @@ ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
 FLAG_DIRECT = 0x2
 # kernel kinds of gdn_kernel_times, in slot order
-KERNELS = ("recurrence", "readout", "gram", "state")
+KERNELS = ("recurrence", "readout", "gram", "state", "backward")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_ABI", 8: "GDN_ERR_WORKSPACE",
           9: "GDN_ERR_HIP"}
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
            "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
-           "gdn_kernel_times")
+           "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward")
 
 
 class GDNError(RuntimeError):
@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_backward_workspace_size.restype = sz
+    L.gdn_backward_workspace_size.argtypes = [pdesc]
+    L.gdn_frame_backward.restype = ctypes.c_int
+    L.gdn_frame_backward.argtypes = [pdesc] + [vp] * 15 + [sz, vp]
     L.gdn_kernel_times.restype = ctypes.c_int
     L.gdn_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     if L.gdn_abi_version() != ABI_VERSION:
@@ -205,3 +209,47 @@ def frame_step(q, k, v, gamma, beta, state, beta_mode="erase", out=None, state_o
     out = _call("gdn_frame_step", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
                 workspace, stream, _flags(path, time_kernels))
     return out, state_out, norms
+
+
+def backward_workspace_size(desc: Desc) -> int:
+    return int(lib().gdn_backward_workspace_size(ctypes.byref(desc)))
+
+
+def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, beta_mode="erase",
+                   want=("dq", "dk", "dv", "dgamma", "dbeta", "dstate"), workspace=None, stream=None,
+                   time_kernels=False):
+    """Gradients of frame_forward(q, k, v, gamma, beta, state) for dL/dO = d_out and
+    dL/dM_final = d_state_out (or zero).  bf16 q, k, v, d_out [B,H,T,S,D]; T <= 1024.
+    Returns a dict with the requested gradients (dq, dk, dv bf16; dgamma, dbeta
+    [B,H,T] and dstate [B,H,D,D] fp32)."""
+    import torch
+    B, H, T, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_out", d_out), ("gamma", gamma), ("beta", beta)):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16 or any(t.dtype != torch.bfloat16 for t in (k, v, d_out)):
+        raise TypeError("frame_backward takes bfloat16 q, k, v and d_out")
+    desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
+    if workspace is None:
+        n = backward_workspace_size(desc)
+        if n == 0:
+            raise GDNError(6, "frame_backward: unsupported shape (bf16 only, T <= 1024)")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    out = {}
+    like = lambda: torch.empty_like(q)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    out["dq"] = like() if "dq" in want else None
+    out["dk"] = like() if "dk" in want else None
+    out["dv"] = like() if "dv" in want else None
+    out["dgamma"] = f32(B, H, T) if "dgamma" in want else None
+    out["dbeta"] = f32(B, H, T) if "dbeta" in want else None
+    out["dstate"] = f32(B, H, D, D) if "dstate" in want else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().gdn_frame_backward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma), _addr(beta),
+                                  _addr(state), _addr(d_out), _addr(d_state_out), _addr(out["dq"]),
+                                  _addr(out["dk"]), _addr(out["dv"]), _addr(out["dgamma"]), _addr(out["dbeta"]),
+                                  _addr(out["dstate"]), _addr(workspace), workspace.numel(),
+                                  ctypes.c_void_p(stream))
+    _raise(st)
+    return {k_: v_ for k_, v_ in out.items() if v_ is not None}

@@ -288,6 +288,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
       sa.snap = snap;
       sa.BH = (int)p.bh; sa.T = d->T; sa.t0 = t0 + f0; sa.Tc = f1 - f0;
       sa.Fs = tc; sa.f0 = f0; sa.beta_mode = d->beta_mode;
+      sa.snap_Fs = tc; sa.snap_f0 = f0;
       e = launch_timed(timed, GDN_KERNEL_STATE, st, [&] { return gdn::launch_state(d->D, sa, st); });
       if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
     }
@@ -368,6 +369,84 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
   hipStream_t s = (hipStream_t)stream;
   return p.gram ? run_gram(d, p, x, workspace, workspace_bytes, s)
                 : run_direct(d, p, x, workspace, workspace_bytes, s);
+}
+
+// ---------------------------------------------------------------------------
+// Backward.  Workspace, per head and frame (bf16 blocks unless noted): the
+// forward replay's G_t and B_t, the snapshots of M_{t-1} (T + 1 slots, slot 0
+// the initial state), C_t = ReLU(Q_t)^T dO_t, the snapshots of Lambda_t and
+// Z_t, and the adjoint pass's fp32 partial sums.
+// ---------------------------------------------------------------------------
+struct BackwardPlan {
+  size_t bh, gfb, bfb, sfb, pfb, io_bytes, gb_bytes, state_bytes;
+  size_t gfr, bfr, cfr, msnap, lsnap, zsnap, part, total;
+};
+
+BackwardPlan make_backward_plan(const gdn_desc* d) {
+  BackwardPlan b;
+  const size_t T = (size_t)d->T, D = (size_t)d->D, nb = D / 16;
+  b.bh = (size_t)d->B * (size_t)d->H;
+  b.gfb = gdn::gram_frame_bytes(d->D);
+  b.bfb = gdn::input_frame_bytes(d->D);
+  b.sfb = D * D * 2;
+  b.pfb = nb * nb * 16;
+  b.io_bytes = b.bh * T * (size_t)d->S * D * 2;
+  b.gb_bytes = b.bh * T * 4;
+  b.state_bytes = b.bh * D * D * 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t r = off; off += round_up(bytes); return r; };
+  b.gfr = take(b.bh * T * b.gfb);
+  b.bfr = take(b.bh * T * b.bfb);
+  b.cfr = take(b.bh * T * b.bfb);
+  b.msnap = take(b.bh * (T + 1) * b.sfb);
+  b.lsnap = take(b.bh * T * b.sfb);
+  b.zsnap = take(b.bh * T * b.sfb);
+  b.part = take(b.bh * T * b.pfb);
+  b.total = off;
+  return b;
+}
+
+gdn_status check_backward(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+                          const float* beta, const float* state_in, const void* d_out, const float* d_state_out,
+                          const void* dq, const void* dk, const void* dv, const float* d_gamma,
+                          const float* d_beta, const float* d_state_in, const void* workspace,
+                          size_t workspace_bytes) {
+  g_last_error.clear();
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  if (d->io_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn_frame_backward takes bf16 I/O only");
+  if (d->flags & GDN_FLAG_DIRECT) return fail(GDN_ERR_UNSUPPORTED, "gdn_frame_backward has no single-pass form");
+  if (d->T > kMaxFramesPerLaunch)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_frame_backward takes at most %d frames per call", kMaxFramesPerLaunch);
+  if (!q || !k || !v || !d_out) return fail(GDN_ERR_NULL, "q, k, v and d_out are required");
+  if (!gamma || !beta) return fail(GDN_ERR_NULL, "gamma and beta are required");
+  if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is required (gdn_backward_workspace_size)");
+  const BackwardPlan b = make_backward_plan(d);
+  if (workspace_bytes < b.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", workspace_bytes, b.total);
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(d_out, 16) || misaligned(dq, 16) ||
+      misaligned(dk, 16) || misaligned(dv, 16))
+    return fail(GDN_ERR_ALIGN, "q, k, v, d_out, dq, dk and dv must be 16-byte aligned");
+  if (misaligned(gamma, 4) || misaligned(beta, 4) || misaligned(state_in, 4) || misaligned(d_state_out, 4) ||
+      misaligned(d_gamma, 4) || misaligned(d_beta, 4) || misaligned(d_state_in, 4))
+    return fail(GDN_ERR_ALIGN, "gamma, beta, states and their gradients must be 4-byte aligned");
+  if (misaligned(workspace, kAlign)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+  struct Buf { const void* p; size_t n; const char* name; };
+  const Buf ins[] = {{q, b.io_bytes, "q"}, {k, b.io_bytes, "k"}, {v, b.io_bytes, "v"},
+                     {d_out, b.io_bytes, "d_out"}, {gamma, b.gb_bytes, "gamma"}, {beta, b.gb_bytes, "beta"},
+                     {state_in, b.state_bytes, "state_in"}, {d_state_out, b.state_bytes, "d_state_out"}};
+  const Buf outs[] = {{dq, b.io_bytes, "dq"}, {dk, b.io_bytes, "dk"}, {dv, b.io_bytes, "dv"},
+                      {d_gamma, b.gb_bytes, "d_gamma"}, {d_beta, b.gb_bytes, "d_beta"},
+                      {d_state_in, b.state_bytes, "d_state_in"}, {workspace, workspace_bytes, "workspace"}};
+  for (const Buf& x : outs) {
+    if (!x.p) continue;
+    for (const Buf& y : ins)
+      if (overlap(x.p, x.n, y.p, y.n)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
+    for (const Buf& y : outs)
+      if (&y != &x && y.p && overlap(x.p, x.n, y.p, y.n))
+        return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
+  }
+  return GDN_OK;
 }
 
 }  // namespace
@@ -494,6 +573,80 @@ gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_ou
     if (reset) { g_time_ms[i] = 0.0; g_time_n[i] = 0; }
   }
   return st;
+}
+
+size_t gdn_backward_workspace_size(const gdn_desc* d) {
+  if (check_desc(d) != GDN_OK || d->io_dtype != GDN_BF16 || d->T > kMaxFramesPerLaunch) return 0;
+  return make_backward_plan(d).total;
+}
+
+gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, const void* v,
+                              const float* gamma, const float* beta, const float* state_in,
+                              const void* d_out, const float* d_state_out,
+                              void* dq, void* dk, void* dv, float* d_gamma, float* d_beta, float* d_state_in,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  gdn_status st = check_backward(d, q, k, v, gamma, beta, state_in, d_out, d_state_out, dq, dk, dv, d_gamma,
+                                 d_beta, d_state_in, workspace, workspace_bytes);
+  if (st != GDN_OK) return st;
+  const BackwardPlan b = make_backward_plan(d);
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  const int BH = (int)b.bh, T = d->T, D = d->D;
+  const double c = 1.0 / std::sqrt((double)D * (double)d->S);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  void* msnap = ws + b.msnap;
+  hipError_t e = gdn::launch_state_snapshot(state_in, msnap, BH, D, (size_t)(T + 1) * b.sfb, s);
+  // forward replay: G_t and B_t, then M_t into snapshot slots 1..T
+  gdn::GramArgs ga;
+  ga.k = k; ga.v = v; ga.gfr = ws + b.gfr; ga.bfr = ws + b.bfr;
+  ga.BH = BH; ga.T = T; ga.S = d->S; ga.t0 = 0; ga.Tc = T;
+  ga.kscale = (float)c; ga.kscale2 = (float)(c * c); ga.fp8 = 0;
+  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(D, ga, s); });
+  gdn::StateArgs sa;
+  sa.gfr = ws + b.gfr; sa.bfr = ws + b.bfr; sa.gamma = gamma; sa.beta = beta;
+  sa.state_src = state_in; sa.state_dst = nullptr; sa.snap = msnap;
+  sa.BH = BH; sa.T = T; sa.t0 = 0; sa.Tc = T; sa.Fs = T; sa.f0 = 0; sa.beta_mode = d->beta_mode;
+  sa.snap_Fs = T + 1; sa.snap_f0 = 1;
+  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_STATE, s, [&] { return gdn::launch_state(D, sa, s); });
+  // C_t = ReLU(Q_t)^T dO_t
+  gdn::GramArgs gc = ga;
+  gc.k = q; gc.v = d_out; gc.gfr = nullptr; gc.bfr = ws + b.cfr; gc.kscale = 1.f; gc.kscale2 = 1.f;
+  if (e == hipSuccess)
+    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_gram_cross(D, gc, s); });
+  // adjoint pass
+  gdn::AdjointArgs aa;
+  aa.gfr = ws + b.gfr; aa.bfr = ws + b.bfr; aa.cfr = ws + b.cfr; aa.msnap = msnap;
+  aa.gamma = gamma; aa.beta = beta; aa.dstate_out = d_state_out; aa.dstate_in = d_state_in;
+  aa.lsnap = ws + b.lsnap; aa.part = (float*)(ws + b.part);
+  aa.BH = BH; aa.T = T; aa.beta_mode = d->beta_mode;
+  if (e == hipSuccess)
+    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_adjoint(D, aa, s); });
+  // gradient products
+  const bool write = d->beta_mode == GDN_BETA_WRITE;
+  auto product = [&](int kind, const void* x, void* out, const void* snap, int Fs, int f0, float scale,
+                     const float* s1, const float* s2, const void* mask) {
+    gdn::ReadoutArgs r{};
+    r.q = x; r.o = out; r.snap = snap; r.norm_part = nullptr; r.norms = nullptr;
+    r.BH = BH; r.T = T; r.S = d->S; r.t0 = 0; r.Tc = T; r.Fs = Fs; r.f0 = f0; r.fp8 = 0;
+    r.mask = mask; r.s1 = s1; r.s2 = s2; r.scale = scale;
+    return launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_grad_product(D, kind, r, s); });
+  };
+  if (e == hipSuccess && dq) e = product(gdn::kReadDQ, d_out, dq, msnap, T + 1, 1, 1.f, nullptr, nullptr, q);
+  if (e == hipSuccess && dv)
+    e = product(gdn::kReadDV, k, dv, ws + b.lsnap, T, 0, (float)c, write ? beta : nullptr, nullptr, nullptr);
+  if (e == hipSuccess && dk) {
+    gdn::ZmatArgs za;
+    za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
+    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
+    if (e == hipSuccess)
+      e = product(gdn::kReadDK1, v, dk, ws + b.lsnap, T, 0, (float)c, write ? beta : nullptr, nullptr, nullptr);
+    if (e == hipSuccess) e = product(gdn::kReadDK2, k, dk, ws + b.zsnap, T, 0, (float)(-c * c), beta, gamma, k);
+  }
+  if (e == hipSuccess && (d_gamma || d_beta))
+    e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,
+                                   d->beta_mode, s);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
+  return GDN_OK;
 }
 
 }  // extern "C"

@@ -128,13 +128,15 @@ constexpr uint32_t gram_ymask(int NB, int b0, int b1) {
 // twice that for launches too small to fill the GPU, where the time of one
 // workgroup is the latency of the whole launch).  Every block is accumulated
 // over the chunks in the same order whatever NW is, so the bits do not change.
-template <int D, bool FP8, int NW, int W>
+// CROSS: only the NB*NB blocks of X^T Y (the backward's C_t = ReLU(Q)^T dO with
+// the query in the key's place), no Gram blocks.
+template <int D, bool FP8, int NW, int W, bool CROSS = false>
 __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem, int bh, int tl) {
   using Sh = GramShape<D>;
   using IO = IoFmt<FP8>;
   constexpr int NB = Sh::NB, UPR = Sh::UPR, NLD = Sh::NLD, RS = Sh::RS;
   constexpr int LPW = (2 * NLD + NW - 1) / NW;        // pieces loaded per wave per chunk
-  constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT;
+  constexpr int NBB = Sh::NBB, NOUT = CROSS ? Sh::NBB : Sh::NOUT;
   constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
   constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
   const int l = lane_id(), g = l >> 4, n = l & 15;
@@ -241,7 +243,7 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   });
 }
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, bool CROSS = false>
 __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gram_kernel(GramArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int fh = blockIdx.x;   // over BH * Tc
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gr
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   static_for<NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    if (w == W) gram_wave<D, FP8, NW, W>(a, smem, bh, tl);
+    if (w == W) gram_wave<D, FP8, NW, W, CROSS>(a, smem, bh, tl);
   });
 }
 
@@ -516,8 +518,9 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
   const size_t fb = (size_t)bh * a.Fs + a.f0;
   const __amdgpu_buffer_rsrc_t grs = make_rsrc((const unsigned char*)a.gfr + fb * gfb, (uint32_t)(Tc * gfb));
   const __amdgpu_buffer_rsrc_t brs = make_rsrc((const unsigned char*)a.bfr + fb * bfb, (uint32_t)(Tc * bfb));
+  const size_t sfb = (size_t)bh * a.snap_Fs + a.snap_f0;
   const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc((unsigned char*)a.snap + fb * D * D * 2, (uint32_t)(Tc * D * D * 2));
+      make_rsrc((unsigned char*)a.snap + sfb * D * D * 2, (uint32_t)(Tc * D * D * 2));
   const __amdgpu_buffer_rsrc_t gars = make_rsrc(a.gamma + (size_t)bh * a.T + a.t0, (uint32_t)(Tc * 4));
   const __amdgpu_buffer_rsrc_t bers = make_rsrc(a.beta + (size_t)bh * a.T + a.t0, (uint32_t)(Tc * 4));
   const uint32_t bbase = (uint32_t)((j * NB + I) * 512 + l * 8);
@@ -625,6 +628,201 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
   });
 }
 
+
+// ----------------------------------------------------------------------------
+// Adjoint state pass (backward).  Write Lambda_t for dL/dM_t, the gradient of
+// the loss with respect to the post-update state of frame t through
+// everything after it.  The forward update M_t = g M_{t-1} - b g G_t M_{t-1} +
+// w B_t (w = 1 ERASE, b WRITE) and the readout O_t = ReLU(Q_t) M_t give,
+// frames last to first,
+//   Lambda_{T-1} = dL/dM_final + C_{T-1},       C_t = ReLU(Q_t)^T dO_t,
+//   Lambda_{t-1} = g_t Lambda_t - b_t g_t G_t Lambda_t + C_{t-1}
+// (G_t is symmetric), and dL/dM_in = g_0 Lambda_0 - b_0 g_0 G_0 Lambda_0.  The
+// workgroup layout is the state pass's: one workgroup per (head, value tile
+// j), wave I owns the fp32 block Lambda[16I..16I+15][16j..16j+15], and the
+// product G_t bf16(Lambda_t) is formed as the state pass forms G_t bf16(M).
+// Per frame each wave also writes its block of the bf16 snapshot of Lambda_t
+// and the partial sums over its block of <Lambda_t, M_{t-1}>,
+// <G_t Lambda_t, M_{t-1}> and (WRITE) <Lambda_t, B_t>, from which
+//   dL/dg_t = <Lambda_t, M_{t-1}> - b_t <G_t Lambda_t, M_{t-1}>,
+//   dL/db_t = -g_t <G_t Lambda_t, M_{t-1}>   (+ <Lambda_t, B_t> for WRITE)
+// are summed in a fixed order by gdn_adjoint_reduce.
+// ----------------------------------------------------------------------------
+template <int D, bool ERASE, int I>
+__device__ __forceinline__ void adjoint_wave(const AdjointArgs& a, unsigned char* smem, int bh, int j) {
+  using Sh = StateShape<D>;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, NGL = Sh::NGL, LPG = Sh::LPG;
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  const int T = a.T;
+  unsigned char* gsl = smem;                                  // 2 G slots
+  unsigned char* xch = smem + 2 * Sh::g_slot;                 // 2 exchange buffers
+
+  if ((NB & 1) && I == 0) {
+    *(u32x2*)(xch + ((size_t)(NKC - 1) * 64 + l) * 16 + 8) = u32x2{0u, 0u};
+    *(u32x2*)(xch + Sh::xch_bytes / 2 + ((size_t)(NKC - 1) * 64 + l) * 16 + 8) = u32x2{0u, 0u};
+  }
+  const int row0 = 16 * I + 4 * g, col = 16 * j + n;
+  const size_t gfb = GramShape<D>::g_frame_bytes, bfb = GramShape<D>::b_frame_bytes;
+  const size_t sfb = (size_t)D * D * 2;
+  const size_t hb = (size_t)bh * T;
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc((const unsigned char*)a.gfr + hb * gfb, (uint32_t)(T * gfb));
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc((const unsigned char*)a.bfr + hb * bfb, (uint32_t)(T * bfb));
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc((const unsigned char*)a.cfr + hb * bfb, (uint32_t)(T * bfb));
+  const __amdgpu_buffer_rsrc_t mrs =
+      make_rsrc((const unsigned char*)a.msnap + (size_t)bh * (T + 1) * sfb, (uint32_t)((T + 1) * sfb));
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc((unsigned char*)a.lsnap + hb * sfb, (uint32_t)(T * sfb));
+  const __amdgpu_buffer_rsrc_t prs =
+      make_rsrc(a.part + hb * (size_t)(NB * NB * 4), (uint32_t)(T * NB * NB * 16));
+  const __amdgpu_buffer_rsrc_t gars = make_rsrc(a.gamma + hb, (uint32_t)(T * 4));
+  const __amdgpu_buffer_rsrc_t bers = make_rsrc(a.beta + hb, (uint32_t)(T * 4));
+  const uint32_t bbase = (uint32_t)((j * NB + I) * 512 + l * 8);        // B / C block (I, j)
+  const uint32_t sbase = (uint32_t)(((j * NB + I) * 64 + l) * 8);       // snapshot block (I, j)
+  auto widen4 = [](u32x2 w) -> f32x4 {
+    return f32x4{bf16_lo_f32(w[0]), bf16_hi_f32(w[0]), bf16_lo_f32(w[1]), bf16_hi_f32(w[1])};
+  };
+
+  // Lambda_{T-1} = dL/dM_final + C_{T-1}
+  f32x4 m = {0.f, 0.f, 0.f, 0.f};
+  if (a.dstate_out) {
+    const float* src = a.dstate_out + (size_t)bh * D * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = src[(size_t)(row0 + r) * D + col];
+  }
+  {
+    const f32x4 c0 = widen4(__builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(crs, (uint32_t)(T - 1) * (uint32_t)bfb + bbase, 0, 0)));
+    m += c0;
+  }
+  auto publish = [&](int buf, f32x4 x) {
+    const u32x2 v = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    *(u32x2*)(xch + (size_t)buf * (Sh::xch_bytes / 2) + ((size_t)(I >> 1) * 64 + l) * 16 + 8 * (I & 1)) = v;
+    return v;
+  };
+  u32x2 pub = publish(0, m);
+
+  u32x4 Gr[kStateRing][LPG];
+  u32x2 Cp[kStateRing], Mp[kStateRing], Bf[kStateRing];
+  float Ga[kStateRing], Be[kStateRing];
+  // step u handles frame t = T-1-u
+  auto load_frame = [&](int u, int r) {
+    const int t = T - 1 - u;
+    const bool ok = u < T;
+    Ga[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gars, ok ? (uint32_t)t * 4u : kOOB, 0, 0));
+    Be[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bers, ok ? (uint32_t)t * 4u : kOOB, 0, 0));
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int q = I + NB * i;
+      Gr[r][i] = buf_load16(grs, (ok && q < NGL) ? (uint32_t)t * (uint32_t)gfb + q * 1024 + l * 16 : kOOB);
+    }
+    Cp[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                          crs, (ok && t >= 1) ? (uint32_t)(t - 1) * (uint32_t)bfb + bbase : kOOB, 0, 0));
+    Mp[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                          mrs, ok ? (uint32_t)t * (uint32_t)sfb + sbase : kOOB, 0, 0));
+    Bf[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                          brs, (!ERASE && ok) ? (uint32_t)t * (uint32_t)bfb + bbase : kOOB, 0, 0));
+  };
+  auto stage_g = [&](int slot, int r) {
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int q = I + NB * i;
+      if (q < NGL) *(u32x4*)(gsl + (size_t)slot * Sh::g_slot + q * 1024 + l * 16) = Gr[r][i];
+    }
+  };
+  auto g_half = [&](const unsigned char* gs, auto Lc) -> u32x2 {
+    constexpr int L = decltype(Lc)::value;
+    if constexpr (L >= NB) {
+      return u32x2{0u, 0u};
+    } else if constexpr (L <= I) {
+      return *(const u32x2*)(gs + (size_t)(I * (I + 1) / 2 + L) * 512 + l * 8);
+    } else {
+      const unsigned char* blk = gs + (size_t)(L * (L + 1) / 2 + I) * 512;
+      return lds_tr16((const uint16_t*)(blk + ((n & 3) * 16 + 4 * g + (n >> 2)) * 8));
+    }
+  };
+
+#pragma unroll
+  for (int r = 0; r < kStateRing; ++r) load_frame(r, r);
+  stage_g(0, 0);
+  lds_barrier();
+
+  for (int base = 0; base < T; base += kStateRing) {
+#pragma unroll
+    for (int r = 0; r < kStateRing; ++r) {
+      const int u = base + r, t = T - 1 - u;
+      const bool ok = u < T;
+      const unsigned char* xr = xch + (size_t)(r & 1) * (Sh::xch_bytes / 2);
+      const unsigned char* gs = gsl + (size_t)(r & 1) * Sh::g_slot;
+      // bf16 snapshot of Lambda_t: the copy the waves exchanged
+      __builtin_amdgcn_raw_buffer_store_b64(pub, lrs, ok ? (uint32_t)t * (uint32_t)sfb + sbase : kOOB, 0, 0);
+      u32x4 aop[NKC], bop[NKC];
+      static_for<NKC>([&](auto kbc) {
+        constexpr int kb = decltype(kbc)::value;
+        const u32x2 lo = g_half(gs, Int<2 * kb>{}), hi = g_half(gs, Int<2 * kb + 1>{});
+        aop[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        bop[kb] = *(const u32x4*)(xr + ((size_t)kb * 64 + l) * 16);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) p = mfma_bf16(aop[kb], bop[kb], p);
+      const float gm = Ga[r], bt = Be[r], bg = bt * gm;
+      // partial sums over this wave's block
+      const f32x4 mp = widen4(Mp[r]);
+      float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s1 += m[e] * mp[e];
+        s2 += p[e] * mp[e];
+      }
+      if constexpr (!ERASE) {
+        const f32x4 bw = widen4(Bf[r]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s3 += m[e] * bw[e];
+      }
+#pragma unroll
+      for (int sft = 32; sft >= 1; sft >>= 1) {
+        s1 += __shfl_xor(s1, sft, 64);
+        s2 += __shfl_xor(s2, sft, 64);
+        if constexpr (!ERASE) s3 += __shfl_xor(s3, sft, 64);
+      }
+      const f32x4 ps = {s1, s2, s3, 0.f};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, ps), prs,
+          (ok && l == 0) ? (uint32_t)((t * NB * NB + j * NB + I) * 16) : kOOB, 0, 0);
+      // Lambda_{t-1} = g Lambda_t - b g G_t Lambda_t + C_{t-1}
+      const f32x4 cp = widen4(Cp[r]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float nv = gm * m[e] - bg * p[e] + cp[e];
+        m[e] = ok ? nv : m[e];
+      }
+      stage_g((r + 1) & 1, (r + 1) % kStateRing);
+      load_frame(u + kStateRing, r);
+      pub = publish((r & 1) ^ 1, m);
+      lds_barrier();
+    }
+  }
+  if (a.dstate_in) {
+    float* dst = a.dstate_in + (size_t)bh * D * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(size_t)(row0 + r) * D + col] = m[r];
+  }
+}
+
+template <int D, bool ERASE>
+__global__ __launch_bounds__(D / 16 * 64, 1) void gdn_adjoint_bf16_kernel(AdjointArgs a) {
+  constexpr int NB = D / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int unit = xcd_unit(a.BH * NB);
+  if (unit < 0) return;
+  const int bh = unit / NB, j = unit % NB;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  static_for<NB>([&](auto ic) {
+    constexpr int I = decltype(ic)::value;
+    if (w == I) adjoint_wave<D, ERASE, I>(a, smem, bh, j);
+  });
+}
+
 // ----------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------
@@ -700,6 +898,44 @@ static hipError_t launch_state_t(const StateArgs& sa, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_gram_cross_t(const GramArgs& ga, hipStream_t stream) {
+  constexpr int NW = GramShape<D>::NW;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, false, NW, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gdn_gram_kernel<D, false, NW, true>), dim3((unsigned)(ga.BH * ga.Tc)), dim3(NW * 64),
+                     GramShape<D>::lds_bytes, stream, ga);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_adjoint_t(const AdjointArgs& aa, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gdn_adjoint_bf16_kernel<D, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gdn_adjoint_bf16_kernel<D, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int units = aa.BH * (D / 16);
+  const int grid = 8 * ((units + 7) / 8);
+  if (aa.beta_mode == 0)
+    hipLaunchKernelGGL((gdn_adjoint_bf16_kernel<D, true>), dim3(grid), dim3(D / 16 * 64), StateShape<D>::lds_bytes,
+                       stream, aa);
+  else
+    hipLaunchKernelGGL((gdn_adjoint_bf16_kernel<D, false>), dim3(grid), dim3(D / 16 * 64), StateShape<D>::lds_bytes,
+                       stream, aa);
+  return hipGetLastError();
+}
+
 #define GDN_DISPATCH(FN, ARGS)                                                 \
   switch (D) {                                                                 \
     case 16: return FN<16> ARGS;                                               \
@@ -718,6 +954,12 @@ hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream) {
 }
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream) {
   GDN_DISPATCH(launch_state_t, (sa, stream))
+}
+hipError_t launch_gram_cross(int D, const GramArgs& ga, hipStream_t stream) {
+  GDN_DISPATCH(launch_gram_cross_t, (ga, stream))
+}
+hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream) {
+  GDN_DISPATCH(launch_adjoint_t, (aa, stream))
 }
 #undef GDN_DISPATCH
 

@@ -37,6 +37,19 @@ struct ReadoutArgs {
   int BH, T, S, t0, Tc;
   int Fs, f0;               // snapshots (and norm partials) hold [BH][Fs] frames from f0
   int fp8;                  // 1: Q and O are OCP e4m3 bytes (bf16 snapshots only)
+  // gradient products of the backward (see ReadoutMode in gdn_kernels.hip):
+  const void* mask;         // [BH][T][S][D] bf16: output zeroed where mask <= 0
+  const float* s1;          // [BH][T] per-frame output scale factor or nullptr
+  const float* s2;          // [BH][T] second per-frame factor or nullptr
+  float scale;              // constant output scale
+};
+
+// Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame) (backward).
+struct ZmatArgs {
+  const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
+  const void* lsnap;        // bf16 snapshots of Lambda_t: [BH][T]
+  void* zsnap;              // out: bf16 snapshots of Z_t: [BH][T]
+  int BH, T;
 };
 
 // Gram pass (bf16 or e4m3 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
@@ -62,6 +75,22 @@ struct StateArgs {
   int BH, T, t0, Tc;
   int Fs, f0;               // staging arrays hold [BH][Fs] frames; this launch's first frame is f0
   int beta_mode;            // 0 ERASE, 1 WRITE
+  int snap_Fs, snap_f0;     // snapshot array: [BH][snap_Fs] frames, this launch's first at snap_f0
+};
+
+// Adjoint state pass of the backward: Lambda_t = dL/dM_t, frames last to first.
+struct AdjointArgs {
+  const void* gfr;          // G_t as in GramArgs, [BH][T] frames
+  const void* bfr;          // B_t (WRITE mode only; else unused), [BH][T]
+  const void* cfr;          // C_t = ReLU(Q_t)^T dO_t in B's layout, [BH][T]
+  const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
+  const float* gamma;       // [BH][T]
+  const float* beta;        // [BH][T]
+  const float* dstate_out;  // [BH][D][D] or nullptr
+  float* dstate_in;         // [BH][D][D] or nullptr
+  void* lsnap;              // out: bf16 snapshots of Lambda_t, [BH][T] (block layout)
+  float* part;              // out: [BH][T][NB*NB][4] per-wave partial sums
+  int BH, T, beta_mode;
 };
 
 // Kernel launchers (enqueue only).  D in {16, ..., 128}.
@@ -69,6 +98,19 @@ hipError_t launch_recurrence(int D, bool bf16, const RecurArgs& ra, hipStream_t 
 hipError_t launch_readout(int D, bool bf16, const ReadoutArgs& ro, hipStream_t stream);
 hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream);
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream);
+hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream);
+hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream);
+hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
+                                 hipStream_t stream);
+hipError_t launch_adjoint_reduce(const float* part, const float* gamma, const float* beta, float* dgamma,
+                                 float* dbeta, int BH, int T, int D, int beta_mode, hipStream_t stream);
+// Gradient products: O = scale * X W (optionally W^T, ReLU on X, += existing O,
+// masked), X streamed like Q in the readout, W from block snapshots.
+enum ReadoutKind { kReadDQ = 1, kReadDV = 2, kReadDK1 = 3, kReadDK2 = 4 };
+hipError_t launch_grad_product(int D, int kind, const ReadoutArgs& ro, hipStream_t stream);
+// C_t = ReLU(Q_t)^T dO_t per (head, frame), in B's layout (the gram pass's
+// cross blocks with scale 1): ga.k = q, ga.v = dO, ga.bfr = C array.
+hipError_t launch_gram_cross(int D, const GramArgs& ga, hipStream_t stream);
 
 // Workspace bytes per (head, frame) of the Gram pass outputs.
 size_t gram_frame_bytes(int D);

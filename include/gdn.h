@@ -104,7 +104,8 @@ typedef enum gdn_status {
 #define GDN_KERNEL_READOUT 1    /* O_t = Qf M_t from the per-frame state snapshots */
 #define GDN_KERNEL_GRAM 2       /* Gram pass: G_t, B_t per (head, frame) */
 #define GDN_KERNEL_STATE 3      /* serial state pass over G_t, B_t */
-#define GDN_KERNEL_SLOTS 4
+#define GDN_KERNEL_BACKWARD 4   /* the backward's own kernels (its forward replay books as GRAM/STATE) */
+#define GDN_KERNEL_SLOTS 5
 
 typedef struct gdn_desc {
   int32_t abi_version; /* GDN_ABI_VERSION */
@@ -173,6 +174,31 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
                           const float* gamma, const float* beta, const float* state_in,
                           void* o, float* state_out, float* state_norms,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of gdn_frame_forward (bf16 I/O; the single-pass recurrence and e4m3
+ * I/O have none): given dL/dO (d_out, [B][H][T][S][D] bf16) and optionally
+ * dL/dM_final (d_state_out, fp32 [B][H][D][D]) for the forward over the same
+ * q, k, v, gamma, beta and state_in, writes
+ *   dq, dk, dv    [B][H][T][S][D] bf16   (each may be NULL: not computed)
+ *   d_gamma, d_beta [B][H][T] fp32       (may be NULL)
+ *   d_state_in    [B][H][D][D] fp32      (may be NULL)
+ * The gradients are those of the recurrence in the SANA-WM news article
+ * ("NVIDIA Apresenta SANA-WM ...", section "1. Atencao Linear Hibrida com Gated
+ * DeltaNet (GDN)"), taken in exact arithmetic (ReLU's derivative is 0 at 0)
+ * and evaluated with the same bf16 operands as the forward.  The forward is
+ * replayed inside the call (its per-frame states are not kept by
+ * gdn_frame_forward).  T <= 1024 frames per call; the workspace must hold
+ * gdn_backward_workspace_size(d) bytes (0 if d is invalid or unsupported).
+ * Same conventions as gdn_frame_forward (device pointers, stream, errors);
+ * no output may overlap an input or another output.
+ */
+size_t gdn_backward_workspace_size(const gdn_desc* d);
+gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, const void* v,
+                              const float* gamma, const float* beta, const float* state_in,
+                              const void* d_out, const float* d_state_out,
+                              void* dq, void* dk, void* dv, float* d_gamma, float* d_beta, float* d_state_in,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Device time of the kernels launched by calls that set GDN_FLAG_TIME_KERNELS
