@@ -9,8 +9,9 @@ oracle's CPU rate on a bounded sample.  A `streaming` field adds the
 chunk-causal rollout check: the short-clip shape (B1 H16 T81 S880 D64) fed 4
 frames per gdn_frame_step call, its per-chunk latency and back-to-back rate.
 A `variants` field times the same 720p-shaped step with OCP E4M3 Q, K, V, O
-(the low-precision I/O variant, 4*D bytes per token-head); the headline
-`value` stays the bf16 step.
+(the low-precision I/O variant, 4*D bytes per token-head), and a `backward`
+field times gdn_frame_backward on the bf16 inputs (14*D algorithmic bytes per
+token-head); the headline `value` stays the bf16 forward step.
 
 The default bf16 path is the Gram pipeline (gram pass, serial state pass,
 readout); --path direct times the single-pass recurrence instead.
@@ -163,12 +164,45 @@ def fp8_variant(gdn, wl, torch, dev, steps: int, warmup: int):
                               "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes}}
 
 
+def backward_variant(gdn, wl, torch, dev, inp, steps: int, warmup: int):
+    """gdn_frame_backward on the same 720p-shaped inputs (dL/dO Gaussian, bf16):
+    algorithmic bytes 14*D per token-head (q, k, v, dO read; dq, dk, dv written)."""
+    w = wl.MINUTE_720P
+    g = torch.Generator(device=dev).manual_seed(11)
+    d_out = torch.randn((w.B, w.H, w.T, w.S, w.D), generator=g, device=dev).to(torch.bfloat16)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, "bf16", w.beta_mode)
+    ws = torch.empty(gdn.backward_workspace_size(desc), dtype=torch.uint8, device=dev)
+    call = lambda timed: gdn.frame_backward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], d_out,
+                                            beta_mode=w.beta_mode, workspace=ws, time_kernels=timed)
+    for _ in range(warmup):
+        call(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call(False)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gdn.kernel_times(reset=True)
+    for _ in range(steps):
+        call(True)
+    torch.cuda.synchronize()
+    kms = {name: t / steps for name, (t, n) in gdn.kernel_times(reset=True).items() if n > 0}
+    path_bytes = w.B * w.H * w.T * w.S * 14 * w.D
+    gbs = path_bytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "kernels_ms_per_step": kms,
+            "path_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-heads", type=int, default=12, help="oracle heads timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--no-backward", dest="backward", action="store_false",
+                    help="skip the timing of gdn_frame_backward on the same inputs")
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the E4M3 I/O variant of the step")
     ap.add_argument("--stream-reps", type=int, default=5,
@@ -271,6 +305,8 @@ def main():
     }
     if args.stream_reps > 0:
         rec["streaming"] = streaming_latency(gdn, wl, torch, dev, args.stream_reps)
+    if args.backward and args.path == "auto":
+        rec["backward"] = backward_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
     if args.fp8 and args.path == "auto":
         rec["variants"] = {"fp8_e4m3_io": fp8_variant(gdn, wl, torch, dev, args.steps, args.warmup)}
     if args.cpu_heads > 0:

@@ -99,3 +99,26 @@ def test_backward_repeat_is_bitwise(env):
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_backward_minute_720p_sampled_head(env):
+    """The 720p-shaped launch (B1 H20 T961 S880 D112, one call); reference
+    gradients on a sampled head."""
+    torch, gdn, wl, go, gb = env
+    w = wl.MINUTE_720P
+    inp = wl.generate(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    d_out = torch.randn((w.B, w.H, w.T, w.S, w.D), generator=g, device="cuda").to(torch.bfloat16)
+    got = gdn.frame_backward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], d_out)
+    torch.cuda.synchronize()
+    for key in got:
+        assert bool(torch.isfinite(got[key].float()).all()), key
+    b, h = 0, 7
+    ref = gb.backward_head(*(f64(torch, inp[n][b, h]) for n in ("q", "k", "v")), f64(torch, inp["gamma"][b, h]),
+                           f64(torch, inp["beta"][b, h]), f64(torch, d_out[b, h]))
+    errs = {key: rel(f64(torch, got[key][b, h]), ref[rk]) for key, rk in
+            (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dgamma", "dgamma"), ("dbeta", "dbeta"),
+             ("dstate", "dstate_in"))}
+    print({k: f"{v:.2e}" for k, v in errs.items()})
+    for k, v in errs.items():
+        assert v < TOL, f"{k}: rel err {v:.3e}"
