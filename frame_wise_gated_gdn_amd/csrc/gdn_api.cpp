@@ -576,7 +576,9 @@ gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_ou
 }
 
 size_t gdn_backward_workspace_size(const gdn_desc* d) {
-  if (check_desc(d) != GDN_OK || d->io_dtype != GDN_BF16 || d->T > kMaxFramesPerLaunch) return 0;
+  if (check_desc(d) != GDN_OK || d->io_dtype != GDN_BF16 || (d->flags & GDN_FLAG_DIRECT) ||
+      d->T > kMaxFramesPerLaunch)
+    return 0;
   return make_backward_plan(d).total;
 }
 
@@ -608,11 +610,10 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
   sa.BH = BH; sa.T = T; sa.t0 = 0; sa.Tc = T; sa.Fs = T; sa.f0 = 0; sa.beta_mode = d->beta_mode;
   sa.snap_Fs = T + 1; sa.snap_f0 = 1;
   if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_STATE, s, [&] { return gdn::launch_state(D, sa, s); });
-  // C_t = ReLU(Q_t)^T dO_t
-  gdn::GramArgs gc = ga;
-  gc.k = q; gc.v = d_out; gc.gfr = nullptr; gc.bfr = ws + b.cfr; gc.kscale = 1.f; gc.kscale2 = 1.f;
-  if (e == hipSuccess)
-    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_gram_cross(D, gc, s); });
+  // C_t = ReLU(Q_t)^T dO_t and dQ_t in one pass over Q and dO
+  gdn::CdqArgs ca;
+  ca.q = q; ca.dout = d_out; ca.msnap = msnap; ca.cfr = ws + b.cfr; ca.dq = dq; ca.BH = BH; ca.T = T; ca.S = d->S;
+  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_cdq(D, ca, s); });
   // adjoint pass
   gdn::AdjointArgs aa;
   aa.gfr = ws + b.gfr; aa.bfr = ws + b.bfr; aa.cfr = ws + b.cfr; aa.msnap = msnap;
@@ -621,26 +622,17 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
   aa.BH = BH; aa.T = T; aa.beta_mode = d->beta_mode;
   if (e == hipSuccess)
     e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_adjoint(D, aa, s); });
-  // gradient products
-  const bool write = d->beta_mode == GDN_BETA_WRITE;
-  auto product = [&](int kind, const void* x, void* out, const void* snap, int Fs, int f0, float scale,
-                     const float* s1, const float* s2, const void* mask) {
-    gdn::ReadoutArgs r{};
-    r.q = x; r.o = out; r.snap = snap; r.norm_part = nullptr; r.norms = nullptr;
-    r.BH = BH; r.T = T; r.S = d->S; r.t0 = 0; r.Tc = T; r.Fs = Fs; r.f0 = f0; r.fp8 = 0;
-    r.mask = mask; r.s1 = s1; r.s2 = s2; r.scale = scale;
-    return launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_grad_product(D, kind, r, s); });
-  };
-  if (e == hipSuccess && dq) e = product(gdn::kReadDQ, d_out, dq, msnap, T + 1, 1, 1.f, nullptr, nullptr, q);
-  if (e == hipSuccess && dv)
-    e = product(gdn::kReadDV, k, dv, ws + b.lsnap, T, 0, (float)c, write ? beta : nullptr, nullptr, nullptr);
+  // dV and dK in one pass over K and V (Z_t first, when dK is wanted)
   if (e == hipSuccess && dk) {
     gdn::ZmatArgs za;
     za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
     e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
-    if (e == hipSuccess)
-      e = product(gdn::kReadDK1, v, dk, ws + b.lsnap, T, 0, (float)c, write ? beta : nullptr, nullptr, nullptr);
-    if (e == hipSuccess) e = product(gdn::kReadDK2, k, dk, ws + b.zsnap, T, 0, (float)(-c * c), beta, gamma, k);
+  }
+  if (e == hipSuccess && (dv || dk)) {
+    gdn::DvkArgs da;
+    da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.zsnap = ws + b.zsnap; da.gamma = gamma; da.beta = beta;
+    da.dv = dv; da.dk = dk; da.BH = BH; da.T = T; da.S = d->S; da.beta_mode = d->beta_mode; da.kscale = (float)c;
+    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_dvdk(D, da, s); });
   }
   if (e == hipSuccess && (d_gamma || d_beta))
     e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,

@@ -128,15 +128,13 @@ constexpr uint32_t gram_ymask(int NB, int b0, int b1) {
 // twice that for launches too small to fill the GPU, where the time of one
 // workgroup is the latency of the whole launch).  Every block is accumulated
 // over the chunks in the same order whatever NW is, so the bits do not change.
-// CROSS: only the NB*NB blocks of X^T Y (the backward's C_t = ReLU(Q)^T dO with
-// the query in the key's place), no Gram blocks.
-template <int D, bool FP8, int NW, int W, bool CROSS = false>
+template <int D, bool FP8, int NW, int W>
 __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem, int bh, int tl) {
   using Sh = GramShape<D>;
   using IO = IoFmt<FP8>;
   constexpr int NB = Sh::NB, UPR = Sh::UPR, NLD = Sh::NLD, RS = Sh::RS;
   constexpr int LPW = (2 * NLD + NW - 1) / NW;        // pieces loaded per wave per chunk
-  constexpr int NBB = Sh::NBB, NOUT = CROSS ? Sh::NBB : Sh::NOUT;
+  constexpr int NBB = Sh::NBB, NOUT = Sh::NOUT;
   constexpr int B0 = W * NOUT / NW, B1 = (W + 1) * NOUT / NW, NMB = B1 - B0;   // my output blocks
   constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
   const int l = lane_id(), g = l >> 4, n = l & 15;
@@ -243,7 +241,7 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   });
 }
 
-template <int D, bool FP8, int NW, bool CROSS = false>
+template <int D, bool FP8, int NW>
 __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gram_kernel(GramArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int fh = blockIdx.x;   // over BH * Tc
@@ -251,7 +249,7 @@ __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gr
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   static_for<NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    if (w == W) gram_wave<D, FP8, NW, W, CROSS>(a, smem, bh, tl);
+    if (w == W) gram_wave<D, FP8, NW, W>(a, smem, bh, tl);
   });
 }
 
@@ -630,6 +628,182 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
 
 
 // ----------------------------------------------------------------------------
+// Backward: C_t = ReLU(Q_t)^T dO_t and dQ_t = (dO_t M_t^T) * [Q_t > 0] in one
+// pass over Q_t and dO_t.  One workgroup per (head, frame) with the gram
+// pass's waves and chunk pipeline (Q in the key's place, dO in the value's):
+// every wave accumulates its compile-time range of the NB*NB blocks of C as
+// the gram pass accumulates B, and also forms dQ for its output column
+// blocks jb = W, W + NW, ... from the staged chunk, with M_t^T as MFMA A
+// operands in registers (transposed LDS reads of the staged snapshot of
+// M_t) and the mask read from the staged ReLU(Q).  dQ is assembled in an LDS
+// tile and stored with the loads' coalesced 1 KB pieces; C goes out at the
+// end of the frame in B's layout.
+// ----------------------------------------------------------------------------
+template <int D, int W>
+__device__ __forceinline__ void cdq_wave(const CdqArgs& a, unsigned char* smem, int bh, int t) {
+  using Sh = GramShape<D>;
+  constexpr int NB = Sh::NB, NW = Sh::NW, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, RS = Sh::RS;
+  constexpr int NKC = Sh::NKC, NBB = Sh::NBB;
+  constexpr int B0 = W * NBB / NW, B1 = (W + 1) * NBB / NW, NMB = B1 - B0;   // my C blocks
+  constexpr uint32_t XM = gram_xmask(NB, B0, B1), YM = gram_ymask(NB, B0, B1);
+  constexpr int JPW = (NB + NW - 1) / NW;                                    // my dQ column blocks
+  constexpr int SPW = (NLD + NW - 1) / NW;                                   // dQ pieces stored per wave
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  const int S = a.S, T = a.T;
+  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
+  const size_t head0 = (size_t)bh * T * S * D * 2;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const unsigned char*)a.q + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc((const unsigned char*)a.dout + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t dqrs =
+      make_rsrc(a.dq ? (unsigned char*)a.dq + head0 : nullptr, a.dq ? head_bytes : 0u);
+  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * 2u;
+  // chunks in flight (even, for the LDS buffer parity); at D = 128 a deeper
+  // ring does not fit the registers next to the C accumulators and M_t^T
+  constexpr int RG = D >= 128 ? 2 : kGramRing;
+  const int nch = (S + 31) / 32;
+  const int nit = (nch + RG - 1) / RG * RG;
+  uint16_t* const ot = (uint16_t*)(smem + 4 * Sh::tile_bytes);               // dQ tile
+
+  // M_t^T operands of my column blocks (snapshot staged in the tiles' space)
+  const unsigned char* msn = (const unsigned char*)a.msnap + ((size_t)bh * (T + 1) + t + 1) * D * D * 2;
+  for (int u = (int)threadIdx.x; u < D * D * 2 / 16; u += NW * 64)
+    *(u32x4*)(smem + (size_t)u * 16) = *(const u32x4*)(msn + (size_t)u * 16);
+  __syncthreads();
+  const uint32_t trofs = (uint32_t)(((n & 3) * 16 + 4 * g + (n >> 2)) * 8);
+  u32x4 AM[JPW][NKC];
+  static_for<JPW>([&](auto ic) {
+    constexpr int i = decltype(ic)::value, jb = W + NW * i;
+    if constexpr (jb < NB) {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const u32x2 lo = lds_tr16((const uint16_t*)(smem + (size_t)((2 * kc) * NB + jb) * 512 + trofs));
+        const u32x2 hi = (2 * kc + 1 < NB)
+                             ? lds_tr16((const uint16_t*)(smem + (size_t)((2 * kc + 1) * NB + jb) * 512 + trofs))
+                             : u32x2{0u, 0u};
+        AM[i][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+  });
+  __syncthreads();
+
+  auto unit_off = [&](int ch, int u) -> uint32_t {
+    const int tok = ch * 32 + u / UPR;
+    return (ch < nch && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * 16u : kOOB;
+  };
+  auto load_chunk = [&](int ch, u32x4 (&X)[LPW]) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int p = W + NW * i;
+      const uint32_t off = p < 2 * NLD ? unit_off(ch, 64 * (p % NLD) + l) : kOOB;
+      X[i] = buf_load16_nt(p < NLD ? qrs : drs, off);
+    }
+  };
+  auto stage = [&](int buf, const u32x4 (&X)[LPW]) {
+    uint16_t* qt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
+    uint16_t* dt = qt + 32 * RS;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int p = W + NW * i;
+      if (p < 2 * NLD) {
+        const int u = 64 * (p % NLD) + l;
+        *(u32x4*)((p < NLD ? qt : dt) + (u / UPR) * RS + 8 * (u % UPR)) = p < NLD ? relu8(X[i]) : X[i];
+      }
+    }
+  };
+  auto frag = [&](const uint16_t* tile, int blk) -> u32x4 {
+    const uint16_t* p0 = tile + (4 * g + (n >> 2)) * RS + 16 * blk + 4 * (n & 3);
+    const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
+    return u32x4{x[0], x[1], y[0], y[1]};
+  };
+
+  f32x4 acc[NMB];
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 R[RG][LPW];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) load_chunk(r, R[r]);
+
+  for (int base = 0; base < nit; base += RG) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int c = base + r;
+      stage(r & 1, R[r]);
+      load_chunk(c + RG, R[r]);
+      lds_barrier();
+      if (c < nch) {
+        const uint16_t* qt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
+        const uint16_t* dt = qt + 32 * RS;
+        u32x4 X[NB], Y[NB];
+        static_for<NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr ((XM >> j) & 1u) X[j] = frag(qt, j);
+          if constexpr ((YM >> j) & 1u) Y[j] = frag(dt, j);
+        });
+        static_for<NMB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value, b = B0 + i;
+          acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
+        });
+        static_for<JPW>([&](auto ic) {
+          constexpr int i = decltype(ic)::value, jb = W + NW * i;
+          if constexpr (jb < NB) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              u32x4 BD[NKC];
+#pragma unroll
+              for (int kc = 0; kc < NKC; ++kc) {
+                const uint16_t* rp = dt + (16 * half + n) * RS + 32 * kc + 4 * g;
+                const u32x2 lo = *(const u32x2*)rp;
+                const u32x2 hi = (32 * kc + 32 <= D) ? *(const u32x2*)(rp + 16) : u32x2{0u, 0u};
+                BD[kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+              }
+              f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kc = 0; kc < NKC; ++kc) y = mfma_bf16(AM[i][kc], BD[kc], y);
+              const int oo = (16 * half + n) * RS + 16 * jb + 4 * g;
+              const u32x2 qr = *(const u32x2*)(qt + oo);    // ReLU(Q) at the same (token, column)
+              y[0] = (qr[0] & 0xffffu) ? y[0] : 0.f;
+              y[1] = (qr[0] >> 16) ? y[1] : 0.f;
+              y[2] = (qr[1] & 0xffffu) ? y[2] : 0.f;
+              y[3] = (qr[1] >> 16) ? y[3] : 0.f;
+              *(u32x2*)(ot + oo) = u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+            }
+          }
+        });
+      }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < SPW; ++i) {
+        const int p = W + NW * i;
+        if (p < NLD) {
+          const int u = 64 * p + l;
+          const u32x4 yv = *(const u32x4*)(ot + (u / UPR) * RS + 8 * (u % UPR));
+          __builtin_amdgcn_raw_buffer_store_b128(yv, dqrs, unit_off(c, u), 0, kNT);
+        }
+      }
+    }
+  }
+  // C blocks in B's layout (scale 1)
+  unsigned char* cout = (unsigned char*)a.cfr + ((size_t)bh * T + t) * Sh::b_frame_bytes;
+  static_for<NMB>([&](auto ic) {
+    constexpr int i = decltype(ic)::value, b = B0 + i;
+    const f32x4 x = acc[i];
+    *(u32x2*)(cout + (size_t)b * 512 + l * 8) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+  });
+}
+
+template <int D>
+__global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_cdq_kernel(CdqArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int fh = blockIdx.x;   // over BH * T
+  const int bh = fh / a.T, t = fh % a.T;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  static_for<GramShape<D>::NW>([&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    if (w == W) cdq_wave<D, W>(a, smem, bh, t);
+  });
+}
+
+// ----------------------------------------------------------------------------
 // Adjoint state pass (backward).  Write Lambda_t for dL/dM_t, the gradient of
 // the loss with respect to the post-update state of frame t through
 // everything after it.  The forward update M_t = g M_{t-1} - b g G_t M_{t-1} +
@@ -899,17 +1073,18 @@ static hipError_t launch_state_t(const StateArgs& sa, hipStream_t stream) {
 }
 
 template <int D>
-static hipError_t launch_gram_cross_t(const GramArgs& ga, hipStream_t stream) {
-  constexpr int NW = GramShape<D>::NW;
+static hipError_t launch_cdq_t(const CdqArgs& ca, hipStream_t stream) {
   static bool attr_set = false;
+  const size_t lds = 5 * GramShape<D>::tile_bytes;   // Q, dO x 2 buffers; dQ tile
+  static_assert((size_t)D * D * 2 <= 4 * GramShape<D>::tile_bytes, "snapshot staged in the tiles' space");
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, false, NW, true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
+    hipError_t e = hipFuncSetAttribute((const void*)gdn_cdq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gdn_gram_kernel<D, false, NW, true>), dim3((unsigned)(ga.BH * ga.Tc)), dim3(NW * 64),
-                     GramShape<D>::lds_bytes, stream, ga);
+  hipLaunchKernelGGL((gdn_cdq_kernel<D>), dim3((unsigned)(ca.BH * ca.T)), dim3(GramShape<D>::NW * 64), lds, stream,
+                     ca);
   return hipGetLastError();
 }
 
@@ -955,11 +1130,11 @@ hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream) {
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream) {
   GDN_DISPATCH(launch_state_t, (sa, stream))
 }
-hipError_t launch_gram_cross(int D, const GramArgs& ga, hipStream_t stream) {
-  GDN_DISPATCH(launch_gram_cross_t, (ga, stream))
-}
 hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream) {
   GDN_DISPATCH(launch_adjoint_t, (aa, stream))
+}
+hipError_t launch_cdq(int D, const CdqArgs& ca, hipStream_t stream) {
+  GDN_DISPATCH(launch_cdq_t, (ca, stream))
 }
 #undef GDN_DISPATCH
 

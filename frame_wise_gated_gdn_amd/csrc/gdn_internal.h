@@ -37,11 +37,30 @@ struct ReadoutArgs {
   int BH, T, S, t0, Tc;
   int Fs, f0;               // snapshots (and norm partials) hold [BH][Fs] frames from f0
   int fp8;                  // 1: Q and O are OCP e4m3 bytes (bf16 snapshots only)
-  // gradient products of the backward (see ReadoutMode in gdn_kernels.hip):
-  const void* mask;         // [BH][T][S][D] bf16: output zeroed where mask <= 0
-  const float* s1;          // [BH][T] per-frame output scale factor or nullptr
-  const float* s2;          // [BH][T] second per-frame factor or nullptr
-  float scale;              // constant output scale
+};
+
+// C_t = ReLU(Q_t)^T dO_t and dQ_t of the backward in one pass over Q_t and dO_t.
+struct CdqArgs {
+  const void* q;            // [BH][T][S][D] bf16
+  const void* dout;         // [BH][T][S][D] bf16
+  const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1] (slot t+1 holds M_t)
+  void* cfr;                // out: C_t in B's layout, [BH][T]
+  void* dq;                 // out: [BH][T][S][D] bf16 or nullptr
+  int BH, T, S;
+};
+
+// dV_t and dK_t of the backward in one pass over K_t and V_t.
+struct DvkArgs {
+  const void* k;            // [BH][T][S][D] bf16
+  const void* v;            // [BH][T][S][D] bf16
+  const void* lsnap;        // bf16 snapshots of Lambda_t: [BH][T]
+  const void* zsnap;        // bf16 snapshots of Z_t: [BH][T]
+  const float* gamma;       // [BH][T]
+  const float* beta;        // [BH][T]
+  void* dv;                 // [BH][T][S][D] bf16 or nullptr
+  void* dk;                 // [BH][T][S][D] bf16 or nullptr
+  int BH, T, S, beta_mode;
+  float kscale;             // 1/sqrt(D*S)
 };
 
 // Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame) (backward).
@@ -100,17 +119,13 @@ hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream);
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream);
 hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream);
 hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream);
+hipError_t launch_dvdk(int D, const DvkArgs& da, hipStream_t stream);
+hipError_t launch_cdq(int D, const CdqArgs& ca, hipStream_t stream);
 hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
                                  hipStream_t stream);
 hipError_t launch_adjoint_reduce(const float* part, const float* gamma, const float* beta, float* dgamma,
                                  float* dbeta, int BH, int T, int D, int beta_mode, hipStream_t stream);
-// Gradient products: O = scale * X W (optionally W^T, ReLU on X, += existing O,
-// masked), X streamed like Q in the readout, W from block snapshots.
-enum ReadoutKind { kReadDQ = 1, kReadDV = 2, kReadDK1 = 3, kReadDK2 = 4 };
-hipError_t launch_grad_product(int D, int kind, const ReadoutArgs& ro, hipStream_t stream);
-// C_t = ReLU(Q_t)^T dO_t per (head, frame), in B's layout (the gram pass's
-// cross blocks with scale 1): ga.k = q, ga.v = dO, ga.bfr = C array.
-hipError_t launch_gram_cross(int D, const GramArgs& ga, hipStream_t stream);
+
 
 // Workspace bytes per (head, frame) of the Gram pass outputs.
 size_t gram_frame_bytes(int D);

@@ -567,43 +567,10 @@ struct ReadShape {
   static constexpr size_t lds_bytes(int waves) { return (size_t)waves * 2 * tile_bytes; }
 };
 
-// What the kernel computes.  The forward readout is O_t = ReLU(Q_t) M_t.  The
-// backward's gradient products use the same frame-streaming structure with
-// X in Q's place and a snapshot W in M_t's: O = scale * X W (or X W^T), with
-// optional ReLU on X, accumulation into the existing O and a mask that zeroes
-// O where a given tensor is <= 0.
-template <bool RELU_, bool TRANS_, bool SCALE_, bool ACCUM_, bool MASK_>
-struct ReadoutMode {
-  static constexpr bool RELU = RELU_, TRANS = TRANS_, SCALE = SCALE_, ACCUM = ACCUM_, MASK = MASK_;
-};
-using ReadFwd = ReadoutMode<true, false, false, false, false>;
-using ReadDQ = ReadoutMode<false, true, false, false, true>;    // dO M_t^T, masked by Q > 0
-using ReadDV = ReadoutMode<true, false, true, false, false>;    // c w ReLU(K) Lambda_t
-using ReadDK1 = ReadoutMode<false, true, true, false, false>;   // c w V Lambda_t^T
-using ReadDK2 = ReadoutMode<true, false, true, true, true>;     // + (-c^2 b g) ReLU(K) Z_t, masked by K > 0
-
-// bf16 helpers of the gradient products' store phase
-__device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = pack_bf16(bf16_lo_f32(a[i]) + bf16_lo_f32(b[i]), bf16_hi_f32(a[i]) + bf16_hi_f32(b[i]));
-  return r;
-}
-__device__ __forceinline__ u32x4 mask_bf16x8(u32x4 y, u32x4 m) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int16_t lo = (int16_t)(m[i] & 0xffffu), hi = (int16_t)(m[i] >> 16);
-    r[i] = (lo > 0 ? (y[i] & 0xffffu) : 0u) | (hi > 0 ? (y[i] & 0xffff0000u) : 0u);
-  }
-  return r;
-}
-
 // RW waves per workgroup split the frame's chunks: kReadWaves, or twice that
 // for launches with fewer frames than CUs.  Every output element is computed
 // the same way whatever RW is.
-template <int D, bool FP8, int RW, class MODE = ReadFwd>
+template <int D, bool FP8, int RW>
 __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_kernel(ReadoutArgs a) {
   using Sh = ReadShape<D>;
   using IO = IoFmt<FP8>;
@@ -649,45 +616,15 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
   // and (jb, 2kc + 1) of this lane
   const unsigned char* snap = (const unsigned char*)a.snap + sf * D * D * 2;
   u32x4 A[NB][NKC];
-  if constexpr (!MODE::TRANS) {
 #pragma unroll
-    for (int jb = 0; jb < NB; ++jb)
+  for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const u32x2 lo = *(const u32x2*)(snap + ((size_t)(jb * NB + 2 * kc) * 64 + l) * 8);
-        const u32x2 hi = (2 * kc + 1 < NB) ? *(const u32x2*)(snap + ((size_t)(jb * NB + 2 * kc + 1) * 64 + l) * 8)
-                                           : u32x2{0u, 0u};
-        A[jb][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-  } else {
-    // W^T: lane (n, g) needs W[16jb + n][32kc + 4g..+3] (and + 16): row n of
-    // snapshot block [2kc][jb] at columns 4g..4g+3, a transposed LDS read of
-    // the snapshot staged by the whole workgroup (in the tiles' space, before
-    // any tile is written)
-    for (int u = tid; u < D * D * 2 / 16; u += RW * 64)
-      *(u32x4*)(smem + (size_t)u * 16) = *(const u32x4*)(snap + (size_t)u * 16);
-    __syncthreads();
-    const uint32_t trofs = (uint32_t)(((n & 3) * 16 + 4 * g + (n >> 2)) * 8);
-#pragma unroll
-    for (int jb = 0; jb < NB; ++jb)
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const u32x2 lo = lds_tr16((const uint16_t*)(smem + (size_t)((2 * kc) * NB + jb) * 512 + trofs));
-        const u32x2 hi = (2 * kc + 1 < NB)
-                             ? lds_tr16((const uint16_t*)(smem + (size_t)((2 * kc + 1) * NB + jb) * 512 + trofs))
-                             : u32x2{0u, 0u};
-        A[jb][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-    __syncthreads();
-  }
-  float scl = 1.f;
-  if constexpr (MODE::SCALE) {
-    scl = a.scale;
-    if (a.s1) scl *= a.s1[(size_t)bh * T + t];
-    if (a.s2) scl *= a.s2[(size_t)bh * T + t];
-  }
-  const __amdgpu_buffer_rsrc_t mkrs = make_rsrc(MODE::MASK ? (const unsigned char*)a.mask + head0 : nullptr,
-                                                MODE::MASK ? head_bytes : 0u);
+    for (int kc = 0; kc < NKC; ++kc) {
+      const u32x2 lo = *(const u32x2*)(snap + ((size_t)(jb * NB + 2 * kc) * 64 + l) * 8);
+      const u32x2 hi = (2 * kc + 1 < NB) ? *(const u32x2*)(snap + ((size_t)(jb * NB + 2 * kc + 1) * 64 + l) * 8)
+                                         : u32x2{0u, 0u};
+      A[jb][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
   constexpr int RING = Sh::RING;
   raw X[RING][NLD];
 #pragma unroll
@@ -725,8 +662,7 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
           const int u = 64 * j + l;
-          const u32x4 x = IO::to_bf16(X[r][j]);
-          *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = MODE::RELU ? relu8(x) : x;
+          *(u32x4*)(qs + (u / UPR) * RS + 8 * (u % UPR)) = relu8(IO::to_bf16(X[r][j]));
         }
       }
       load_chunk(i + RING, X[r]);
@@ -748,7 +684,6 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kc = 0; kc < NKC; ++kc) acc = mfma_bf16(A[jb][kc], B[kc], acc);
-          if constexpr (MODE::SCALE) acc *= scl;
           if constexpr (FP8) {
             // one rounding, fp32 -> e4m3
             *(uint32_t*)((unsigned char*)os + (16 * half + n) * RS8 + 16 * jb + 4 * g) = f32x4_to_fp8x4(acc);
@@ -766,11 +701,8 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
           const u32x2 y = *(const u32x2*)((const unsigned char*)os + (u / UPR) * RS8 + 8 * (u % UPR));
           __builtin_amdgcn_raw_buffer_store_b64(y, ors, i < NC ? unit_off(ch, u) : kOOB, 0, kNT);
         } else {
-          u32x4 y = *(const u32x4*)(os + (u / UPR) * RS + 8 * (u % UPR));
-          const uint32_t off = i < NC ? unit_off(ch, u) : kOOB;
-          if constexpr (MODE::ACCUM) y = add_bf16x8(y, buf_load16(ors, off));
-          if constexpr (MODE::MASK) y = mask_bf16x8(y, buf_load16(mkrs, off));
-          __builtin_amdgcn_raw_buffer_store_b128(y, ors, off, 0, kNT);
+          const u32x4 y = *(const u32x4*)(os + (u / UPR) * RS + 8 * (u % UPR));
+          __builtin_amdgcn_raw_buffer_store_b128(y, ors, i < NC ? unit_off(ch, u) : kOOB, 0, kNT);
         }
       }
     }
@@ -858,46 +790,6 @@ static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
                        (size_t)D * (D + 1) * 4, stream, ro);
   }
   return hipGetLastError();
-}
-
-template <int D, class MODE>
-static hipError_t launch_grad_t(const ReadoutArgs& ro, hipStream_t stream) {
-  constexpr int RW = kReadWaves;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_readout_kernel<D, false, RW, MODE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)ReadShape<D>::lds_bytes(RW));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((gdn_readout_kernel<D, false, RW, MODE>), dim3((unsigned)(ro.BH * ro.Tc)), dim3(RW * 64),
-                     ReadShape<D>::lds_bytes(RW), stream, ro);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_grad_product_t(int kind, const ReadoutArgs& ro, hipStream_t stream) {
-  switch (kind) {
-    case kReadDQ: return launch_grad_t<D, ReadDQ>(ro, stream);
-    case kReadDV: return launch_grad_t<D, ReadDV>(ro, stream);
-    case kReadDK1: return launch_grad_t<D, ReadDK1>(ro, stream);
-    case kReadDK2: return launch_grad_t<D, ReadDK2>(ro, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_grad_product(int D, int kind, const ReadoutArgs& ro, hipStream_t stream) {
-  switch (D) {
-    case 16: return launch_grad_product_t<16>(kind, ro, stream);
-    case 32: return launch_grad_product_t<32>(kind, ro, stream);
-    case 48: return launch_grad_product_t<48>(kind, ro, stream);
-    case 64: return launch_grad_product_t<64>(kind, ro, stream);
-    case 80: return launch_grad_product_t<80>(kind, ro, stream);
-    case 96: return launch_grad_product_t<96>(kind, ro, stream);
-    case 112: return launch_grad_product_t<112>(kind, ro, stream);
-    case 128: return launch_grad_product_t<128>(kind, ro, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 #define GDN_DISPATCH2(FN, ARGS)                                                                  \

@@ -177,3 +177,66 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         binding.lib()
+
+
+# gdn_frame_backward: every case below fails the host-side checks, so the call
+# returns before it touches a device.
+BW_FIELDS = ("q", "k", "v", "gamma", "beta", "state_in", "d_out", "d_state_out",
+             "dq", "dk", "dv", "d_gamma", "d_beta", "d_state_in", "workspace")
+
+
+def bw_args(gdn, d):
+    a = dict(zip(BW_FIELDS, addrs(len(BW_FIELDS))))
+    a["workspace_bytes"] = gdn.backward_workspace_size(d)
+    return a
+
+
+def backward_status(gdn, d, a):
+    import ctypes
+    return gdn.lib().gdn_frame_backward(ctypes.byref(d), *(a[f] for f in BW_FIELDS), a["workspace_bytes"], None)
+
+
+def test_backward_workspace_size(gdn):
+    sizes = [gdn.backward_workspace_size(gdn.make_desc(1, 2, T, 64, 64, "bf16")) for T in (1, 10, 100, 1024)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes) and len(set(sizes)) == 4
+    for d in (gdn.make_desc(1, 2, 3, 16, 16, "f32"), gdn.make_desc(1, 2, 3, 16, 16, "fp8"),
+              gdn.make_desc(1, 2, 1025, 16, 16, "bf16"), gdn.make_desc(1, 2, 3, 16, 24, "bf16"),
+              gdn.make_desc(1, 2, 3, 16, 16, "bf16", flags=gdn.binding.FLAG_DIRECT),
+              gdn.make_desc(0, 2, 3, 16, 16, "bf16")):
+        assert gdn.backward_workspace_size(d) == 0
+
+
+@pytest.mark.parametrize("dt,flags,T,code", [("f32", 0, 3, 6), ("fp8", 0, 3, 6), ("bf16", "direct", 3, 6),
+                                             ("bf16", 0, 1025, 6)])
+def test_backward_unsupported(gdn, dt, flags, T, code):
+    fl = gdn.binding.FLAG_DIRECT if flags == "direct" else 0
+    d = gdn.make_desc(1, 2, T, 16, 16, dt, flags=fl)
+    a = bw_args(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16"))
+    assert backward_status(gdn, d, a) == code
+    assert gdn.lib().gdn_last_error() != b""
+
+
+@pytest.mark.parametrize("field,code", [("q", 1), ("k", 1), ("v", 1), ("d_out", 1), ("gamma", 1), ("beta", 1),
+                                        ("workspace", 8)])
+def test_backward_null_errors(gdn, field, code):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    a = bw_args(gdn, d)
+    a[field] = 0
+    assert backward_status(gdn, d, a) == code
+
+
+def test_backward_workspace_align_alias_errors(gdn):
+    d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")
+    a = bw_args(gdn, d)
+    a["workspace_bytes"] -= 1
+    assert backward_status(gdn, d, a) == 8
+    for field, off in (("dq", 8), ("d_out", 2), ("d_gamma", 2), ("d_state_out", 1), ("workspace", 64)):
+        a = bw_args(gdn, d)
+        a[field] += off
+        assert backward_status(gdn, d, a) == 4, field
+    for out, other in (("dq", "q"), ("dk", "d_out"), ("d_state_in", "state_in"), ("dv", "dk"),
+                       ("workspace", "dq")):
+        a = bw_args(gdn, d)
+        a[out] = a[other]
+        assert backward_status(gdn, d, a) == 5, out
+    assert backward_status(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16", abi_version=2), bw_args(gdn, d)) == 7
