@@ -124,3 +124,54 @@ def to_numpy_io(x: torch.Tensor):
     if x.dtype == torch.float8_e4m3fn:
         return x.view(torch.uint8).numpy()
     return x.numpy()
+
+
+# ---------------------------------------------------------------------------
+# Block-causal temporal convolution (the causal FFN of the SANA-Video talk).
+#
+# x [B, T, S, C] is one frame-major activation tensor: T latent frames of S
+# spatial tokens with C channels.  No FFN width is given on the pages; the
+# 720p-shaped workload takes C = 2240, the width 20 heads of D = 112 make, and
+# the streaming chunk of 4 frames.  Draw recipe: x and the carried cache are
+# fp32 ``randn`` rounded to the I/O dtype; the three taps w [3, C] and the bias
+# [C] are fp32 ``rand`` mapped onto +-1/sqrt(3) (the default initialisation of
+# a depthwise convolution with three taps); one generator per tensor, seeded
+# seed * 1_000_003 + 7_000_000 + tensor index (x 0, w 1, bias 2, cache 3).
+
+@dataclasses.dataclass(frozen=True)
+class TconvWorkload:
+    name: str
+    B: int
+    T: int
+    S: int
+    C: int
+    chunk: int                          # frames per block of the chunk-causal generator
+    dtype: str = "bf16"                 # I/O dtype of x, y and the cache: "bf16" or "f32"
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T * self.S
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+
+    def with_(self, **kw) -> "TconvWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+TCONV_720P = TconvWorkload("tconv-720p B1 T961 S880 C2240 chunk4", 1, 961, 880, 2240, 4)
+TCONV_SMALL = TconvWorkload("tconv-small B2 T13 S40 C64 chunk4", 2, 13, 40, 64, 4)
+
+
+def generate_tconv(w: TconvWorkload, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """x [B, T, S, C] and cache [B, S, C] in the I/O dtype; w [3, C] and bias [C] fp32."""
+    base = seed * 1_000_003 + 7_000_000
+    x = torch.randn((w.B, w.T, w.S, w.C), generator=_gen(device, base, 0), device=device,
+                    dtype=torch.float32).to(w.torch_dtype)
+    bound = 3.0 ** -0.5
+    taps = torch.rand((3, w.C), generator=_gen(device, base, 1), device=device, dtype=torch.float32)
+    bias = torch.rand((w.C,), generator=_gen(device, base, 2), device=device, dtype=torch.float32)
+    cache = torch.randn((w.B, w.S, w.C), generator=_gen(device, base, 3), device=device,
+                        dtype=torch.float32).to(w.torch_dtype)
+    return {"x": x, "w": taps * (2 * bound) - bound, "bias": bias * (2 * bound) - bound, "cache": cache}
