@@ -11,7 +11,11 @@ frames per gdn_frame_step call, its per-chunk latency and back-to-back rate.
 A `variants` field times the same 720p-shaped step with OCP E4M3 Q, K, V, O
 (the low-precision I/O variant, 4*D bytes per token-head), and a `backward`
 field times gdn_frame_backward on the bf16 inputs (14*D algorithmic bytes per
-token-head); the headline `value` stays the bf16 forward step.
+token-head).  A `temporal_conv` field times gdn_tconv_forward, the block-causal
+temporal convolution of the streaming FFN, on a 720p-shaped activation
+(B1 T961 S880 C2240, blocks of 4 frames, bf16: 4*C algorithmic bytes per
+token), plus one block's call latency.  The headline `value` stays the bf16
+forward step.
 
 The default bf16 path is the Gram pipeline (gram pass, serial state pass,
 readout); --path direct times the single-pass recurrence instead.
@@ -195,6 +199,58 @@ def backward_variant(gdn, wl, torch, dev, inp, steps: int, warmup: int):
                               "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes}}
 
 
+def tconv_variant(gdn, wl, torch, dev, steps: int, warmup: int, block_reps: int = 50):
+    """gdn_tconv_forward over the whole 720p-shaped activation in one call, and one
+    block of `chunk` frames per call (the streaming use) with the cache handed on."""
+    w = wl.TCONV_720P
+    inp = wl.generate_tconv(w, device=dev)
+    y = torch.empty_like(inp["x"])
+    cache_out = torch.empty_like(inp["cache"])
+    call = lambda timed: gdn.tconv_forward(inp["x"], inp["w"], inp["bias"], w.chunk, inp["cache"], out=y,
+                                           cache_out=cache_out, time_kernels=timed)
+    for _ in range(warmup):
+        call(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call(False)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gdn.kernel_times(reset=True)
+    for _ in range(steps):
+        call(True)
+    torch.cuda.synchronize()
+    kms = gdn.kernel_times(reset=True)["tconv"][0] / steps
+    alg = w.B * w.T * w.S * w.C * 2 * 2
+    gbs = alg / (kms * 1e-3) / 1e9
+    # one block per call, cache updated in place
+    xb = inp["x"][:, :w.chunk].contiguous()
+    yb = torch.empty_like(xb)
+    cache = inp["cache"].clone()
+    blk = lambda: gdn.tconv_forward(xb, inp["w"], inp["bias"], w.chunk, cache, out=yb, cache_out="inplace")
+    for _ in range(5):
+        blk()
+    torch.cuda.synchronize()
+    lat = []
+    for _ in range(block_reps):
+        t1 = time.perf_counter()
+        blk()
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t1) * 1e6)
+    t1 = time.perf_counter()
+    for _ in range(block_reps):
+        blk()
+    torch.cuda.synchronize()
+    b2b = (time.perf_counter() - t1) * 1e6 / block_reps
+    lat.sort()
+    return {"workload": w.name, "value": w.tokens / (ms * 1e-3), "unit": "tokens/s (B*T*S)", "ms_per_step": ms,
+            "kernel_ms": kms,
+            "roofline": {"bound": "hbm", "kernel": "tconv", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": alg},
+            "block_call": {"frames": w.chunk, "latency_us_median": lat[len(lat) // 2],
+                           "back_to_back_us": b2b}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +259,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=12, help="oracle heads timed for cpu_baseline (0 = skip)")
     ap.add_argument("--no-backward", dest="backward", action="store_false",
                     help="skip the timing of gdn_frame_backward on the same inputs")
+    ap.add_argument("--no-tconv", dest="tconv", action="store_false",
+                    help="skip the timing of the block-causal temporal convolution")
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the E4M3 I/O variant of the step")
     ap.add_argument("--stream-reps", type=int, default=5,
@@ -307,6 +365,8 @@ def main():
         rec["streaming"] = streaming_latency(gdn, wl, torch, dev, args.stream_reps)
     if args.backward and args.path == "auto":
         rec["backward"] = backward_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
+    if args.tconv:
+        rec["temporal_conv"] = tconv_variant(gdn, wl, torch, dev, args.steps, args.warmup)
     if args.fp8 and args.path == "auto":
         rec["variants"] = {"fp8_e4m3_io": fp8_variant(gdn, wl, torch, dev, args.steps, args.warmup)}
     if args.cpu_heads > 0:

@@ -1,4 +1,5 @@
-"""MI355X-native frame-wise Gated DeltaNet (SANA-WM) forward path.
+"""MI355X-native frame-wise Gated DeltaNet (SANA-WM): forward, streaming step,
+backward, and the block-causal temporal convolution of the streaming FFN.
 
 The recurrence runs in hand-written gfx950 HIP kernels behind the C ABI of
 ``libgdn.so`` (include/gdn.h); this package holds that library's sources, the
@@ -7,7 +8,9 @@ device memory and streams.
 """
 from .binding import (ABI_VERSION, BF16, ERASE, F32, FP8, WRITE, Desc, GDNError, check_args,  # noqa: F401
                       backward_workspace_size, frame_backward, frame_forward, frame_step, kernel_times, lib,
-                      make_desc, workspace_min_size, workspace_size)
+                      make_desc, make_tconv_desc, tconv_check_args, tconv_forward, workspace_min_size,
+                      workspace_size)
 
-__all__ = ["frame_forward", "frame_step", "frame_backward", "backward_workspace_size", "GDNError", "workspace_size", "workspace_min_size",
-           "kernel_times", "check_args", "make_desc", "lib"]
+__all__ = ["frame_forward", "frame_step", "frame_backward", "backward_workspace_size", "tconv_forward",
+           "GDNError", "workspace_size", "workspace_min_size", "kernel_times", "check_args", "tconv_check_args",
+           "make_desc", "make_tconv_desc", "lib"]

@@ -19,14 +19,15 @@ ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
 FLAG_DIRECT = 0x2
 # kernel kinds of gdn_kernel_times, in slot order
-KERNELS = ("recurrence", "readout", "gram", "state", "backward")
+KERNELS = ("recurrence", "readout", "gram", "state", "backward", "tconv")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_ABI", 8: "GDN_ERR_WORKSPACE",
           9: "GDN_ERR_HIP"}
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
            "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
-           "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward")
+           "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward", "gdn_tconv_forward",
+           "gdn_tconv_check_args")
 
 
 class GDNError(RuntimeError):
@@ -40,6 +41,12 @@ class Desc(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("T", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("beta_mode", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class TconvDesc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("C", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 _lib = None
@@ -74,6 +81,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_backward_workspace_size.argtypes = [pdesc]
     L.gdn_frame_backward.restype = ctypes.c_int
     L.gdn_frame_backward.argtypes = [pdesc] + [vp] * 15 + [sz, vp]
+    ptd = ctypes.POINTER(TconvDesc)
+    L.gdn_tconv_forward.restype = ctypes.c_int
+    L.gdn_tconv_forward.argtypes = [ptd, vp, vp, vp, vp, vp, vp, vp]
+    L.gdn_tconv_check_args.restype = ctypes.c_int
+    L.gdn_tconv_check_args.argtypes = [ptd, vp, vp, vp, vp, vp, vp]
     L.gdn_kernel_times.restype = ctypes.c_int
     L.gdn_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     if L.gdn_abi_version() != ABI_VERSION:
@@ -253,3 +265,48 @@ def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, be
                                   ctypes.c_void_p(stream))
     _raise(st)
     return {k_: v_ for k_, v_ in out.items() if v_ is not None}
+
+
+def make_tconv_desc(B, T, S, C, chunk, io_dtype, flags=0, abi_version=ABI_VERSION) -> TconvDesc:
+    dt = {"bf16": BF16, "f32": F32, "fp8": FP8}.get(io_dtype, io_dtype)
+    return TconvDesc(abi_version, B, T, S, C, chunk, dt, flags)
+
+
+def tconv_check_args(desc: TconvDesc, x=0, w=0, bias=0, cache_in=0, y=0, cache_out=0) -> int:
+    """Host-only argument check of gdn_tconv_forward on raw addresses."""
+    p = lambda a: ctypes.c_void_p(a or None)
+    return int(lib().gdn_tconv_check_args(ctypes.byref(desc), p(x), p(w), p(bias), p(cache_in), p(y),
+                                          p(cache_out)))
+
+
+def tconv_forward(x, w, bias=None, chunk: int = 1, cache=None, out=None, cache_out=None, stream=None,
+                  time_kernels=False):
+    """Block-causal temporal convolution: x [B, T, S, C] (bf16 or fp32), w [3, C]
+    and bias [C] fp32, cache [B, S, C] (the previous call's last frame) or None.
+    cache_out: None (not written), a tensor [B, S, C], or "inplace" (written
+    into `cache`).  Returns (y, cache_out)."""
+    import torch
+    B, T, S, C = x.shape
+    dt = {torch.bfloat16: BF16, torch.float32: F32}.get(x.dtype)
+    if dt is None:
+        raise TypeError(f"x must be bf16 or fp32, not {x.dtype}")
+    if w.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise TypeError("w and bias must be fp32")
+    for t in (x, w, bias, cache, out):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if cache is not None and cache.dtype != x.dtype:
+        raise TypeError("cache must have the dtype of x")
+    if isinstance(cache_out, str):
+        if cache_out != "inplace" or cache is None:
+            raise ValueError('cache_out="inplace" needs a cache')
+        cache_out = cache
+    if out is None:
+        out = torch.empty_like(x)
+    desc = make_tconv_desc(B, T, S, C, chunk, dt, FLAG_TIME_KERNELS if time_kernels else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib().gdn_tconv_forward(ctypes.byref(desc), _addr(x), _addr(w), _addr(bias), _addr(cache), _addr(out),
+                                 _addr(cache_out), ctypes.c_void_p(stream))
+    _raise(st)
+    return out, cache_out

@@ -449,6 +449,40 @@ gdn_status check_backward(const gdn_desc* d, const void* q, const void* k, const
   return GDN_OK;
 }
 
+gdn_status check_tconv(const gdn_tconv_desc* d, const void* x, const float* w, const float* bias,
+                       const void* cache_in, const void* y, const void* cache_out) {
+  g_last_error.clear();
+  if (!d) return fail(GDN_ERR_NULL, "desc is NULL");
+  if (d->abi_version != GDN_ABI_VERSION)
+    return fail(GDN_ERR_ABI, "desc.abi_version %d != library ABI %d", d->abi_version, GDN_ABI_VERSION);
+  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16)
+    return fail(GDN_ERR_DTYPE, "io_dtype %d: the temporal convolution takes GDN_BF16 or GDN_F32", d->io_dtype);
+  if (d->flags & ~GDN_FLAG_TIME_KERNELS) return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->B < 1 || d->T < 1 || d->S < 1 || d->C < 1 || d->chunk < 1)
+    return fail(GDN_ERR_SHAPE, "B=%d T=%d S=%d C=%d chunk=%d: every size must be >= 1", d->B, d->T, d->S, d->C,
+                d->chunk);
+  if (d->C % 8 != 0) return fail(GDN_ERR_UNSUPPORTED, "C=%d: channels must be a multiple of 8", d->C);
+  if (d->B > 65535) return fail(GDN_ERR_SHAPE, "B=%d: at most 65535", d->B);
+  const long double elems = (long double)d->B * d->T * d->S * d->C;
+  if (elems * 4 >= (long double)SIZE_MAX / 4 || (long double)d->S * d->C >= 2147483648.0L * 4)
+    return fail(GDN_ERR_SHAPE, "tensor sizes overflow");
+  if (!x || !w || !y) return fail(GDN_ERR_NULL, "x, w and y are required");
+  if (misaligned(x, 16) || misaligned(y, 16) || misaligned(cache_in, 16) || misaligned(cache_out, 16))
+    return fail(GDN_ERR_ALIGN, "x, y and the caches must be 16-byte aligned");
+  if (misaligned(w, 4) || misaligned(bias, 4)) return fail(GDN_ERR_ALIGN, "w and bias must be 4-byte aligned");
+  const size_t esz = d->io_dtype == GDN_F32 ? 4 : 2;
+  const size_t xb = (size_t)d->B * d->T * d->S * d->C * esz, cb = (size_t)d->B * d->S * d->C * esz;
+  const size_t wb = (size_t)3 * d->C * 4, bb = (size_t)d->C * 4;
+  if (overlap(y, xb, x, xb) || overlap(y, xb, w, wb) || overlap(y, xb, bias, bb) || overlap(y, xb, cache_in, cb))
+    return fail(GDN_ERR_ALIAS, "y overlaps an input");
+  if (overlap(cache_out, cb, x, xb) || overlap(cache_out, cb, y, xb) || overlap(cache_out, cb, w, wb) ||
+      overlap(cache_out, cb, bias, bb))
+    return fail(GDN_ERR_ALIAS, "cache_out overlaps x, y, w or bias");
+  if (cache_out && cache_in && cache_out != cache_in && overlap(cache_out, cb, cache_in, cb))
+    return fail(GDN_ERR_ALIAS, "cache_out partially overlaps cache_in");
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -638,6 +672,25 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
     e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,
                                    d->beta_mode, s);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+gdn_status gdn_tconv_check_args(const gdn_tconv_desc* d, const void* x, const float* w, const float* bias,
+                                const void* cache_in, const void* y, const void* cache_out) {
+  return check_tconv(d, x, w, bias, cache_in, y, cache_out);
+}
+
+gdn_status gdn_tconv_forward(const gdn_tconv_desc* d, const void* x, const float* w, const float* bias,
+                             const void* cache_in, void* y, void* cache_out, void* stream) {
+  const gdn_status st = check_tconv(d, x, w, bias, cache_in, y, cache_out);
+  if (st != GDN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  gdn::TconvArgs ta;
+  ta.x = x; ta.w = w; ta.bias = bias; ta.cache_in = cache_in; ta.y = y; ta.cache_out = cache_out;
+  ta.B = d->B; ta.T = d->T; ta.S = d->S; ta.C = d->C; ta.chunk = d->chunk; ta.f32 = d->io_dtype == GDN_F32;
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const hipError_t e = launch_timed(timed, GDN_KERNEL_TCONV, s, [&] { return gdn::launch_tconv(ta, s); });
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "temporal convolution launch: %s", hipGetErrorString(e));
   return GDN_OK;
 }
 

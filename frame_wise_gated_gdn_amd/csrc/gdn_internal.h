@@ -63,6 +63,20 @@ struct DvkArgs {
   float kscale;             // 1/sqrt(D*S)
 };
 
+// Block-causal temporal convolution (gdn_tconv.hip).
+struct TconvArgs {
+  const void* x;            // [B][T][S][C] bf16 or fp32
+  const float* w;           // [3][C]: taps of the previous, current, next frame
+  const float* bias;        // [C] or nullptr
+  const void* cache_in;     // [B][S][C] or nullptr (zeros)
+  void* y;                  // [B][T][S][C]
+  void* cache_out;          // [B][S][C] or nullptr
+  int B, T, S, C, chunk, f32;
+  // set by launch_tconv
+  int cols_per_token, seg_frames;
+  long long cols;
+};
+
 // Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame) (backward).
 struct ZmatArgs {
   const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
@@ -120,6 +134,7 @@ hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream);
 hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream);
 hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream);
 hipError_t launch_dvdk(int D, const DvkArgs& da, hipStream_t stream);
+hipError_t launch_tconv(const TconvArgs& ta, hipStream_t stream);
 hipError_t launch_cdq(int D, const CdqArgs& ca, hipStream_t stream);
 hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
                                  hipStream_t stream);

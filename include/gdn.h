@@ -105,7 +105,8 @@ typedef enum gdn_status {
 #define GDN_KERNEL_GRAM 2       /* Gram pass: G_t, B_t per (head, frame) */
 #define GDN_KERNEL_STATE 3      /* serial state pass over G_t, B_t */
 #define GDN_KERNEL_BACKWARD 4   /* the backward's own kernels (its forward replay books as GRAM/STATE) */
-#define GDN_KERNEL_SLOTS 5
+#define GDN_KERNEL_TCONV 5      /* block-causal temporal convolution */
+#define GDN_KERNEL_SLOTS 6
 
 typedef struct gdn_desc {
   int32_t abi_version; /* GDN_ABI_VERSION */
@@ -199,6 +200,51 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
                               const void* d_out, const float* d_state_out,
                               void* dq, void* dk, void* dv, float* d_gamma, float* d_beta, float* d_state_in,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-causal temporal convolution with a carried-token cache: the causal
+ * FFN's temporal convolution in the talk "SANA-Video: Efficient Video
+ * Generation with Block Linear Diffusion Transformer" (its closing part, the
+ * two-block example: a zero token between blocks, the previous block's last
+ * token carried in before the next block).  Depthwise, three taps along the
+ * frame axis, at every spatial token and channel; for frame t of the call:
+ *
+ *   y[t]    = w[0]*left_t + w[1]*x[t] + w[2]*right_t + bias
+ *   left_t  = x[t-1]; for t = 0 the cache (the previous call's last frame),
+ *             zeros if cache_in is NULL
+ *   right_t = x[t+1] when t+1 < T and t+1 starts no new block of `chunk`
+ *             frames (blocks counted from the call's first frame), else zero
+ *
+ * chunk >= T is the two-sided convolution with zero padding (offline
+ * generation); chunk = 1 is strictly causal.  Computed in fp32 with fused
+ * multiply-adds in the order bias, left, current, right; y rounded to nearest
+ * even.  cache_out (if not NULL) receives x[T-1], the carried token for the
+ * next call: calls of one block each, the cache handed from one to the next,
+ * give bitwise the y of one call over all frames.
+ *
+ * Layouts (device pointers): x, y [B][T][S][C] io_dtype (GDN_BF16 or GDN_F32);
+ * w [3][C] fp32 (taps of the previous, current, next frame); bias [C] fp32 or
+ * NULL; cache_in, cache_out [B][S][C] io_dtype or NULL.  C must be a multiple
+ * of 8; x, y and the caches 16-byte aligned, w and bias 4-byte aligned.  y may
+ * not overlap an input; cache_out may equal cache_in exactly (in-place cache
+ * update) but not overlap it partially, nor overlap x, y, w or bias.  flags:
+ * GDN_FLAG_TIME_KERNELS only.  Same stream and error conventions as the
+ * calls above.
+ */
+typedef struct gdn_tconv_desc {
+  int32_t abi_version; /* GDN_ABI_VERSION */
+  int32_t B, T, S, C;
+  int32_t chunk;       /* frames per block, >= 1 */
+  int32_t io_dtype;    /* GDN_BF16 or GDN_F32 */
+  uint32_t flags;
+} gdn_tconv_desc;
+
+gdn_status gdn_tconv_forward(const gdn_tconv_desc* d, const void* x, const float* w, const float* bias,
+                             const void* cache_in, void* y, void* cache_out, void* stream);
+
+/* Host-only argument check of gdn_tconv_forward (no device is touched). */
+gdn_status gdn_tconv_check_args(const gdn_tconv_desc* d, const void* x, const float* w, const float* bias,
+                                const void* cache_in, const void* y, const void* cache_out);
 
 /*
  * Device time of the kernels launched by calls that set GDN_FLAG_TIME_KERNELS

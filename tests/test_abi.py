@@ -240,3 +240,59 @@ def test_backward_workspace_align_alias_errors(gdn):
         a[out] = a[other]
         assert backward_status(gdn, d, a) == 5, out
     assert backward_status(gdn, gdn.make_desc(1, 2, 3, 16, 16, "bf16", abi_version=2), bw_args(gdn, d)) == 7
+
+
+# gdn_tconv_check_args / gdn_tconv_forward: host-side checks only.
+TC_FIELDS = ("x", "w", "bias", "cache_in", "y", "cache_out")
+
+
+def tc_args():
+    return dict(zip(TC_FIELDS, addrs(len(TC_FIELDS))))
+
+
+def test_tconv_valid_arguments(gdn):
+    for dt in ("bf16", "f32"):
+        for C, chunk in ((8, 1), (2240, 4), (64, 1000)):
+            d = gdn.make_tconv_desc(2, 5, 17, C, chunk, dt)
+            assert gdn.tconv_check_args(d, **tc_args()) == 0, gdn.lib().gdn_last_error()
+    a = tc_args()
+    a["cache_out"] = a["cache_in"]                # exact in-place cache update is allowed
+    assert gdn.tconv_check_args(gdn.make_tconv_desc(1, 4, 8, 16, 4, "bf16"), **a) == 0
+    a = tc_args()
+    a["bias"] = a["cache_in"] = a["cache_out"] = 0
+    assert gdn.tconv_check_args(gdn.make_tconv_desc(1, 4, 8, 16, 4, "bf16"), **a) == 0
+
+
+@pytest.mark.parametrize("shape,dt,code", [((0, 4, 8, 16, 4), "bf16", 2), ((1, 0, 8, 16, 4), "bf16", 2),
+                                           ((1, 4, 0, 16, 4), "bf16", 2), ((1, 4, 8, 0, 4), "bf16", 2),
+                                           ((1, 4, 8, 16, 0), "bf16", 2), ((1, 4, 8, 12, 4), "bf16", 6),
+                                           ((1, 4, 8, 4, 4), "f32", 6), ((1, 4, 8, 16, 4), "fp8", 3),
+                                           ((1, 4, 8, 16, 4), 7, 3), ((70000, 4, 8, 16, 4), "bf16", 2)])
+def test_tconv_shape_and_dtype_errors(gdn, shape, dt, code):
+    assert gdn.tconv_check_args(gdn.make_tconv_desc(*shape, dt), **tc_args()) == code
+
+
+def test_tconv_flag_abi_null_align_alias_errors(gdn):
+    d = gdn.make_tconv_desc(1, 4, 8, 16, 4, "bf16")
+    assert gdn.tconv_check_args(gdn.make_tconv_desc(1, 4, 8, 16, 4, "bf16", flags=gdn.binding.FLAG_DIRECT),
+                                **tc_args()) == 6
+    assert gdn.tconv_check_args(gdn.make_tconv_desc(1, 4, 8, 16, 4, "bf16", abi_version=2), **tc_args()) == 7
+    for f in ("x", "w", "y"):
+        a = tc_args()
+        a[f] = 0
+        assert gdn.tconv_check_args(d, **a) == 1, f
+    for f, off in (("x", 8), ("y", 2), ("cache_in", 4), ("cache_out", 8), ("w", 2), ("bias", 1)):
+        a = tc_args()
+        a[f] += off
+        assert gdn.tconv_check_args(d, **a) == 4, f
+    for f, other in (("y", "x"), ("y", "w"), ("y", "cache_in"), ("cache_out", "x"), ("cache_out", "y"),
+                     ("cache_out", "bias")):
+        a = tc_args()
+        a[f] = a[other]
+        assert gdn.tconv_check_args(d, **a) == 5, (f, other)
+    a = tc_args()
+    a["cache_out"] = a["cache_in"] + 16           # partial overlap of the caches
+    assert gdn.tconv_check_args(d, **a) == 5
+    import ctypes
+    assert gdn.lib().gdn_tconv_forward(ctypes.byref(d), *([None] * 6), None) == 1
+    assert gdn.lib().gdn_tconv_check_args(None, *([None] * 6)) == 1
