@@ -175,3 +175,47 @@ def generate_tconv(w: TconvWorkload, device="cpu", seed: int = 0) -> Dict[str, t
     cache = torch.randn((w.B, w.S, w.C), generator=_gen(device, base, 3), device=device,
                         dtype=torch.float32).to(w.torch_dtype)
     return {"x": x, "w": taps * (2 * bound) - bound, "bias": bias * (2 * bound) - bound, "cache": cache}
+
+
+# ---------------------------------------------------------------------------
+# Block-causal softmax attention (the hybrid's periodic softmax blocks).
+#
+# q [B, H, Tq, S, D], k and v [B, H, Tk, S, D], frame-major like the GDN
+# tensors; the queries are the last Tq frames.  Heads and head dim follow the
+# 720p-shaped GDN workload (H20, D112, S880); a whole-sequence softmax block
+# over all 961 frames is the all-softmax case the pages report running out of
+# memory, so the measured clip is 81 frames (the short-clip length) with the
+# chunk-causal generator's blocks of 4 frames.  Draw recipe: fp32 ``randn``
+# rounded to bf16, one generator per tensor, seeded
+# seed * 1_000_003 + 8_000_000 + tensor index (q 0, k 1, v 2).
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    Tq: int
+    Tk: int
+    S: int
+    D: int
+    chunk: int
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.Tq * self.S
+
+    def with_(self, **kw) -> "AttnWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+ATTN_CLIP_720P = AttnWorkload("attn-720p-clip B1 H20 T81 S880 D112 chunk4", 1, 20, 81, 81, 880, 112, 4)
+ATTN_STREAM_720P = AttnWorkload("attn-720p-stream B1 H20 Tq4 Tk81 S880 D112 chunk4", 1, 20, 4, 81, 880, 112, 4)
+
+
+def generate_attn(w: AttnWorkload, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """q [B, H, Tq, S, D], k and v [B, H, Tk, S, D], bf16."""
+    base = seed * 1_000_003 + 8_000_000
+    shapes = {"q": (w.B, w.H, w.Tq, w.S, w.D), "k": (w.B, w.H, w.Tk, w.S, w.D), "v": (w.B, w.H, w.Tk, w.S, w.D)}
+    return {name: torch.randn(shape, generator=_gen(device, base, i), device=device,
+                              dtype=torch.float32).to(torch.bfloat16)
+            for i, (name, shape) in enumerate(shapes.items())}
