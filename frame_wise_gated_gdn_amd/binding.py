@@ -19,7 +19,7 @@ ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
 FLAG_DIRECT = 0x2
 # kernel kinds of gdn_kernel_times, in slot order
-KERNELS = ("recurrence", "readout", "gram", "state", "backward", "tconv")
+KERNELS = ("recurrence", "readout", "gram", "state", "backward", "tconv", "attention")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_ABI", 8: "GDN_ERR_WORKSPACE",
           9: "GDN_ERR_HIP"}
@@ -27,7 +27,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE"
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
            "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
            "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward", "gdn_tconv_forward",
-           "gdn_tconv_check_args")
+           "gdn_tconv_check_args", "gdn_attention_forward", "gdn_attention_check_args")
 
 
 class GDNError(RuntimeError):
@@ -47,6 +47,13 @@ class TconvDesc(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("S", ctypes.c_int32), ("C", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Tq", ctypes.c_int32), ("Tk", ctypes.c_int32), ("S", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("scale", ctypes.c_float)]
 
 
 _lib = None
@@ -86,6 +93,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_tconv_forward.argtypes = [ptd, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_tconv_check_args.restype = ctypes.c_int
     L.gdn_tconv_check_args.argtypes = [ptd, vp, vp, vp, vp, vp, vp]
+    pad = ctypes.POINTER(AttnDesc)
+    L.gdn_attention_forward.restype = ctypes.c_int
+    L.gdn_attention_forward.argtypes = [pad, vp, vp, vp, vp, vp]
+    L.gdn_attention_check_args.restype = ctypes.c_int
+    L.gdn_attention_check_args.argtypes = [pad, vp, vp, vp, vp]
     L.gdn_kernel_times.restype = ctypes.c_int
     L.gdn_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     if L.gdn_abi_version() != ABI_VERSION:
@@ -310,3 +322,38 @@ def tconv_forward(x, w, bias=None, chunk: int = 1, cache=None, out=None, cache_o
                                  _addr(cache_out), ctypes.c_void_p(stream))
     _raise(st)
     return out, cache_out
+
+
+def make_attn_desc(B, H, Tq, Tk, S, D, chunk, io_dtype="bf16", flags=0, scale=0.0,
+                   abi_version=ABI_VERSION) -> AttnDesc:
+    dt = {"bf16": BF16, "f32": F32, "fp8": FP8}.get(io_dtype, io_dtype)
+    return AttnDesc(abi_version, B, H, Tq, Tk, S, D, chunk, dt, flags, scale)
+
+
+def attention_check_args(desc: AttnDesc, q=0, k=0, v=0, o=0) -> int:
+    """Host-only argument check of gdn_attention_forward on raw addresses."""
+    p = lambda a: ctypes.c_void_p(a or None)
+    return int(lib().gdn_attention_check_args(ctypes.byref(desc), p(q), p(k), p(v), p(o)))
+
+
+def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, stream=None, time_kernels=False):
+    """Block-causal softmax attention: q [B, H, Tq, S, D], k and v [B, H, Tk, S, D]
+    (bf16; the queries are the last Tq key frames).  Returns o like q."""
+    import torch
+    if q.dim() != 5 or k.shape != v.shape or k.dim() != 5:
+        raise ValueError("q [B,H,Tq,S,D], k and v [B,H,Tk,S,D]")
+    B, H, Tq, S, D = q.shape
+    Tk = k.shape[2]
+    if k.shape[:2] != (B, H) or k.shape[3:] != (S, D):
+        raise ValueError("k and v must match q in B, H, S and D")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("q, k and v must be contiguous bf16")
+    if out is None:
+        out = torch.empty_like(q)
+    desc = make_attn_desc(B, H, Tq, Tk, S, D, chunk, BF16, FLAG_TIME_KERNELS if time_kernels else 0, scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _raise(lib().gdn_attention_forward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(out),
+                                       ctypes.c_void_p(stream)))
+    return out

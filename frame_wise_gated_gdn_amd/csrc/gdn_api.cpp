@@ -483,6 +483,33 @@ gdn_status check_tconv(const gdn_tconv_desc* d, const void* x, const float* w, c
   return GDN_OK;
 }
 
+gdn_status check_attn(const gdn_attn_desc* d, const void* q, const void* k, const void* v, const void* o) {
+  g_last_error.clear();
+  if (!d) return fail(GDN_ERR_NULL, "desc is NULL");
+  if (d->abi_version != GDN_ABI_VERSION)
+    return fail(GDN_ERR_ABI, "desc.abi_version %d != library ABI %d", d->abi_version, GDN_ABI_VERSION);
+  if (d->io_dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "io_dtype %d: the attention takes GDN_BF16", d->io_dtype);
+  if (d->flags & ~GDN_FLAG_TIME_KERNELS) return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->B < 1 || d->H < 1 || d->Tq < 1 || d->Tk < 1 || d->S < 1 || d->D < 1 || d->chunk < 1)
+    return fail(GDN_ERR_SHAPE, "B=%d H=%d Tq=%d Tk=%d S=%d D=%d chunk=%d: every size must be >= 1", d->B, d->H,
+                d->Tq, d->Tk, d->S, d->D, d->chunk);
+  if (d->Tq > d->Tk) return fail(GDN_ERR_SHAPE, "Tq=%d > Tk=%d: the queries are the last Tq key frames", d->Tq, d->Tk);
+  if (d->D % 16 != 0 || d->D > 128)
+    return fail(GDN_ERR_UNSUPPORTED, "D=%d: supported head dims are 16, 32, ..., 128", d->D);
+  if (!std::isfinite(d->scale)) return fail(GDN_ERR_SHAPE, "scale must be finite");
+  const long double nk = (long double)d->Tk * d->S, bh = (long double)d->B * d->H;
+  if (nk >= 2147483648.0L - 256 || bh * ((long double)d->Tq * d->S / 128 + 1) >= 2147483648.0L)
+    return fail(GDN_ERR_SHAPE, "too many tokens per head for 32-bit indexing");
+  if (bh * nk * d->D * 2 >= (long double)SIZE_MAX / 4) return fail(GDN_ERR_SHAPE, "tensor sizes overflow");
+  if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o are required");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  const size_t qb = (size_t)d->B * d->H * d->Tq * d->S * d->D * 2, kb = (size_t)d->B * d->H * d->Tk * d->S * d->D * 2;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
+    return fail(GDN_ERR_ALIAS, "o overlaps q, k or v");
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -672,6 +699,27 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
     e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,
                                    d->beta_mode, s);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+gdn_status gdn_attention_check_args(const gdn_attn_desc* d, const void* q, const void* k, const void* v,
+                                    const void* o) {
+  return check_attn(d, q, k, v, o);
+}
+
+gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const void* k, const void* v, void* o,
+                                 void* stream) {
+  const gdn_status st = check_attn(d, q, k, v, o);
+  if (st != GDN_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  gdn::AttnArgs aa;
+  aa.q = q; aa.k = k; aa.v = v; aa.o = o;
+  aa.BH = d->B * d->H; aa.Tq = d->Tq; aa.Tk = d->Tk; aa.S = d->S; aa.chunk = d->chunk;
+  const double scale = d->scale != 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->D);
+  aa.scale_log2 = (float)(scale * 1.4426950408889634);   // log2(e)
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const hipError_t e = launch_timed(timed, GDN_KERNEL_ATTN, s, [&] { return gdn::launch_attn(d->D, aa, s); });
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return GDN_OK;
 }
 

@@ -1,0 +1,282 @@
+// Block-causal softmax attention on gfx950 (the hybrid's periodic softmax
+// blocks: SANA-WM keeps softmax attention blocks between its frame-wise GDN
+// blocks, per the GeekNews summary of SANA-WM and the SANA-WM abstract).
+//
+//   O = softmax(Q K^T * scale) V   per (batch, head), tokens frame-major;
+//   a query in frame f (of the key sequence; the queries are its last Tq
+//   frames) sees the keys of every frame up to the end of its block of
+//   `chunk` frames.
+//
+// One workgroup of four waves owns 128 consecutive queries of one head and
+// streams the visible keys and values through LDS in tiles of 64 tokens
+// (double-buffered; one barrier per tile).  Each wave owns 32 queries.
+//
+// Transposed formulation.  The wave computes S^T = K Q^T (keys as MFMA rows,
+// queries as columns) and O^T = V^T P^T, so that in every accumulator a lane
+// holds one query (column l%16) and four keys or four head-dim entries (rows
+// 4g..4g+3):
+//   * the online softmax state (running max m, running sum) is per lane, and
+//     rescaling O by exp(m_old - m_new) needs no cross-lane traffic; the max
+//     over a tile's keys takes two lane shuffles (the four lanes of a query);
+//   * P goes from the S^T accumulators straight into the B operand of the
+//     V^T P^T product (bf16), with the keys of a 32-key step taken in the
+//     order 4g..4g+3, 16+4g..16+4g+3, which is the order in which the
+//     transposing LDS read (ds_read_b64_tr_b16) hands each lane its column of
+//     V; no LDS round trip for P.
+//   * Q^T is the B operand of S^T: each lane loads its query row once, from
+//     global memory, and keeps it in registers.
+// Scores are scaled by scale*log2(e) and exponentiated with exp2.  Masked keys
+// (past the query's block, or past the key sequence) score -inf.
+//
+// MFMA lane layouts are those of gdn_device.h (16x16x32 bf16).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnQW = 32;                        // queries per wave
+constexpr int kAttnBM = kAttnWaves * kAttnQW;      // queries per workgroup
+constexpr int kAttnBN = 64;                        // keys per tile
+
+template <int D>
+struct AttnShape {
+  static constexpr int NB = D / 16;                // 16-wide head-dim blocks
+  static constexpr int NKC = (D + 31) / 32;        // 32-wide k-steps of Q K^T
+  static constexpr int NQ = kAttnQW / 16;          // query tiles per wave
+  static constexpr int NKT = kAttnBN / 16;         // 16-key tiles per key tile
+  static constexpr int NK2 = kAttnBN / 32;         // 32-key steps of V^T P^T
+  static constexpr int UPR = D / 8;                // 16-byte units per token row
+  static constexpr int UNITS = kAttnBN * UPR;      // units per K (or V) tile
+  static constexpr int LPT = (UNITS + kAttnWaves * 64 - 1) / (kAttnWaves * 64);   // units per thread
+  static constexpr int RS = D + 8;                 // LDS row stride (elements)
+  static constexpr size_t tile_bytes = (size_t)kAttnBN * RS * 2;
+  static constexpr size_t lds_bytes = 2 * 2 * tile_bytes;   // (K, V) x 2 buffers
+};
+
+__device__ __forceinline__ float wave_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+// Keys visible to a query token qi of the query sequence (last Tq frames).
+__device__ __forceinline__ int key_end(int qi, const AttnArgs& a) {
+  const int fq = (a.Tk - a.Tq) + qi / a.S;
+  return min(a.Tk, (fq / a.chunk + 1) * a.chunk) * a.S;
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void gdn_attn_kernel(AttnArgs a) {
+  using Sh = AttnShape<D>;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, NQ = Sh::NQ, NKT = Sh::NKT, NK2 = Sh::NK2;
+  constexpr int UPR = Sh::UPR, UNITS = Sh::UNITS, LPT = Sh::LPT, RS = Sh::RS;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int Nq = a.Tq * a.S, Nk = a.Tk * a.S;
+  const int nqt = (Nq + kAttnBM - 1) / kAttnBM;
+  const int bh = blockIdx.x / nqt;
+  const int qtile = nqt - 1 - (int)(blockIdx.x % nqt);     // the longest key ranges start first
+  const int q0 = qtile * kAttnBM;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
+  const uint16_t* qh = (const uint16_t*)a.q + (size_t)bh * Nq * D;
+  const uint16_t* kh = (const uint16_t*)a.k + (size_t)bh * Nk * D;
+  const uint16_t* vh = (const uint16_t*)a.v + (size_t)bh * Nk * D;
+  uint16_t* oh = (uint16_t*)a.o + (size_t)bh * Nq * D;
+
+  // the workgroup's key range: up to the block end of its last query
+  const int kend_wg = key_end(min(q0 + kAttnBM, Nq) - 1, a);
+  const int ntiles = (kend_wg + kAttnBN - 1) / kAttnBN;
+
+  // this lane's queries (one per query tile) and their key ends
+  int kend[NQ];
+  u32x4 QB[NQ][NKC];
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt) {
+    const int qi = q0 + kAttnQW * w + 16 * qt + n;
+    kend[qt] = key_end(min(qi, Nq - 1), a);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int d = 32 * kc + 8 * g;
+      QB[qt][kc] = (qi < Nq && d < D) ? *(const u32x4*)(qh + (size_t)qi * D + d) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4 O[NQ][NB];
+  float m[NQ], lsum[NQ];
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt) {
+    m[qt] = -1e30f;
+    lsum[qt] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NB; ++db) O[qt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // K/V tile staging through registers
+  u32x4 RK[LPT], RV[LPT];
+  auto load_tile = [&](int t) {
+    const int kb = t * kAttnBN;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int u = tid + kAttnWaves * 64 * i;
+      const int row = u / UPR, col = 8 * (u % UPR);
+      const bool ok = u < UNITS && t < ntiles && kb + row < Nk;
+      const size_t off = (size_t)(kb + row) * D + col;
+      RK[i] = ok ? __builtin_nontemporal_load((const u32x4*)(kh + off)) : u32x4{0u, 0u, 0u, 0u};
+      RV[i] = ok ? __builtin_nontemporal_load((const u32x4*)(vh + off)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
+    uint16_t* vt = kt + kAttnBN * RS;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int u = tid + kAttnWaves * 64 * i;
+      if (u < UNITS) {
+        const int row = u / UPR, col = 8 * (u % UPR);
+        *(u32x4*)(kt + row * RS + col) = RK[i];
+        *(u32x4*)(vt + row * RS + col) = RV[i];
+      }
+    }
+  };
+
+  const float sl2 = a.scale_log2;
+  load_tile(0);
+  store_tile(0);
+  load_tile(1);
+  for (int t = 0; t < ntiles; ++t) {
+    lds_barrier();
+    const uint16_t* kt = (const uint16_t*)(smem + (size_t)(t & 1) * 2 * Sh::tile_bytes);
+    const uint16_t* vt = kt + kAttnBN * RS;
+    const int kb = t * kAttnBN;
+
+    // S^T = K Q^T for the tile: S[kt][qt], lane: query 16 qt + n, keys 16 kt + 4 g + r
+    f32x4 S[NKT][NQ];
+#pragma unroll
+    for (int k16 = 0; k16 < NKT; ++k16) {
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int d = 32 * kc + 8 * g;
+        const u32x4 A = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A, QB[qt][kc], S[k16][qt]);
+      }
+    }
+
+    // online softmax per query (lane), P^T operands
+    u32x4 PB[NQ][NK2];
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 16 * k16 + 4 * g + r;
+          const float s = key < kend[qt] ? S[k16][qt][r] * sl2 : -INFINITY;
+          S[k16][qt][r] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = wave_max4(mx);
+      const float mnew = fmaxf(m[qt], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+      m[qt] = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(S[k16][qt][r] - mnew);
+          S[k16][qt][r] = p;
+          ps += p;
+        }
+      lsum[qt] = lsum[qt] * alpha + ps;
+#pragma unroll
+      for (int db = 0; db < NB; ++db) O[qt][db] *= alpha;
+#pragma unroll
+      for (int k2 = 0; k2 < NK2; ++k2) {
+        const f32x4 lo = S[2 * k2][qt], hi = S[2 * k2 + 1][qt];
+        PB[qt][k2] = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+                           pack_bf16(hi[2], hi[3])};
+      }
+    }
+
+    // O^T += V^T P^T: A operand = V columns 16 db + n at keys 32 k2 + {4g..4g+3, 16+4g..16+4g+3}
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+#pragma unroll
+      for (int k2 = 0; k2 < NK2; ++k2) {
+        const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
+        const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
+        const u32x4 A = u32x4{x[0], x[1], y[0], y[1]};
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(A, PB[qt][k2], O[qt][db]);
+      }
+    }
+
+    // next tile: registers -> the other buffer (free: every wave passed this
+    // iteration's barrier after finishing the previous tile), then prefetch
+    store_tile((t + 1) & 1);
+    load_tile(t + 2);
+  }
+
+  // normalise and store: lane holds O[query 16 qt + n][16 db + 4 g + r]
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt) {
+    const int qi = q0 + kAttnQW * w + 16 * qt + n;
+    const float inv = 1.f / wave_sum4(lsum[qt]);
+    if (qi < Nq) {
+#pragma unroll
+      for (int db = 0; db < NB; ++db) {
+        const f32x4 x = O[qt][db] * inv;
+        *(u32x2*)(oh + (size_t)qi * D + 16 * db + 4 * g) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
+  using Sh = AttnShape<D>;
+  const long long Nq = (long long)a.Tq * a.S;
+  const long long nqt = (Nq + kAttnBM - 1) / kAttnBM;
+  const long long blocks = nqt * a.BH;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gdn_attn_kernel<D>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(gdn_attn_kernel<D>, dim3((unsigned)blocks), dim3(kAttnWaves * 64), Sh::lds_bytes, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(int D, const AttnArgs& a, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_attn_t<16>(a, stream);
+    case 32: return launch_attn_t<32>(a, stream);
+    case 48: return launch_attn_t<48>(a, stream);
+    case 64: return launch_attn_t<64>(a, stream);
+    case 80: return launch_attn_t<80>(a, stream);
+    case 96: return launch_attn_t<96>(a, stream);
+    case 112: return launch_attn_t<112>(a, stream);
+    case 128: return launch_attn_t<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn

@@ -77,6 +77,16 @@ struct TconvArgs {
   long long cols;
 };
 
+// Block-causal softmax attention (gdn_attn.hip).
+struct AttnArgs {
+  const void* q;            // [BH][Tq*S][D] bf16 (the last Tq frames of the key sequence)
+  const void* k;            // [BH][Tk*S][D] bf16
+  const void* v;            // [BH][Tk*S][D] bf16
+  void* o;                  // [BH][Tq*S][D] bf16
+  int BH, Tq, Tk, S, chunk;
+  float scale_log2;         // softmax scale times log2(e)
+};
+
 // Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame) (backward).
 struct ZmatArgs {
   const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
@@ -135,6 +145,7 @@ hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream);
 hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream);
 hipError_t launch_dvdk(int D, const DvkArgs& da, hipStream_t stream);
 hipError_t launch_tconv(const TconvArgs& ta, hipStream_t stream);
+hipError_t launch_attn(int D, const AttnArgs& aa, hipStream_t stream);
 hipError_t launch_cdq(int D, const CdqArgs& ca, hipStream_t stream);
 hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
                                  hipStream_t stream);

@@ -106,7 +106,8 @@ typedef enum gdn_status {
 #define GDN_KERNEL_STATE 3      /* serial state pass over G_t, B_t */
 #define GDN_KERNEL_BACKWARD 4   /* the backward's own kernels (its forward replay books as GRAM/STATE) */
 #define GDN_KERNEL_TCONV 5      /* block-causal temporal convolution */
-#define GDN_KERNEL_SLOTS 6
+#define GDN_KERNEL_ATTN 6       /* block-causal softmax attention */
+#define GDN_KERNEL_SLOTS 7
 
 typedef struct gdn_desc {
   int32_t abi_version; /* GDN_ABI_VERSION */
@@ -245,6 +246,43 @@ gdn_status gdn_tconv_forward(const gdn_tconv_desc* d, const void* x, const float
 /* Host-only argument check of gdn_tconv_forward (no device is touched). */
 gdn_status gdn_tconv_check_args(const gdn_tconv_desc* d, const void* x, const float* w, const float* bias,
                                 const void* cache_in, const void* y, const void* cache_out);
+
+/*
+ * Block-causal softmax attention: the periodic softmax attention blocks that
+ * SANA-WM's hybrid keeps between its frame-wise GDN blocks (GeekNews summary
+ * of SANA-WM, on the Hybrid Linear Diffusion Transformer; SANA-WM abstract).
+ * Per (batch, head), with tokens frame-major (token i in frame i / S):
+ *
+ *   O = softmax(Q K^T * scale) V,  scale = desc.scale, or 1/sqrt(D) if 0
+ *
+ * masked block-causally over frames: the queries are the last Tq of the Tk
+ * key frames, and a query in key frame f sees the keys of every frame before
+ * the end of its block of `chunk` frames (blocks counted from key frame 0).
+ * chunk >= Tk is full bidirectional attention; Tq < Tk is the streaming case
+ * (queries of the current chunk against cached keys and values).
+ *
+ * Layouts (device pointers, bf16, 16-byte aligned): q, o [B][H][Tq][S][D];
+ * k, v [B][H][Tk][S][D].  D in {16, 32, ..., 128}; Tk*S < 2^31 - 256.  fp32
+ * accumulation and softmax (exp2 of scaled scores, running max and sum), the
+ * probabilities rounded to bf16 for the product with V, o rounded to nearest
+ * even.  o may not overlap q, k or v.  flags: GDN_FLAG_TIME_KERNELS only.
+ * Same stream and error conventions as the calls above.
+ */
+typedef struct gdn_attn_desc {
+  int32_t abi_version; /* GDN_ABI_VERSION */
+  int32_t B, H, Tq, Tk, S, D;
+  int32_t chunk;       /* frames per block, >= 1 */
+  int32_t io_dtype;    /* GDN_BF16 */
+  uint32_t flags;
+  float scale;         /* softmax scale; 0 selects 1/sqrt(D) */
+} gdn_attn_desc;
+
+gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const void* k, const void* v, void* o,
+                                 void* stream);
+
+/* Host-only argument check of gdn_attention_forward (no device is touched). */
+gdn_status gdn_attention_check_args(const gdn_attn_desc* d, const void* q, const void* k, const void* v,
+                                    const void* o);
 
 /*
  * Device time of the kernels launched by calls that set GDN_FLAG_TIME_KERNELS

@@ -296,3 +296,50 @@ def test_tconv_flag_abi_null_align_alias_errors(gdn):
     import ctypes
     assert gdn.lib().gdn_tconv_forward(ctypes.byref(d), *([None] * 6), None) == 1
     assert gdn.lib().gdn_tconv_check_args(None, *([None] * 6)) == 1
+
+
+# gdn_attention_check_args / gdn_attention_forward: host-side checks only.
+def at_args():
+    return dict(zip(("q", "k", "v", "o"), addrs(4)))
+
+
+def test_attention_valid_arguments(gdn):
+    for D in range(16, 129, 16):
+        for Tq, Tk, chunk in ((3, 3, 1), (1, 9, 4), (5, 5, 100)):
+            d = gdn.make_attn_desc(2, 3, Tq, Tk, 17, D, chunk)
+            assert gdn.attention_check_args(d, **at_args()) == 0, gdn.lib().gdn_last_error()
+    a = at_args()
+    a["k"] = a["v"] = a["q"]                       # inputs may alias
+    assert gdn.attention_check_args(gdn.make_attn_desc(1, 1, 2, 2, 8, 32, 1), **a) == 0
+
+
+@pytest.mark.parametrize("shape,code", [((0, 1, 1, 1, 8, 32, 1), 2), ((1, 0, 1, 1, 8, 32, 1), 2),
+                                        ((1, 1, 0, 1, 8, 32, 1), 2), ((1, 1, 1, 0, 8, 32, 1), 2),
+                                        ((1, 1, 1, 1, 0, 32, 1), 2), ((1, 1, 1, 1, 8, 32, 0), 2),
+                                        ((1, 1, 3, 2, 8, 32, 1), 2), ((1, 1, 1, 1, 8, 24, 1), 6),
+                                        ((1, 1, 1, 1, 8, 144, 1), 6), ((1, 1, 1, 100000, 30000, 32, 1), 2)])
+def test_attention_shape_errors(gdn, shape, code):
+    assert gdn.attention_check_args(gdn.make_attn_desc(*shape), **at_args()) == code
+
+
+def test_attention_dtype_flag_abi_null_align_alias_errors(gdn):
+    d = gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1)
+    assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, io_dtype="f32"), **at_args()) == 3
+    assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, flags=gdn.binding.FLAG_DIRECT),
+                                    **at_args()) == 6
+    assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, abi_version=2), **at_args()) == 7
+    assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, scale=float("inf")), **at_args()) == 2
+    for f in ("q", "k", "v", "o"):
+        a = at_args()
+        a[f] = 0
+        assert gdn.attention_check_args(d, **a) == 1, f
+        a = at_args()
+        a[f] += 8
+        assert gdn.attention_check_args(d, **a) == 4, f
+    for other in ("q", "k", "v"):
+        a = at_args()
+        a["o"] = a[other] + 16
+        assert gdn.attention_check_args(d, **a) == 5, other
+    import ctypes
+    assert gdn.lib().gdn_attention_forward(ctypes.byref(d), None, None, None, None, None) == 1
+    assert gdn.lib().gdn_attention_check_args(None, None, None, None, None) == 1
