@@ -14,8 +14,12 @@ field times gdn_frame_backward on the bf16 inputs (14*D algorithmic bytes per
 token-head).  A `temporal_conv` field times gdn_tconv_forward, the block-causal
 temporal convolution of the streaming FFN, on a 720p-shaped activation
 (B1 T961 S880 C2240, blocks of 4 frames, bf16: 4*C algorithmic bytes per
-token), plus one block's call latency.  The headline `value` stays the bf16
-forward step.
+token), plus one block's call latency.  An `attention` field times
+gdn_attention_forward, the block-causal softmax attention of the hybrid's
+softmax blocks, on an 81-frame 720p-shaped clip (B1 H20 S880 D112, blocks of
+4 frames) and on one 4-frame chunk of queries against the whole clip, against
+the dense bf16 MFMA peak (4*D flops per visible query-key pair).  The headline
+`value` stays the bf16 forward step.
 
 The default bf16 path is the Gram pipeline (gram pass, serial state pass,
 readout); --path direct times the single-pass recurrence instead.
@@ -251,6 +255,44 @@ def tconv_variant(gdn, wl, torch, dev, steps: int, warmup: int, block_reps: int 
                            "back_to_back_us": b2b}}
 
 
+def attn_flops(w) -> int:
+    """4*D flops per visible (query, key) pair: Q K^T and P V, 2*D each."""
+    S, Tq, Tk, c = w.S, w.Tq, w.Tk, w.chunk
+    pairs = 0
+    for f in range(Tk - Tq, Tk):
+        pairs += S * min(Tk, (f // c + 1) * c) * S
+    return w.B * w.H * pairs * 4 * w.D
+
+
+def attention_variant(gdn, wl, torch, dev, steps: int, warmup: int):
+    res = {}
+    for key, w in (("clip", wl.ATTN_CLIP_720P), ("stream_chunk", wl.ATTN_STREAM_720P)):
+        inp = wl.generate_attn(w, device=dev)
+        o = torch.empty_like(inp["q"])
+        call = lambda timed: gdn.attention_forward(inp["q"], inp["k"], inp["v"], w.chunk, out=o, time_kernels=timed)
+        for _ in range(warmup):
+            call(False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call(False)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        gdn.kernel_times(reset=True)
+        for _ in range(steps):
+            call(True)
+        torch.cuda.synchronize()
+        kms = gdn.kernel_times(reset=True)["attention"][0] / steps
+        fl = attn_flops(w)
+        tfs = fl / (kms * 1e-3) / 1e12
+        res[key] = {"workload": w.name, "value": w.tokens / (ms * 1e-3), "unit": "query tokens/s (B*H*Tq*S)",
+                    "ms_per_step": ms, "kernel_ms": kms,
+                    "roofline": {"bound": "mfma", "kernel": "attention", "achieved": tfs, "peak": BF16_MFMA_PEAK_TFS,
+                                 "unit": "TFLOP/s", "frac": tfs / BF16_MFMA_PEAK_TFS, "flops_per_launch": fl}}
+        del inp, o
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +303,8 @@ def main():
                     help="skip the timing of gdn_frame_backward on the same inputs")
     ap.add_argument("--no-tconv", dest="tconv", action="store_false",
                     help="skip the timing of the block-causal temporal convolution")
+    ap.add_argument("--no-attention", dest="attention", action="store_false",
+                    help="skip the timing of the block-causal softmax attention")
     ap.add_argument("--no-fp8", dest="fp8", action="store_false",
                     help="skip the E4M3 I/O variant of the step")
     ap.add_argument("--stream-reps", type=int, default=5,
@@ -367,6 +411,8 @@ def main():
         rec["backward"] = backward_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
     if args.tconv:
         rec["temporal_conv"] = tconv_variant(gdn, wl, torch, dev, args.steps, args.warmup)
+    if args.attention:
+        rec["attention"] = attention_variant(gdn, wl, torch, dev, max(1, args.steps // 4), 1)
     if args.fp8 and args.path == "auto":
         rec["variants"] = {"fp8_e4m3_io": fp8_variant(gdn, wl, torch, dev, args.steps, args.warmup)}
     if args.cpu_heads > 0:
