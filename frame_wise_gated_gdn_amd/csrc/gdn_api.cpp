@@ -496,10 +496,11 @@ gdn_status check_attn(const gdn_attn_desc* d, const void* q, const void* k, cons
   if (d->Tq > d->Tk) return fail(GDN_ERR_SHAPE, "Tq=%d > Tk=%d: the queries are the last Tq key frames", d->Tq, d->Tk);
   if (d->D % 16 != 0 || d->D > 128)
     return fail(GDN_ERR_UNSUPPORTED, "D=%d: supported head dims are 16, 32, ..., 128", d->D);
-  if (!std::isfinite(d->scale)) return fail(GDN_ERR_SHAPE, "scale must be finite");
+  if (!std::isfinite(d->scale) || d->scale < 0.f)
+    return fail(GDN_ERR_SHAPE, "scale must be finite and >= 0 (0 selects 1/sqrt(D))");
   const long double nk = (long double)d->Tk * d->S, bh = (long double)d->B * d->H;
-  if (nk >= 2147483648.0L - 256 || bh * ((long double)d->Tq * d->S / 128 + 1) >= 2147483648.0L)
-    return fail(GDN_ERR_SHAPE, "too many tokens per head for 32-bit indexing");
+  if (nk * d->D * 2 >= 2147483648.0L || bh * ((long double)d->Tq * d->S / 128 + 1) >= 2147483648.0L)
+    return fail(GDN_ERR_SHAPE, "too many tokens per head: Tk*S*D*2 bytes must stay below 2 GiB");
   if (bh * nk * d->D * 2 >= (long double)SIZE_MAX / 4) return fail(GDN_ERR_SHAPE, "tensor sizes overflow");
   if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o are required");
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))

@@ -7,9 +7,16 @@
 //   frames) sees the keys of every frame up to the end of its block of
 //   `chunk` frames.
 //
-// One workgroup of four waves owns 128 consecutive queries of one head and
-// streams the visible keys and values through LDS in tiles of 64 tokens
-// (double-buffered; one barrier per tile).  Each wave owns 32 queries.
+// One workgroup of eight waves owns 256 consecutive queries of one head and
+// streams the visible keys and values through LDS in tiles of 64 tokens, one
+// barrier per tile.  Each wave owns 32 queries.  Every key and value byte
+// brought into a CU serves 256 queries: at 128 the kernel was bound by these
+// re-reads (about 5 TB/s of K/V per call at the 720p clip).
+//
+// Software pipeline across key tiles: iteration t issues the S^T MFMAs of tile
+// t, then the V^T P^T MFMAs of tile t-1, then the softmax of tile t, whose
+// VALU work overlaps the P V products still in the matrix pipe.  K is
+// double-buffered in LDS; V, read one iteration later, triple-buffered.
 //
 // Transposed formulation.  The wave computes S^T = K Q^T (keys as MFMA rows,
 // queries as columns) and O^T = V^T P^T, so that in every accumulator a lane
@@ -17,7 +24,9 @@
 // 4g..4g+3):
 //   * the online softmax state (running max m, running sum) is per lane, and
 //     rescaling O by exp(m_old - m_new) needs no cross-lane traffic; the max
-//     over a tile's keys takes two lane shuffles (the four lanes of a query);
+//     over a tile's keys takes two lane shuffles (the four lanes of a query),
+//     and the sum is one more MFMA row block (bf16 ones times P^T), so the
+//     denominator sums the same bf16 probabilities as the numerator;
 //   * P goes from the S^T accumulators straight into the B operand of the
 //     V^T P^T product (bf16), with the keys of a 32-key step taken in the
 //     order 4g..4g+3, 16+4g..16+4g+3, which is the order in which the
@@ -25,8 +34,9 @@
 //     V; no LDS round trip for P.
 //   * Q^T is the B operand of S^T: each lane loads its query row once, from
 //     global memory, and keeps it in registers.
-// Scores are scaled by scale*log2(e) and exponentiated with exp2.  Masked keys
-// (past the query's block, or past the key sequence) score -inf.
+// Scores are scaled by scale*log2(e) (> 0) inside the exponent:
+// p = exp2(s * scale*log2(e) - m).  Masked keys (past the query's block) score
+// -inf; the running max starts finite, so no lane ever computes -inf - -inf.
 //
 // MFMA lane layouts are those of gdn_device.h (16x16x32 bf16).
 #include <hip/hip_runtime.h>
@@ -39,7 +49,7 @@ namespace gdn {
 
 namespace {
 
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 8;
 constexpr int kAttnQW = 32;                        // queries per wave
 constexpr int kAttnBM = kAttnWaves * kAttnQW;      // queries per workgroup
 constexpr int kAttnBN = 64;                        // keys per tile
@@ -56,16 +66,12 @@ struct AttnShape {
   static constexpr int LPT = (UNITS + kAttnWaves * 64 - 1) / (kAttnWaves * 64);   // units per thread
   static constexpr int RS = D + 8;                 // LDS row stride (elements)
   static constexpr size_t tile_bytes = (size_t)kAttnBN * RS * 2;
-  static constexpr size_t lds_bytes = 2 * 2 * tile_bytes;   // (K, V) x 2 buffers
+  static constexpr size_t lds_bytes = 5 * tile_bytes;       // K x 2 buffers, V x 3 buffers
 };
 
 __device__ __forceinline__ float wave_max4(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float wave_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
 }
 
 // Keys visible to a query token qi of the query sequence (last Tq frames).
@@ -75,7 +81,7 @@ __device__ __forceinline__ int key_end(int qi, const AttnArgs& a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnWaves * 64, 2) void gdn_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a) {
   using Sh = AttnShape<D>;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, NQ = Sh::NQ, NKT = Sh::NKT, NK2 = Sh::NK2;
   constexpr int UPR = Sh::UPR, UNITS = Sh::UNITS, LPT = Sh::LPT, RS = Sh::RS;
@@ -83,8 +89,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void gdn_attn_kernel(AttnArgs a
 
   const int Nq = a.Tq * a.S, Nk = a.Tk * a.S;
   const int nqt = (Nq + kAttnBM - 1) / kAttnBM;
+  // head-major; within a head the longest key ranges start first
   const int bh = blockIdx.x / nqt;
-  const int qtile = nqt - 1 - (int)(blockIdx.x % nqt);     // the longest key ranges start first
+  const int qtile = nqt - 1 - (int)(blockIdx.x % nqt);
   const int q0 = qtile * kAttnBM;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
   const uint16_t* qh = (const uint16_t*)a.q + (size_t)bh * Nq * D;
@@ -96,7 +103,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void gdn_attn_kernel(AttnArgs a
   const int kend_wg = key_end(min(q0 + kAttnBM, Nq) - 1, a);
   const int ntiles = (kend_wg + kAttnBN - 1) / kAttnBN;
 
-  // this lane's queries (one per query tile) and their key ends
+  // this lane's queries (one per query tile) and their key ends; lane 0 holds
+  // the wave's first query, whose key end is the wave's smallest
   int kend[NQ];
   u32x4 QB[NQ][NKC];
 #pragma unroll
@@ -110,131 +118,163 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void gdn_attn_kernel(AttnArgs a
     }
   }
 
+  const int kend_lo = __builtin_amdgcn_readfirstlane(kend[0]);
   f32x4 O[NQ][NB];
-  float m[NQ], lsum[NQ];
+  float m[NQ];
+  f32x4 L[NQ];                  // running sum of P per query (every row of a lane holds it)
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     m[qt] = -1e30f;
-    lsum[qt] = 0.f;
+    L[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < NB; ++db) O[qt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K/V tile staging through registers
+  // K/V tile staging through registers.  A tile's rows are contiguous in HBM,
+  // so unit u (16 bytes) sits 8u elements after the tile's first key; in LDS
+  // the rows are padded to RS elements (offset hoisted out of the tile loop).
   u32x4 RK[LPT], RV[LPT];
+  int lds_u[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int u = tid + kAttnWaves * 64 * i;
+    lds_u[i] = 8 * u + 8 * (u / UPR);
+  }
+  // buffer loads: a unit past the head's keys (or past the last tile) reads zeros
+  const uint32_t head_bytes = (uint32_t)Nk * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, head_bytes), vrs = make_rsrc(vh, head_bytes);
   auto load_tile = [&](int t) {
-    const int kb = t * kAttnBN;
+    const uint32_t base = (uint32_t)t * kAttnBN * D * 2;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int u = tid + kAttnWaves * 64 * i;
-      const int row = u / UPR, col = 8 * (u % UPR);
-      const bool ok = u < UNITS && t < ntiles && kb + row < Nk;
-      const size_t off = (size_t)(kb + row) * D + col;
-      RK[i] = ok ? __builtin_nontemporal_load((const u32x4*)(kh + off)) : u32x4{0u, 0u, 0u, 0u};
-      RV[i] = ok ? __builtin_nontemporal_load((const u32x4*)(vh + off)) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t off = (u < UNITS && t < ntiles) ? base + 16u * u : kOOB;
+      RK[i] = buf_load16_nt(krs, off);
+      RV[i] = buf_load16_nt(vrs, off);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
-    uint16_t* vt = kt + kAttnBN * RS;
+  auto store_tile = [&](int kbuf, int vbuf) {
+    uint16_t* kt = (uint16_t*)(smem + (size_t)kbuf * Sh::tile_bytes);
+    uint16_t* vt = (uint16_t*)(smem + (size_t)(2 + vbuf) * Sh::tile_bytes);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int u = tid + kAttnWaves * 64 * i;
-      if (u < UNITS) {
-        const int row = u / UPR, col = 8 * (u % UPR);
-        *(u32x4*)(kt + row * RS + col) = RK[i];
-        *(u32x4*)(vt + row * RS + col) = RV[i];
+      if (tid + kAttnWaves * 64 * i < UNITS) {
+        *(u32x4*)(kt + lds_u[i]) = RK[i];
+        *(u32x4*)(vt + lds_u[i]) = RV[i];
       }
     }
   };
 
   const float sl2 = a.scale_log2;
+  u32x4 PB[NQ][NK2];            // P^T operands of the previous tile
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   load_tile(1);
-  for (int t = 0; t < ntiles; ++t) {
+  int vcur = 0;                 // V buffer of tile t
+  for (int t = 0; t <= ntiles; ++t) {
     lds_barrier();
-    const uint16_t* kt = (const uint16_t*)(smem + (size_t)(t & 1) * 2 * Sh::tile_bytes);
-    const uint16_t* vt = kt + kAttnBN * RS;
+    const int vprev = vcur == 0 ? 2 : vcur - 1;
     const int kb = t * kAttnBN;
-
-    // S^T = K Q^T for the tile: S[kt][qt], lane: query 16 qt + n, keys 16 kt + 4 g + r
     f32x4 S[NKT][NQ];
+    if (t < ntiles) {
+      // S^T = K Q^T for tile t: S[k16][qt], lane: query 16 qt + n, keys 16 k16 + 4 g + r
+      const uint16_t* kt = (const uint16_t*)(smem + (size_t)(t & 1) * Sh::tile_bytes);
 #pragma unroll
-    for (int k16 = 0; k16 < NKT; ++k16) {
+      for (int k16 = 0; k16 < NKT; ++k16) {
 #pragma unroll
-      for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const int d = 32 * kc + 8 * g;
-        const u32x4 A = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
+        for (int kc = 0; kc < NKC; ++kc) {
+          const int d = 32 * kc + 8 * g;
+          const u32x4 A = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A, QB[qt][kc], S[k16][qt]);
-      }
-    }
-
-    // online softmax per query (lane), P^T operands
-    u32x4 PB[NQ][NK2];
-#pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int k16 = 0; k16 < NKT; ++k16)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb + 16 * k16 + 4 * g + r;
-          const float s = key < kend[qt] ? S[k16][qt][r] * sl2 : -INFINITY;
-          S[k16][qt][r] = s;
-          mx = fmaxf(mx, s);
+          for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A, QB[qt][kc], S[k16][qt]);
         }
-      mx = wave_max4(mx);
-      const float mnew = fmaxf(m[qt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
-      m[qt] = mnew;
-      float ps = 0.f;
+      }
+    }
+    if (t > 0) {
+      // O^T += V^T P^T for tile t-1: A operand = V columns 16 db + n at keys
+      // 32 k2 + {4g..4g+3, 16+4g..16+4g+3}
+      const uint16_t* vt = (const uint16_t*)(smem + (size_t)(2 + vprev) * Sh::tile_bytes);
 #pragma unroll
-      for (int k16 = 0; k16 < NKT; ++k16)
+      for (int db = 0; db < NB; ++db) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(S[k16][qt][r] - mnew);
-          S[k16][qt][r] = p;
-          ps += p;
+        for (int k2 = 0; k2 < NK2; ++k2) {
+          const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
+          const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
+          const u32x4 A = u32x4{x[0], x[1], y[0], y[1]};
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(A, PB[qt][k2], O[qt][db]);
         }
-      lsum[qt] = lsum[qt] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < NB; ++db) O[qt][db] *= alpha;
-#pragma unroll
-      for (int k2 = 0; k2 < NK2; ++k2) {
-        const f32x4 lo = S[2 * k2][qt], hi = S[2 * k2 + 1][qt];
-        PB[qt][k2] = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
-                           pack_bf16(hi[2], hi[3])};
       }
+      // the softmax denominator on the matrix cores: a 16-row block of bf16
+      // ones times P^T sums the same bf16 probabilities that weight V
+      const u32x4 ONES = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+      for (int k2 = 0; k2 < NK2; ++k2)
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) L[qt] = mfma_bf16(ONES, PB[qt][k2], L[qt]);
     }
-
-    // O^T += V^T P^T: A operand = V columns 16 db + n at keys 32 k2 + {4g..4g+3, 16+4g..16+4g+3}
+    if (t < ntiles) {
+      // online softmax of tile t per query (lane).  Scores are masked only in
+      // the tiles that reach past the block end of the wave's first query
+      // (the smallest key end of the wave); the max is taken on raw scores
+      // and the scale folded into the exponent (scale > 0).  When no lane's
+      // running max moved, the rescale factor is exactly 1 and is skipped.
+      if (kb + kAttnBN > kend_lo) {
 #pragma unroll
-    for (int db = 0; db < NB; ++db) {
+        for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
-      for (int k2 = 0; k2 < NK2; ++k2) {
-        const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
-        const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
-        const u32x4 A = u32x4{x[0], x[1], y[0], y[1]};
+          for (int k16 = 0; k16 < NKT; ++k16)
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(A, PB[qt][k2], O[qt][db]);
+            for (int r = 0; r < 4; ++r)
+              if (kb + 16 * k16 + 4 * g + r >= kend[qt]) S[k16][qt][r] = -INFINITY;
       }
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[k16][qt][r]);
+        mx = wave_max4(mx);
+        const float mold = m[qt];
+        const float mnew = fmaxf(mold, mx * sl2);
+        m[qt] = mnew;
+#pragma unroll
+        for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[k16][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k16][qt][r], sl2, -mnew));
+        if (__any(mnew > mold)) {
+          // O and L hold the products of tiles 0..t-1 (t-1 issued above)
+          const float alpha = __builtin_amdgcn_exp2f(mold - mnew);
+          L[qt] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NB; ++db) O[qt][db] *= alpha;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NK2; ++k2) {
+          const f32x4 lo = S[2 * k2][qt], hi = S[2 * k2 + 1][qt];
+          PB[qt][k2] = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+                             pack_bf16(hi[2], hi[3])};
+        }
+      }
+      // tile t+1: registers -> K buffer (t+1)&1 (last read for tile t-1) and
+      // V buffer vcur+1 (last read for tile t-2): every wave passed this
+      // iteration's barrier after those reads.  Then prefetch tile t+2.
+      const int vnext = vcur == 2 ? 0 : vcur + 1;
+      if (t + 1 < ntiles) store_tile((t + 1) & 1, vnext);
+      load_tile(t + 2);
+      vcur = vnext;
     }
-
-    // next tile: registers -> the other buffer (free: every wave passed this
-    // iteration's barrier after finishing the previous tile), then prefetch
-    store_tile((t + 1) & 1);
-    load_tile(t + 2);
   }
 
   // normalise and store: lane holds O[query 16 qt + n][16 db + 4 g + r]
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     const int qi = q0 + kAttnQW * w + 16 * qt + n;
-    const float inv = 1.f / wave_sum4(lsum[qt]);
+    const float inv = 1.f / L[qt][0];
     if (qi < Nq) {
 #pragma unroll
       for (int db = 0; db < NB; ++db) {

@@ -262,10 +262,10 @@ gdn_status gdn_tconv_check_args(const gdn_tconv_desc* d, const void* x, const fl
  * (queries of the current chunk against cached keys and values).
  *
  * Layouts (device pointers, bf16, 16-byte aligned): q, o [B][H][Tq][S][D];
- * k, v [B][H][Tk][S][D].  D in {16, 32, ..., 128}; Tk*S < 2^31 - 256.  fp32
- * accumulation and softmax (exp2 of scaled scores, running max and sum), the
- * probabilities rounded to bf16 for the product with V, o rounded to nearest
- * even.  o may not overlap q, k or v.  flags: GDN_FLAG_TIME_KERNELS only.
+ * k, v [B][H][Tk][S][D].  D in {16, 32, ..., 128}; one head's k (and v)
+ * below 2 GiB (Tk*S*D*2 bytes).  fp32 accumulation and softmax (exp2 of scaled
+ * scores, running max), the probabilities rounded to bf16 for the products
+ * with V and with ones (the denominator), o rounded to nearest even.  o may not overlap q, k or v.  flags: GDN_FLAG_TIME_KERNELS only.
  * Same stream and error conventions as the calls above.
  */
 typedef struct gdn_attn_desc {
@@ -274,7 +274,7 @@ typedef struct gdn_attn_desc {
   int32_t chunk;       /* frames per block, >= 1 */
   int32_t io_dtype;    /* GDN_BF16 */
   uint32_t flags;
-  float scale;         /* softmax scale; 0 selects 1/sqrt(D) */
+  float scale;         /* softmax scale, finite and >= 0; 0 selects 1/sqrt(D) */
 } gdn_attn_desc;
 
 gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const void* k, const void* v, void* o,

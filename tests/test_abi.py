@@ -329,6 +329,7 @@ def test_attention_dtype_flag_abi_null_align_alias_errors(gdn):
                                     **at_args()) == 6
     assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, abi_version=2), **at_args()) == 7
     assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, scale=float("inf")), **at_args()) == 2
+    assert gdn.attention_check_args(gdn.make_attn_desc(1, 2, 2, 2, 8, 32, 1, scale=-0.5), **at_args()) == 2
     for f in ("q", "k", "v", "o"):
         a = at_args()
         a[f] = 0

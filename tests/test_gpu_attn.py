@@ -2,12 +2,13 @@
 against the double-precision oracle (oracle/attn_oracle.py), through the C ABI.
 
 Bound.  The inputs are exact bf16 values.  The GPU accumulates Q K^T in fp32
-(relative error ~D 2^-24, negligible), exponentiates in fp32, rounds each
-probability p_j to bf16 (relative 2^-9) for the product with V and
-normalises by the fp32 sum of the unrounded p_j, then rounds O to bf16.  The
-probability rounding moves O_i by at most 2^-9 sum_j p_j |v_j| / sum_j p_j
-<= 2^-9 max|V|, and the output rounding by 2^-9 |O_i| <= 2^-9 max|V|, so
-element by element |O - O_exact| <= 2^-8 max|V| (+1e-6 for the fp32 terms).
+(relative error ~D 2^-24, negligible), exponentiates in fp32 and rounds each
+probability p_j to bf16 (p~_j = p_j (1 + e_j), |e_j| <= 2^-9); numerator and
+denominator both sum the rounded p~_j, so O_i is a convex combination of the
+v_j whose weights are each within a factor (1 +- 2^-9)/(1 -+ 2^-9) of the
+exact ones: |O_i - O_exact| <= 2^-8 (1 + 2^-8) max|V|.  The output rounding
+adds 2^-9 |O_i| <= 2^-9 max|V|, so element by element
+|O - O_exact| <= 2^-7 max|V| (+1e-6 for the fp32 terms).
 The relative Frobenius error per head is also held to the bf16 bar, 2e-2.
 """
 import numpy as np
@@ -36,7 +37,7 @@ def f64(x):
 def check_head(o, q, k, v, S, chunk, ao, scale=None):
     ref = ao.attention_head(q, k, v, S, chunk, scale)
     err = np.abs(o - ref)
-    bound = 2.0 ** -8 * np.abs(v).max() + 1e-6
+    bound = 2.0 ** -7 * np.abs(v).max() + 1e-6
     assert err.max() <= bound, f"max err {err.max():.3e} > bound {bound:.3e}"
     rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
     assert rel < TOL, rel
@@ -114,7 +115,7 @@ def test_attention_720p_clip_sampled_queries(env):
         k = f64(inp["k"][0, h]).reshape(-1, D)
         v = f64(inp["v"][0, h]).reshape(-1, D)
         got = f64(o[0, h]).reshape(-1, D)
-        bound = 2.0 ** -8 * np.abs(v).max() + 1e-6
+        bound = 2.0 ** -7 * np.abs(v).max() + 1e-6
         for i in rows:
             f = i // S
             end = min(w.Tk, (f // w.chunk + 1) * w.chunk) * S
