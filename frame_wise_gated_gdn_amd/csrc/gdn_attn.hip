@@ -13,10 +13,9 @@
 // brought into a CU serves 256 queries: at 128 the kernel was bound by these
 // re-reads (about 5 TB/s of K/V per call at the 720p clip).
 //
-// Software pipeline across key tiles: iteration t issues the S^T MFMAs of tile
-// t, then the V^T P^T MFMAs of tile t-1, then the softmax of tile t, whose
-// VALU work overlaps the P V products still in the matrix pipe.  K is
-// double-buffered in LDS; V, read one iteration later, triple-buffered.
+// The eight waves form two groups that run each tile's phases in different
+// orders (see the main loop), so that the softmax of one wave overlaps the
+// matrix products of the other wave on the same SIMD.
 //
 // Transposed formulation.  The wave computes S^T = K Q^T (keys as MFMA rows,
 // queries as columns) and O^T = V^T P^T, so that in every accumulator a lane
@@ -66,7 +65,7 @@ struct AttnShape {
   static constexpr int LPT = (UNITS + kAttnWaves * 64 - 1) / (kAttnWaves * 64);   // units per thread
   static constexpr int RS = D + 8;                 // LDS row stride (elements)
   static constexpr size_t tile_bytes = (size_t)kAttnBN * RS * 2;
-  static constexpr size_t lds_bytes = 5 * tile_bytes;       // K x 2 buffers, V x 3 buffers
+  static constexpr size_t lds_bytes = 5 * tile_bytes;       // K x 3 buffers, V x 2 buffers
 };
 
 __device__ __forceinline__ float wave_max4(float x) {
@@ -143,131 +142,156 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   // buffer loads: a unit past the head's keys (or past the last tile) reads zeros
   const uint32_t head_bytes = (uint32_t)Nk * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, head_bytes), vrs = make_rsrc(vh, head_bytes);
-  auto load_tile = [&](int t) {
-    const uint32_t base = (uint32_t)t * kAttnBN * D * 2;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int u = tid + kAttnWaves * 64 * i;
-      const uint32_t off = (u < UNITS && t < ntiles) ? base + 16u * u : kOOB;
-      RK[i] = buf_load16_nt(krs, off);
-      RV[i] = buf_load16_nt(vrs, off);
-    }
+  auto tile_off = [&](int t, int i) -> uint32_t {
+    const int u = tid + kAttnWaves * 64 * i;
+    return (u < UNITS && t < ntiles) ? (uint32_t)t * kAttnBN * D * 2 + 16u * u : kOOB;
   };
-  auto store_tile = [&](int kbuf, int vbuf) {
-    uint16_t* kt = (uint16_t*)(smem + (size_t)kbuf * Sh::tile_bytes);
-    uint16_t* vt = (uint16_t*)(smem + (size_t)(2 + vbuf) * Sh::tile_bytes);
+  auto load_k = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      if (tid + kAttnWaves * 64 * i < UNITS) {
-        *(u32x4*)(kt + lds_u[i]) = RK[i];
-        *(u32x4*)(vt + lds_u[i]) = RV[i];
-      }
-    }
+    for (int i = 0; i < LPT; ++i) RK[i] = buf_load16_nt(krs, tile_off(t, i));
+  };
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) RV[i] = buf_load16_nt(vrs, tile_off(t, i));
+  };
+  // LDS: K buffers 0..2, then V buffers 0..1
+  auto kbuf_ptr = [&](int b) { return (uint16_t*)(smem + (size_t)b * Sh::tile_bytes); };
+  auto vbuf_ptr = [&](int b) { return (uint16_t*)(smem + (size_t)(3 + b) * Sh::tile_bytes); };
+  auto store_k = [&](int b) {
+    uint16_t* dst = kbuf_ptr(b);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      if (tid + kAttnWaves * 64 * i < UNITS) *(u32x4*)(dst + lds_u[i]) = RK[i];
+  };
+  auto store_v = [&](int b) {
+    uint16_t* dst = vbuf_ptr(b);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      if (tid + kAttnWaves * 64 * i < UNITS) *(u32x4*)(dst + lds_u[i]) = RV[i];
   };
 
   const float sl2 = a.scale_log2;
-  u32x4 PB[NQ][NK2];            // P^T operands of the previous tile
-  load_tile(0);
-  store_tile(0, 0);
-  load_tile(1);
-  int vcur = 0;                 // V buffer of tile t
-  for (int t = 0; t <= ntiles; ++t) {
-    lds_barrier();
-    const int vprev = vcur == 0 ? 2 : vcur - 1;
-    const int kb = t * kAttnBN;
-    f32x4 S[NKT][NQ];
-    if (t < ntiles) {
-      // S^T = K Q^T for tile t: S[k16][qt], lane: query 16 qt + n, keys 16 k16 + 4 g + r
-      const uint16_t* kt = (const uint16_t*)(smem + (size_t)(t & 1) * Sh::tile_bytes);
+  f32x4 S[NKT][NQ];
+  // S^T = K Q^T for one key tile: S[k16][qt], lane: query 16 qt + n, keys 16 k16 + 4 g + r
+  auto scores = [&](const uint16_t* kt) {
 #pragma unroll
-      for (int k16 = 0; k16 < NKT; ++k16) {
+    for (int k16 = 0; k16 < NKT; ++k16) {
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-          const int d = 32 * kc + 8 * g;
-          const u32x4 A = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int d = 32 * kc + 8 * g;
+        const u32x4 A = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-          for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A, QB[qt][kc], S[k16][qt]);
-        }
+        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A, QB[qt][kc], S[k16][qt]);
       }
     }
-    if (t > 0) {
-      // O^T += V^T P^T for tile t-1: A operand = V columns 16 db + n at keys
-      // 32 k2 + {4g..4g+3, 16+4g..16+4g+3}
-      const uint16_t* vt = (const uint16_t*)(smem + (size_t)(2 + vprev) * Sh::tile_bytes);
+  };
+  // online softmax of the tile at key kb, then O += V^T P^T with the tile's V.
+  // Scores are masked only in the tiles that reach past the block end of the
+  // wave's first query (the smallest key end of the wave); the max is taken
+  // on raw scores and the scale folded into the exponent (scale > 0); when no
+  // lane's running max moved, the rescale factor is exactly 1 and is skipped.
+  auto softmax_pv = [&](int kb, const uint16_t* vt) {
+    if (kb + kAttnBN > kend_lo) {
 #pragma unroll
-      for (int db = 0; db < NB; ++db) {
-#pragma unroll
-        for (int k2 = 0; k2 < NK2; ++k2) {
-          const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
-          const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
-          const u32x4 A = u32x4{x[0], x[1], y[0], y[1]};
-#pragma unroll
-          for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(A, PB[qt][k2], O[qt][db]);
-        }
-      }
-      // the softmax denominator on the matrix cores: a 16-row block of bf16
-      // ones times P^T sums the same bf16 probabilities that weight V
-      const u32x4 ONES = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-#pragma unroll
-      for (int k2 = 0; k2 < NK2; ++k2)
-#pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) L[qt] = mfma_bf16(ONES, PB[qt][k2], L[qt]);
-    }
-    if (t < ntiles) {
-      // online softmax of tile t per query (lane).  Scores are masked only in
-      // the tiles that reach past the block end of the wave's first query
-      // (the smallest key end of the wave); the max is taken on raw scores
-      // and the scale folded into the exponent (scale > 0).  When no lane's
-      // running max moved, the rescale factor is exactly 1 and is skipped.
-      if (kb + kAttnBN > kend_lo) {
-#pragma unroll
-        for (int qt = 0; qt < NQ; ++qt)
-#pragma unroll
-          for (int k16 = 0; k16 < NKT; ++k16)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (kb + 16 * k16 + 4 * g + r >= kend[qt]) S[k16][qt][r] = -INFINITY;
-      }
-#pragma unroll
-      for (int qt = 0; qt < NQ; ++qt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int k16 = 0; k16 < NKT; ++k16)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[k16][qt][r]);
-        mx = wave_max4(mx);
-        const float mold = m[qt];
-        const float mnew = fmaxf(mold, mx * sl2);
-        m[qt] = mnew;
+      for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
         for (int k16 = 0; k16 < NKT; ++k16)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            S[k16][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k16][qt][r], sl2, -mnew));
-        if (__any(mnew > mold)) {
-          // O and L hold the products of tiles 0..t-1 (t-1 issued above)
-          const float alpha = __builtin_amdgcn_exp2f(mold - mnew);
-          L[qt] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NB; ++db) O[qt][db] *= alpha;
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < NK2; ++k2) {
-          const f32x4 lo = S[2 * k2][qt], hi = S[2 * k2 + 1][qt];
-          PB[qt][k2] = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
-                             pack_bf16(hi[2], hi[3])};
-        }
-      }
-      // tile t+1: registers -> K buffer (t+1)&1 (last read for tile t-1) and
-      // V buffer vcur+1 (last read for tile t-2): every wave passed this
-      // iteration's barrier after those reads.  Then prefetch tile t+2.
-      const int vnext = vcur == 2 ? 0 : vcur + 1;
-      if (t + 1 < ntiles) store_tile((t + 1) & 1, vnext);
-      load_tile(t + 2);
-      vcur = vnext;
+            if (kb + 16 * k16 + 4 * g + r >= kend[qt]) S[k16][qt][r] = -INFINITY;
     }
+    u32x4 PB[NQ][NK2];
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[k16][qt][r]);
+      mx = wave_max4(mx);
+      const float mold = m[qt];
+      const float mnew = fmaxf(mold, mx * sl2);
+      m[qt] = mnew;
+#pragma unroll
+      for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[k16][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k16][qt][r], sl2, -mnew));
+      if (__any(mnew > mold)) {
+        const float alpha = __builtin_amdgcn_exp2f(mold - mnew);
+        L[qt] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NB; ++db) O[qt][db] *= alpha;
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < NK2; ++k2) {
+        const f32x4 lo = S[2 * k2][qt], hi = S[2 * k2 + 1][qt];
+        PB[qt][k2] = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+                           pack_bf16(hi[2], hi[3])};
+      }
+    }
+    // A operand = V columns 16 db + n at keys 32 k2 + {4g..4g+3, 16+4g..16+4g+3}
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+#pragma unroll
+      for (int k2 = 0; k2 < NK2; ++k2) {
+        const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
+        const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
+        const u32x4 A = u32x4{x[0], x[1], y[0], y[1]};
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(A, PB[qt][k2], O[qt][db]);
+      }
+    }
+    // the softmax denominator on the matrix cores: a 16-row block of bf16 ones
+    // times P^T sums the same bf16 probabilities that weight V
+    const u32x4 ONES = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+    for (int k2 = 0; k2 < NK2; ++k2)
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) L[qt] = mfma_bf16(ONES, PB[qt][k2], L[qt]);
+  };
+
+  // Two wave groups in opposite phase.  At the top of iteration t the LDS
+  // holds K tiles t and t+1 and V tile t.  Group A (waves 0-3) computes the
+  // scores of tile t, then its softmax and P V; group B (waves 4-7) has the
+  // scores of tile t from the previous iteration, does the softmax and P V
+  // first and the scores of tile t+1 last.  A SIMD runs one wave of each
+  // group, so one wave's softmax (VALU) meets the other's products (MFMA).
+  // Staging keeps K one tile ahead of V: iteration t stores K tile t+2
+  // (buffer (t+2)%3, last read for tile t-1) and V tile t+1 (buffer (t+1)%2,
+  // last read for tile t-1), then prefetches K t+3 and V t+2.
+  const bool grpB = w >= kAttnWaves / 2;
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  load_k(1);
+  store_k(1);
+  load_k(2);
+  load_v(1);
+  lds_barrier();
+  if (grpB) scores(kbuf_ptr(0));
+  int kb0 = 0, kb1 = 1, kb2 = 2;          // K buffers of tiles t, t+1, t+2
+  for (int t = 0; t < ntiles; ++t) {
+    lds_barrier();
+    const uint16_t* vt = vbuf_ptr(t & 1);
+    if (!grpB) {
+      scores(kbuf_ptr(kb0));
+      softmax_pv(t * kAttnBN, vt);
+    } else {
+      softmax_pv(t * kAttnBN, vt);
+      if (t + 1 < ntiles) scores(kbuf_ptr(kb1));
+    }
+    if (t + 2 < ntiles) store_k(kb2);
+    if (t + 1 < ntiles) store_v((t + 1) & 1);
+    load_k(t + 3);
+    load_v(t + 2);
+    const int kfree = kb0;
+    kb0 = kb1;
+    kb1 = kb2;
+    kb2 = kfree;
   }
 
   // normalise and store: lane holds O[query 16 qt + n][16 db + 4 g + r]
