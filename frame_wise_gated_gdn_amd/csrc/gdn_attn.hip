@@ -174,17 +174,26 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   f32x4 S[NKT][NQ];
   // S^T = K Q^T for one key tile: S[k16][qt], lane: query 16 qt + n, keys 16 k16 + 4 g + r
   auto scores = [&](const uint16_t* kt) {
-#pragma unroll
-    for (int k16 = 0; k16 < NKT; ++k16) {
-#pragma unroll
-      for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K operands of the next 16-key group are read while the current group's
+    // products run
+    u32x4 A[2][NKC];
+    auto read_a = [&](int buf, int k16) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const int d = 32 * kc + 8 * g;
-        const u32x4 A = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A, QB[qt][kc], S[k16][qt]);
+        A[buf][kc] = d < D ? *(const u32x4*)(kt + (16 * k16 + n) * RS + d) : u32x4{0u, 0u, 0u, 0u};
       }
+    };
+    read_a(0, 0);
+#pragma unroll
+    for (int k16 = 0; k16 < NKT; ++k16) {
+      if (k16 + 1 < NKT) read_a((k16 + 1) & 1, k16 + 1);
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A[k16 & 1][kc], QB[qt][kc], S[k16][qt]);
     }
   };
   // online softmax of the tile at key kb, then O += V^T P^T with the tile's V.
@@ -232,17 +241,25 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
                            pack_bf16(hi[2], hi[3])};
       }
     }
-    // A operand = V columns 16 db + n at keys 32 k2 + {4g..4g+3, 16+4g..16+4g+3}
-#pragma unroll
-    for (int db = 0; db < NB; ++db) {
+    // A operand = V columns 16 db + n at keys 32 k2 + {4g..4g+3, 16+4g..16+4g+3};
+    // the next column block's operands are read while the current one's run
+    u32x4 VA[2][NK2];
+    auto read_v = [&](int buf, int db) {
 #pragma unroll
       for (int k2 = 0; k2 < NK2; ++k2) {
         const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
         const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
-        const u32x4 A = u32x4{x[0], x[1], y[0], y[1]};
-#pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(A, PB[qt][k2], O[qt][db]);
+        VA[buf][k2] = u32x4{x[0], x[1], y[0], y[1]};
       }
+    };
+    read_v(0, 0);
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      if (db + 1 < NB) read_v((db + 1) & 1, db + 1);
+#pragma unroll
+      for (int k2 = 0; k2 < NK2; ++k2)
+#pragma unroll
+        for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(VA[db & 1][k2], PB[qt][k2], O[qt][db]);
     }
     // the softmax denominator on the matrix cores: a 16-row block of bf16 ones
     // times P^T sums the same bf16 probabilities that weight V
