@@ -379,7 +379,7 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
 // ---------------------------------------------------------------------------
 struct BackwardPlan {
   size_t bh, gfb, bfb, sfb, pfb, io_bytes, gb_bytes, state_bytes;
-  size_t gfr, bfr, cfr, msnap, lsnap, zsnap, part, total;
+  size_t gfr, bfr, cfr, msnap, lsnap, zsnap, part, carrier, total;
 };
 
 BackwardPlan make_backward_plan(const gdn_desc* d) {
@@ -402,6 +402,7 @@ BackwardPlan make_backward_plan(const gdn_desc* d) {
   b.lsnap = take(b.bh * T * b.sfb);
   b.zsnap = take(b.bh * T * b.sfb);
   b.part = take(b.bh * T * b.pfb);
+  b.carrier = take(b.state_bytes);         // fp32 state / adjoint between sub-range launches
   b.total = off;
   return b;
 }
@@ -649,9 +650,9 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
                               const void* d_out, const float* d_state_out,
                               void* dq, void* dk, void* dv, float* d_gamma, float* d_beta, float* d_state_in,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  gdn_status st = check_backward(d, q, k, v, gamma, beta, state_in, d_out, d_state_out, dq, dk, dv, d_gamma,
-                                 d_beta, d_state_in, workspace, workspace_bytes);
-  if (st != GDN_OK) return st;
+  const gdn_status status = check_backward(d, q, k, v, gamma, beta, state_in, d_out, d_state_out, dq, dk, dv,
+                                           d_gamma, d_beta, d_state_in, workspace, workspace_bytes);
+  if (status != GDN_OK) return status;
   const BackwardPlan b = make_backward_plan(d);
   hipStream_t s = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
@@ -659,47 +660,101 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
   const double c = 1.0 / std::sqrt((double)D * (double)d->S);
   const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
   void* msnap = ws + b.msnap;
+  float* carrier = (float*)(ws + b.carrier);
   hipError_t e = gdn::launch_state_snapshot(state_in, msnap, BH, D, (size_t)(T + 1) * b.sfb, s);
-  // forward replay: G_t and B_t, then M_t into snapshot slots 1..T
+  // forward replay: G_t and B_t for every frame
   gdn::GramArgs ga;
   ga.k = k; ga.v = v; ga.gfr = ws + b.gfr; ga.bfr = ws + b.bfr;
   ga.BH = BH; ga.T = T; ga.S = d->S; ga.t0 = 0; ga.Tc = T;
   ga.kscale = (float)c; ga.kscale2 = (float)(c * c); ga.fp8 = 0;
   if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(D, ga, s); });
-  gdn::StateArgs sa;
-  sa.gfr = ws + b.gfr; sa.bfr = ws + b.bfr; sa.gamma = gamma; sa.beta = beta;
-  sa.state_src = state_in; sa.state_dst = nullptr; sa.snap = msnap;
-  sa.BH = BH; sa.T = T; sa.t0 = 0; sa.Tc = T; sa.Fs = T; sa.f0 = 0; sa.beta_mode = d->beta_mode;
-  sa.snap_Fs = T + 1; sa.snap_f0 = 1;
-  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_STATE, s, [&] { return gdn::launch_state(D, sa, s); });
-  // C_t = ReLU(Q_t)^T dO_t and dQ_t in one pass over Q and dO
-  gdn::CdqArgs ca;
-  ca.q = q; ca.dout = d_out; ca.msnap = msnap; ca.cfr = ws + b.cfr; ca.dq = dq; ca.BH = BH; ca.T = T; ca.S = d->S;
-  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_cdq(D, ca, s); });
-  // adjoint pass
-  gdn::AdjointArgs aa;
-  aa.gfr = ws + b.gfr; aa.bfr = ws + b.bfr; aa.cfr = ws + b.cfr; aa.msnap = msnap;
-  aa.gamma = gamma; aa.beta = beta; aa.dstate_out = d_state_out; aa.dstate_in = d_state_in;
-  aa.lsnap = ws + b.lsnap; aa.part = (float*)(ws + b.part);
-  aa.BH = BH; aa.T = T; aa.beta_mode = d->beta_mode;
-  if (e == hipSuccess)
-    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_adjoint(D, aa, s); });
-  // dV and dK in one pass over K and V (Z_t first, when dK is wanted)
-  if (e == hipSuccess && dk) {
-    gdn::ZmatArgs za;
-    za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
-    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
+
+  // The two serial passes run on a side stream in frame sub-ranges, next to
+  // the HBM-bound passes over the tokens on the caller's stream (as in the
+  // forward): the state replay (M_t snapshots, frames first to last) next to
+  // C_t/dQ of the sub-range before, then the adjoint (Lambda_t, frames last
+  // to first, sub-ranges mirrored so the first one is short) next to
+  // Z_t/dV/dK of the sub-range after.  State and adjoint travel between
+  // launches through the fp32 carrier.
+  int bnd[kStateSplit + 1];
+  const int nsub = split_frames(T, bnd);
+  SideStream* ss = nullptr;
+  hipStream_t st = s;
+  if (e == hipSuccess && nsub > 1) {
+    e = side_stream(&ss);
+    if (e == hipSuccess) {
+      st = ss->stream;
+      e = hipEventRecord(ss->ev[0], s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
+    }
   }
-  if (e == hipSuccess && (dv || dk)) {
-    gdn::DvkArgs da;
-    da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.zsnap = ws + b.zsnap; da.gamma = gamma; da.beta = beta;
-    da.dv = dv; da.dk = dk; da.BH = BH; da.T = T; da.S = d->S; da.beta_mode = d->beta_mode; da.kscale = (float)c;
-    e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_dvdk(D, da, s); });
+  for (int i = 0; i < nsub && e == hipSuccess; ++i) {
+    gdn::StateArgs sa;
+    sa.gfr = ws + b.gfr; sa.bfr = ws + b.bfr; sa.gamma = gamma; sa.beta = beta;
+    sa.state_src = i == 0 ? state_in : carrier;
+    sa.state_dst = i == nsub - 1 ? nullptr : carrier;
+    sa.snap = msnap;
+    sa.BH = BH; sa.T = T; sa.t0 = bnd[i]; sa.Tc = bnd[i + 1] - bnd[i]; sa.Fs = T; sa.f0 = bnd[i];
+    sa.beta_mode = d->beta_mode;
+    sa.snap_Fs = T + 1; sa.snap_f0 = 1 + bnd[i];     // slot t+1 holds M_t
+    e = launch_timed(timed, GDN_KERNEL_STATE, st, [&] { return gdn::launch_state(D, sa, st); });
+    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
+  }
+  // C_t = ReLU(Q_t)^T dO_t and dQ_t in one pass over Q and dO
+  for (int i = 0; i < nsub && e == hipSuccess; ++i) {
+    if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + i], 0);
+    gdn::CdqArgs ca;
+    ca.q = q; ca.dout = d_out; ca.msnap = msnap; ca.cfr = ws + b.cfr; ca.dq = dq; ca.BH = BH; ca.T = T;
+    ca.S = d->S; ca.t0 = bnd[i]; ca.Tc = bnd[i + 1] - bnd[i];
+    if (e == hipSuccess)
+      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_cdq(D, ca, s); });
+  }
+  // the adjoint needs every C_t
+  if (e == hipSuccess && st != s) {
+    e = hipEventRecord(ss->ev[0], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
+  }
+  for (int j = 0; j < nsub && e == hipSuccess; ++j) {
+    gdn::AdjointArgs aa;
+    aa.gfr = ws + b.gfr; aa.bfr = ws + b.bfr; aa.cfr = ws + b.cfr; aa.msnap = msnap;
+    aa.gamma = gamma; aa.beta = beta; aa.dstate_out = d_state_out;
+    aa.lam_src = j == 0 ? nullptr : carrier;
+    aa.lam_dst = j == nsub - 1 ? d_state_in : carrier;
+    aa.lsnap = ws + b.lsnap; aa.part = (float*)(ws + b.part);
+    aa.BH = BH; aa.T = T; aa.beta_mode = d->beta_mode;
+    aa.t_hi = T - bnd[j]; aa.t_lo = T - bnd[j + 1];
+    e = launch_timed(timed, GDN_KERNEL_BACKWARD, st, [&] { return gdn::launch_adjoint(D, aa, st); });
+    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + j], st);
+  }
+  // dV and dK in one pass over K and V (Z_t first, when dK is wanted)
+  for (int j = 0; j < nsub && e == hipSuccess; ++j) {
+    const int t_lo = T - bnd[j + 1], tc = bnd[j + 1] - bnd[j];
+    if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + j], 0);
+    if (e == hipSuccess && dk) {
+      gdn::ZmatArgs za;
+      za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
+      za.t0 = t_lo; za.Tc = tc;
+      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
+    }
+    if (e == hipSuccess && (dv || dk)) {
+      gdn::DvkArgs da;
+      da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.zsnap = ws + b.zsnap; da.gamma = gamma; da.beta = beta;
+      da.dv = dv; da.dk = dk; da.BH = BH; da.T = T; da.S = d->S; da.beta_mode = d->beta_mode;
+      da.kscale = (float)c; da.t0 = t_lo; da.Tc = tc;
+      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_dvdk(D, da, s); });
+    }
   }
   if (e == hipSuccess && (d_gamma || d_beta))
     e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,
                                    d->beta_mode, s);
-  if (e != hipSuccess) return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) {
+    // keep the caller's stream ordered after anything already on the side stream
+    if (ss) {
+      const int last = kStateSplit + 1;
+      if (hipEventRecord(ss->ev[last], ss->stream) == hipSuccess) (void)hipStreamWaitEvent(s, ss->ev[last], 0);
+    }
+    return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
+  }
   return GDN_OK;
 }
 

@@ -65,8 +65,8 @@ __global__ __launch_bounds__(kZWaves * 64) void gdn_zmat_kernel(ZmatArgs a) {
   constexpr int NB = D / 16, NKC = (NB + 1) / 2;
   constexpr size_t SB = (size_t)D * D * 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int fh = blockIdx.x;                       // over BH * T
-  const int bh = fh / a.T, t = fh % a.T;
+  const int fh = blockIdx.x;                       // over BH * Tc
+  const int bh = fh / a.Tc, t = a.t0 + fh % a.Tc;
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   unsigned char* ms = smem;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kDvkWaves * 64, 2) void gdn_dvdk_kernel(DvkArgs a) 
   static_assert((size_t)D * D * 2 <= Sh::lds_bytes, "the Lambda snapshot is staged in the tiles' space");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int T = a.T, S = a.S;
-  const int fh = blockIdx.x, bh = fh / T, t = fh % T;
+  const int fh = blockIdx.x, bh = fh / a.Tc, t = a.t0 + fh % a.Tc;
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
@@ -288,7 +288,7 @@ static hipError_t launch_dvdk_t(const DvkArgs& da, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid((unsigned)(da.BH * da.T)), block(kDvkWaves * 64);
+  const dim3 grid((unsigned)(da.BH * da.Tc)), block(kDvkWaves * 64);
   if (da.beta_mode == 0)
     hipLaunchKernelGGL((gdn_dvdk_kernel<D, false>), grid, block, DvkShape<D>::lds_bytes, stream, da);
   else
@@ -340,7 +340,7 @@ static hipError_t launch_zmat_t(const ZmatArgs& za, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gdn_zmat_kernel<D>), dim3((unsigned)(za.BH * za.T)), dim3(kZWaves * 64), lds, stream, za);
+  hipLaunchKernelGGL((gdn_zmat_kernel<D>), dim3((unsigned)(za.BH * za.Tc)), dim3(kZWaves * 64), lds, stream, za);
   return hipGetLastError();
 }
 

@@ -794,8 +794,8 @@ __device__ __forceinline__ void cdq_wave(const CdqArgs& a, unsigned char* smem, 
 template <int D>
 __global__ __launch_bounds__(GramShape<D>::NW * 64, 2) void gdn_cdq_kernel(CdqArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int fh = blockIdx.x;   // over BH * T
-  const int bh = fh / a.T, t = fh % a.T;
+  const int fh = blockIdx.x;   // over BH * Tc
+  const int bh = fh / a.Tc, t = a.t0 + fh % a.Tc;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   static_for<GramShape<D>::NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
@@ -855,14 +855,20 @@ __device__ __forceinline__ void adjoint_wave(const AdjointArgs& a, unsigned char
     return f32x4{bf16_lo_f32(w[0]), bf16_hi_f32(w[0]), bf16_lo_f32(w[1]), bf16_hi_f32(w[1])};
   };
 
-  // Lambda_{T-1} = dL/dM_final + C_{T-1}
+  // Lambda_{t_hi-1}: carried from the previous launch, or, for the first
+  // launch (t_hi = T), dL/dM_final + C_{T-1}
+  const int t_hi = a.t_hi, Tc = a.t_hi - a.t_lo;
   f32x4 m = {0.f, 0.f, 0.f, 0.f};
-  if (a.dstate_out) {
-    const float* src = a.dstate_out + (size_t)bh * D * D;
+  if (a.lam_src) {
+    const float* src = a.lam_src + (size_t)bh * D * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r] = src[(size_t)(row0 + r) * D + col];
-  }
-  {
+  } else {
+    if (a.dstate_out) {
+      const float* src = a.dstate_out + (size_t)bh * D * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = src[(size_t)(row0 + r) * D + col];
+    }
     const f32x4 c0 = widen4(__builtin_bit_cast(
         u32x2, __builtin_amdgcn_raw_buffer_load_b64(crs, (uint32_t)(T - 1) * (uint32_t)bfb + bbase, 0, 0)));
     m += c0;
@@ -877,10 +883,10 @@ __device__ __forceinline__ void adjoint_wave(const AdjointArgs& a, unsigned char
   u32x4 Gr[kStateRing][LPG];
   u32x2 Cp[kStateRing], Mp[kStateRing], Bf[kStateRing];
   float Ga[kStateRing], Be[kStateRing];
-  // step u handles frame t = T-1-u
+  // step u handles frame t = t_hi-1-u
   auto load_frame = [&](int u, int r) {
-    const int t = T - 1 - u;
-    const bool ok = u < T;
+    const int t = t_hi - 1 - u;
+    const bool ok = u < Tc;
     Ga[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gars, ok ? (uint32_t)t * 4u : kOOB, 0, 0));
     Be[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bers, ok ? (uint32_t)t * 4u : kOOB, 0, 0));
 #pragma unroll
@@ -919,11 +925,11 @@ __device__ __forceinline__ void adjoint_wave(const AdjointArgs& a, unsigned char
   stage_g(0, 0);
   lds_barrier();
 
-  for (int base = 0; base < T; base += kStateRing) {
+  for (int base = 0; base < Tc; base += kStateRing) {
 #pragma unroll
     for (int r = 0; r < kStateRing; ++r) {
-      const int u = base + r, t = T - 1 - u;
-      const bool ok = u < T;
+      const int u = base + r, t = t_hi - 1 - u;
+      const bool ok = u < Tc;
       const unsigned char* xr = xch + (size_t)(r & 1) * (Sh::xch_bytes / 2);
       const unsigned char* gs = gsl + (size_t)(r & 1) * Sh::g_slot;
       // bf16 snapshot of Lambda_t: the copy the waves exchanged
@@ -976,8 +982,8 @@ __device__ __forceinline__ void adjoint_wave(const AdjointArgs& a, unsigned char
       lds_barrier();
     }
   }
-  if (a.dstate_in) {
-    float* dst = a.dstate_in + (size_t)bh * D * D;
+  if (a.lam_dst) {
+    float* dst = a.lam_dst + (size_t)bh * D * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[(size_t)(row0 + r) * D + col] = m[r];
   }
@@ -1083,7 +1089,7 @@ static hipError_t launch_cdq_t(const CdqArgs& ca, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gdn_cdq_kernel<D>), dim3((unsigned)(ca.BH * ca.T)), dim3(GramShape<D>::NW * 64), lds, stream,
+  hipLaunchKernelGGL((gdn_cdq_kernel<D>), dim3((unsigned)(ca.BH * ca.Tc)), dim3(GramShape<D>::NW * 64), lds, stream,
                      ca);
   return hipGetLastError();
 }

@@ -47,6 +47,7 @@ struct CdqArgs {
   void* cfr;                // out: C_t in B's layout, [BH][T]
   void* dq;                 // out: [BH][T][S][D] bf16 or nullptr
   int BH, T, S;
+  int t0, Tc;               // this launch's frames: t0 .. t0+Tc-1
 };
 
 // dV_t and dK_t of the backward in one pass over K_t and V_t.
@@ -61,6 +62,7 @@ struct DvkArgs {
   void* dk;                 // [BH][T][S][D] bf16 or nullptr
   int BH, T, S, beta_mode;
   float kscale;             // 1/sqrt(D*S)
+  int t0, Tc;               // this launch's frames: t0 .. t0+Tc-1
 };
 
 // Block-causal temporal convolution (gdn_tconv.hip).
@@ -93,6 +95,7 @@ struct ZmatArgs {
   const void* lsnap;        // bf16 snapshots of Lambda_t: [BH][T]
   void* zsnap;              // out: bf16 snapshots of Z_t: [BH][T]
   int BH, T;
+  int t0, Tc;               // this launch's frames: t0 .. t0+Tc-1
 };
 
 // Gram pass (bf16 or e4m3 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
@@ -129,11 +132,15 @@ struct AdjointArgs {
   const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
   const float* gamma;       // [BH][T]
   const float* beta;        // [BH][T]
-  const float* dstate_out;  // [BH][D][D] or nullptr
-  float* dstate_in;         // [BH][D][D] or nullptr
+  const float* dstate_out;  // [BH][D][D] or nullptr (used when lam_src is null)
+  const float* lam_src;     // [BH][D][D] Lambda_{t_hi-1} from the previous launch, or nullptr
+                            // (then Lambda_{T-1} = dstate_out + C_{T-1}: t_hi must be T)
+  float* lam_dst;           // [BH][D][D] or nullptr: Lambda_{t_lo-1} (dL/dM_in when t_lo = 0);
+                            // may equal lam_src
   void* lsnap;              // out: bf16 snapshots of Lambda_t, [BH][T] (block layout)
   float* part;              // out: [BH][T][NB*NB][4] per-wave partial sums
   int BH, T, beta_mode;
+  int t_lo, t_hi;           // this launch's frames, run from t_hi-1 down to t_lo
 };
 
 // Kernel launchers (enqueue only).  D in {16, ..., 128}.

@@ -76,6 +76,15 @@ def test_backward_parity(env, B, H, T, S, D, mode):
     run_case(env, B, H, T, S, D, mode)
 
 
+@pytest.mark.parametrize("mode", ["erase", "write"])
+@pytest.mark.parametrize("B,H,T,S,D", [(1, 2, 100, 40, 32), (1, 1, 200, 24, 64)])
+def test_backward_parity_frame_subranges(env, B, H, T, S, D, mode):
+    """Enough frames that the state replay and the adjoint run in several
+    sub-range launches next to the passes over the tokens (state and adjoint
+    carried between launches)."""
+    run_case(env, B, H, T, S, D, mode)
+
+
 def test_backward_without_states_and_partial_outputs(env):
     torch, gdn, wl, go, gb = env
     run_case(env, 1, 2, 4, 96, 32, "erase", with_states=False)
