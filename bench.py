@@ -269,7 +269,10 @@ def attention_variant(gdn, wl, torch, dev, steps: int, warmup: int):
     for key, w in (("clip", wl.ATTN_CLIP_720P), ("stream_chunk", wl.ATTN_STREAM_720P)):
         inp = wl.generate_attn(w, device=dev)
         o = torch.empty_like(inp["q"])
-        call = lambda timed: gdn.attention_forward(inp["q"], inp["k"], inp["v"], w.chunk, out=o, time_kernels=timed)
+        nws = gdn.attention_workspace_size(gdn.make_attn_desc(w.B, w.H, w.Tq, w.Tk, w.S, w.D, w.chunk))
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+        call = lambda timed: gdn.attention_forward(inp["q"], inp["k"], inp["v"], w.chunk, out=o, workspace=ws,
+                                                   time_kernels=timed)
         for _ in range(warmup):
             call(False)
         torch.cuda.synchronize()
@@ -286,10 +289,10 @@ def attention_variant(gdn, wl, torch, dev, steps: int, warmup: int):
         fl = attn_flops(w)
         tfs = fl / (kms * 1e-3) / 1e12
         res[key] = {"workload": w.name, "value": w.tokens / (ms * 1e-3), "unit": "query tokens/s (B*H*Tq*S)",
-                    "ms_per_step": ms, "kernel_ms": kms,
+                    "ms_per_step": ms, "kernel_ms": kms, "key_split_workspace_bytes": nws,
                     "roofline": {"bound": "mfma", "kernel": "attention", "achieved": tfs, "peak": BF16_MFMA_PEAK_TFS,
                                  "unit": "TFLOP/s", "frac": tfs / BF16_MFMA_PEAK_TFS, "flops_per_launch": fl}}
-        del inp, o
+        del inp, o, ws
     return res
 
 

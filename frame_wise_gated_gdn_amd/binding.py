@@ -27,7 +27,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE"
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
            "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
            "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward", "gdn_tconv_forward",
-           "gdn_tconv_check_args", "gdn_attention_forward", "gdn_attention_check_args")
+           "gdn_tconv_check_args", "gdn_attention_forward", "gdn_attention_workspace_size",
+           "gdn_attention_check_args")
 
 
 class GDNError(RuntimeError):
@@ -95,9 +96,11 @@ def lib() -> ctypes.CDLL:
     L.gdn_tconv_check_args.argtypes = [ptd, vp, vp, vp, vp, vp, vp]
     pad = ctypes.POINTER(AttnDesc)
     L.gdn_attention_forward.restype = ctypes.c_int
-    L.gdn_attention_forward.argtypes = [pad, vp, vp, vp, vp, vp]
+    L.gdn_attention_forward.argtypes = [pad, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_attention_workspace_size.restype = sz
+    L.gdn_attention_workspace_size.argtypes = [pad]
     L.gdn_attention_check_args.restype = ctypes.c_int
-    L.gdn_attention_check_args.argtypes = [pad, vp, vp, vp, vp]
+    L.gdn_attention_check_args.argtypes = [pad, vp, vp, vp, vp, vp, sz]
     L.gdn_kernel_times.restype = ctypes.c_int
     L.gdn_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
     if L.gdn_abi_version() != ABI_VERSION:
@@ -330,15 +333,23 @@ def make_attn_desc(B, H, Tq, Tk, S, D, chunk, io_dtype="bf16", flags=0, scale=0.
     return AttnDesc(abi_version, B, H, Tq, Tk, S, D, chunk, dt, flags, scale)
 
 
-def attention_check_args(desc: AttnDesc, q=0, k=0, v=0, o=0) -> int:
+def attention_check_args(desc: AttnDesc, q=0, k=0, v=0, o=0, workspace=0, workspace_bytes=0) -> int:
     """Host-only argument check of gdn_attention_forward on raw addresses."""
     p = lambda a: ctypes.c_void_p(a or None)
-    return int(lib().gdn_attention_check_args(ctypes.byref(desc), p(q), p(k), p(v), p(o)))
+    return int(lib().gdn_attention_check_args(ctypes.byref(desc), p(q), p(k), p(v), p(o), p(workspace),
+                                              workspace_bytes))
 
 
-def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, stream=None, time_kernels=False):
+def attention_workspace_size(desc: AttnDesc) -> int:
+    return int(lib().gdn_attention_workspace_size(ctypes.byref(desc)))
+
+
+def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, workspace=None, stream=None,
+                      time_kernels=False):
     """Block-causal softmax attention: q [B, H, Tq, S, D], k and v [B, H, Tk, S, D]
-    (bf16; the queries are the last Tq key frames).  Returns o like q."""
+    (bf16; the queries are the last Tq key frames).  workspace: None (no key
+    split), "auto" (allocate what gdn_attention_workspace_size asks for) or a
+    uint8 device tensor.  Returns o like q."""
     import torch
     if q.dim() != 5 or k.shape != v.shape or k.dim() != 5:
         raise ValueError("q [B,H,Tq,S,D], k and v [B,H,Tk,S,D]")
@@ -352,8 +363,14 @@ def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, stream=
     if out is None:
         out = torch.empty_like(q)
     desc = make_attn_desc(B, H, Tq, Tk, S, D, chunk, BF16, FLAG_TIME_KERNELS if time_kernels else 0, scale)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be None, "auto" or a tensor')
+        nbytes = attention_workspace_size(desc)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _raise(lib().gdn_attention_forward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(out),
+                                       _addr(workspace), 0 if workspace is None else workspace.numel(),
                                        ctypes.c_void_p(stream)))
     return out

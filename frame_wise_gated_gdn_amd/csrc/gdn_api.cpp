@@ -484,7 +484,7 @@ gdn_status check_tconv(const gdn_tconv_desc* d, const void* x, const float* w, c
   return GDN_OK;
 }
 
-gdn_status check_attn(const gdn_attn_desc* d, const void* q, const void* k, const void* v, const void* o) {
+gdn_status check_attn_desc(const gdn_attn_desc* d) {
   g_last_error.clear();
   if (!d) return fail(GDN_ERR_NULL, "desc is NULL");
   if (d->abi_version != GDN_ABI_VERSION)
@@ -503,13 +503,35 @@ gdn_status check_attn(const gdn_attn_desc* d, const void* q, const void* k, cons
   if (nk * d->D * 2 >= 2147483648.0L || bh * ((long double)d->Tq * d->S / 128 + 1) >= 2147483648.0L)
     return fail(GDN_ERR_SHAPE, "too many tokens per head: Tk*S*D*2 bytes must stay below 2 GiB");
   if (bh * nk * d->D * 2 >= (long double)SIZE_MAX / 4) return fail(GDN_ERR_SHAPE, "tensor sizes overflow");
+  return GDN_OK;
+}
+
+gdn_status check_attn(const gdn_attn_desc* d, const void* q, const void* k, const void* v, const void* o,
+                      const void* workspace, size_t workspace_bytes) {
+  const gdn_status st = check_attn_desc(d);
+  if (st != GDN_OK) return st;
   if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o are required");
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
     return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
   const size_t qb = (size_t)d->B * d->H * d->Tq * d->S * d->D * 2, kb = (size_t)d->B * d->H * d->Tk * d->S * d->D * 2;
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
     return fail(GDN_ERR_ALIAS, "o overlaps q, k or v");
+  if (workspace && workspace_bytes) {
+    if (misaligned(workspace, kAlign)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (overlap(workspace, workspace_bytes, q, qb) || overlap(workspace, workspace_bytes, k, kb) ||
+        overlap(workspace, workspace_bytes, v, kb) || overlap(workspace, workspace_bytes, o, qb))
+      return fail(GDN_ERR_ALIAS, "workspace overlaps q, k, v or o");
+  }
   return GDN_OK;
+}
+
+// Key-split parts for an attention launch on the current device (1 if the
+// device cannot be queried).
+int attn_parts(const gdn_attn_desc* d) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 1;
+  return gdn::attn_split_parts(d->D, d->B * d->H, d->Tq, d->Tk, d->S, d->chunk, cus);
 }
 
 }  // namespace
@@ -759,13 +781,18 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
 }
 
 gdn_status gdn_attention_check_args(const gdn_attn_desc* d, const void* q, const void* k, const void* v,
-                                    const void* o) {
-  return check_attn(d, q, k, v, o);
+                                    const void* o, const void* workspace, size_t workspace_bytes) {
+  return check_attn(d, q, k, v, o, workspace, workspace_bytes);
+}
+
+size_t gdn_attention_workspace_size(const gdn_attn_desc* d) {
+  if (check_attn_desc(d) != GDN_OK) return 0;
+  return gdn::attn_split_bytes(d->D, d->B * d->H, d->Tq, d->S, attn_parts(d));
 }
 
 gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const void* k, const void* v, void* o,
-                                 void* stream) {
-  const gdn_status st = check_attn(d, q, k, v, o);
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const gdn_status st = check_attn(d, q, k, v, o, workspace, workspace_bytes);
   if (st != GDN_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   gdn::AttnArgs aa;
@@ -773,6 +800,22 @@ gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const vo
   aa.BH = d->B * d->H; aa.Tq = d->Tq; aa.Tk = d->Tk; aa.S = d->S; aa.chunk = d->chunk;
   const double scale = d->scale != 0.f ? (double)d->scale : 1.0 / std::sqrt((double)d->D);
   aa.scale_log2 = (float)(scale * 1.4426950408889634);   // log2(e)
+  // split the keys when a workspace for it came in
+  aa.split = 1; aa.split_tiles = 0x7fffffff; aa.part_o = nullptr; aa.part_ml = nullptr;
+  if (workspace) {
+    const int parts = attn_parts(d);
+    const size_t need = gdn::attn_split_bytes(d->D, aa.BH, d->Tq, d->S, parts);
+    if (parts > 1 && workspace_bytes >= need) {
+      const long long Nq = (long long)d->Tq * d->S;
+      const long long fq = (long long)(d->Tk - d->Tq) + (Nq - 1) / d->S;
+      const long long kend = std::min<long long>(d->Tk, (fq / d->chunk + 1) * d->chunk) * d->S;
+      const long long tiles = (kend + 63) / 64;
+      aa.split = parts;
+      aa.split_tiles = (int)((tiles + parts - 1) / parts);
+      aa.part_o = (float*)workspace;
+      aa.part_ml = (float*)((unsigned char*)workspace + (size_t)parts * aa.BH * Nq * d->D * 4);
+    }
+  }
   const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
   const hipError_t e = launch_timed(timed, GDN_KERNEL_ATTN, s, [&] { return gdn::launch_attn(d->D, aa, s); });
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "attention launch: %s", hipGetErrorString(e));

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -88,9 +90,11 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
 
   const int Nq = a.Tq * a.S, Nk = a.Tk * a.S;
   const int nqt = (Nq + kAttnBM - 1) / kAttnBM;
-  // head-major; within a head the longest key ranges start first
-  const int bh = blockIdx.x / nqt;
-  const int qtile = nqt - 1 - (int)(blockIdx.x % nqt);
+  // head-major; within a head the longest key ranges start first; the key
+  // split part is innermost
+  const int part = (int)(blockIdx.x % a.split), unit = (int)(blockIdx.x / a.split);
+  const int bh = unit / nqt;
+  const int qtile = nqt - 1 - unit % nqt;
   const int q0 = qtile * kAttnBM;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
   const uint16_t* qh = (const uint16_t*)a.q + (size_t)bh * Nq * D;
@@ -98,9 +102,13 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   const uint16_t* vh = (const uint16_t*)a.v + (size_t)bh * Nk * D;
   uint16_t* oh = (uint16_t*)a.o + (size_t)bh * Nq * D;
 
-  // the workgroup's key range: up to the block end of its last query
+  // the workgroup's key range: up to the block end of its last query, and of
+  // that the tiles of this key-split part
   const int kend_wg = key_end(min(q0 + kAttnBM, Nq) - 1, a);
   const int ntiles = (kend_wg + kAttnBN - 1) / kAttnBN;
+  const int tb = part * a.split_tiles;
+  const int te = min(ntiles, tb + a.split_tiles);
+  const int nt = max(0, te - tb);
 
   // this lane's queries (one per query tile) and their key ends; lane 0 holds
   // the wave's first query, whose key end is the wave's smallest
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, head_bytes), vrs = make_rsrc(vh, head_bytes);
   auto tile_off = [&](int t, int i) -> uint32_t {
     const int u = tid + kAttnWaves * 64 * i;
-    return (u < UNITS && t < ntiles) ? (uint32_t)t * kAttnBN * D * 2 + 16u * u : kOOB;
+    return (u < UNITS && t < te) ? (uint32_t)t * kAttnBN * D * 2 + 16u * u : kOOB;
   };
   auto load_k = [&](int t) {
 #pragma unroll
@@ -280,29 +288,30 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   // (buffer (t+2)%3, last read for tile t-1) and V tile t+1 (buffer (t+1)%2,
   // last read for tile t-1), then prefetches K t+3 and V t+2.
   const bool grpB = w >= kAttnWaves / 2;
-  load_k(0);
-  load_v(0);
+  load_k(tb);
+  load_v(tb);
   store_k(0);
   store_v(0);
-  load_k(1);
+  load_k(tb + 1);
   store_k(1);
-  load_k(2);
-  load_v(1);
+  load_k(tb + 2);
+  load_v(tb + 1);
   lds_barrier();
-  if (grpB) scores(kbuf_ptr(0));
+  if (grpB && nt > 0) scores(kbuf_ptr(0));
   int kb0 = 0, kb1 = 1, kb2 = 2;          // K buffers of tiles t, t+1, t+2
-  for (int t = 0; t < ntiles; ++t) {
+  for (int it = 0; it < nt; ++it) {
+    const int t = tb + it;
     lds_barrier();
-    const uint16_t* vt = vbuf_ptr(t & 1);
+    const uint16_t* vt = vbuf_ptr(it & 1);
     if (!grpB) {
       scores(kbuf_ptr(kb0));
       softmax_pv(t * kAttnBN, vt);
     } else {
       softmax_pv(t * kAttnBN, vt);
-      if (t + 1 < ntiles) scores(kbuf_ptr(kb1));
+      if (it + 1 < nt) scores(kbuf_ptr(kb1));
     }
-    if (t + 2 < ntiles) store_k(kb2);
-    if (t + 1 < ntiles) store_v((t + 1) & 1);
+    if (it + 2 < nt) store_k(kb2);
+    if (it + 1 < nt) store_v((it + 1) & 1);
     load_k(t + 3);
     load_v(t + 2);
     const int kfree = kb0;
@@ -311,7 +320,22 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
     kb2 = kfree;
   }
 
-  // normalise and store: lane holds O[query 16 qt + n][16 db + 4 g + r]
+  // lane holds O[query 16 qt + n][16 db + 4 g + r]
+  if (a.split > 1) {
+    // partial state of this key range: unnormalised O, running max and sum
+    const size_t prow = ((size_t)part * a.BH + bh) * Nq;
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) {
+      const int qi = q0 + kAttnQW * w + 16 * qt + n;
+      if (qi < Nq) {
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+          *(f32x4*)(a.part_o + (prow + qi) * D + 16 * db + 4 * g) = O[qt][db];
+        if (g == 0) *(f32x2*)(a.part_ml + (prow + qi) * 2) = f32x2{m[qt], L[qt][0]};
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
     const int qi = q0 + kAttnQW * w + 16 * qt + n;
@@ -326,13 +350,44 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   }
 }
 
+// Merge of the key-split partial states, one thread per (head, query, eight
+// head-dim entries): O = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) L_p with
+// M = max_p m_p, in a fixed order of the parts.
+__global__ __launch_bounds__(256) void gdn_attn_merge_kernel(AttnArgs a, int D) {
+  const int Nq = a.Tq * a.S, G8 = D / 8;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)a.BH * Nq * G8) return;
+  const long long row = idx / G8;                     // bh * Nq + qi
+  const int d0 = (int)(idx % G8) * 8;
+  const size_t stride = (size_t)a.BH * Nq;
+  float M = -INFINITY;
+  for (int p = 0; p < a.split; ++p) M = fmaxf(M, a.part_ml[(p * stride + row) * 2]);
+  float den = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.split; ++p) {
+    const f32x2 ml = *(const f32x2*)(a.part_ml + (p * stride + row) * 2);
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+    den = __builtin_fmaf(wgt, ml[1], den);
+    const f32x4* src = (const f32x4*)(a.part_o + (p * stride + row) * D + d0);
+    const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = __builtin_fmaf(wgt, x0[i], acc[i]);
+      acc[4 + i] = __builtin_fmaf(wgt, x1[i], acc[4 + i]);
+    }
+  }
+  const float inv = 1.f / den;
+  *(u32x4*)((uint16_t*)a.o + row * D + d0) =
+      u32x4{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
+            pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv)};
+}
+
 template <int D>
 hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   using Sh = AttnShape<D>;
   const long long Nq = (long long)a.Tq * a.S;
   const long long nqt = (Nq + kAttnBM - 1) / kAttnBM;
-  const long long blocks = nqt * a.BH;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long blocks = nqt * a.BH * a.split;
+  if (blocks > 0x7fffffffLL || a.split < 1) return hipErrorInvalidConfiguration;
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute((const void*)gdn_attn_kernel<D>,
@@ -341,10 +396,43 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
     attr_set = true;
   }
   hipLaunchKernelGGL(gdn_attn_kernel<D>, dim3((unsigned)blocks), dim3(kAttnWaves * 64), Sh::lds_bytes, stream, a);
+  if (a.split > 1) {
+    const long long threads = (long long)a.BH * Nq * (D / 8);
+    hipLaunchKernelGGL(gdn_attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, D);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int attn_split_parts(int D, int BH, int Tq, int Tk, int S, int chunk, int cus) {
+  (void)D;
+  const long long Nq = (long long)Tq * S;
+  const long long units = (Nq + kAttnBM - 1) / kAttnBM * BH;        // workgroups without a split
+  // the longest workgroup's key tiles (the last query's block end)
+  const long long fq = (long long)(Tk - Tq) + (Nq - 1) / S;
+  const long long kend = std::min<long long>(Tk, (fq / chunk + 1) * chunk) * S;
+  const long long tiles = (kend + kAttnBN - 1) / kAttnBN;
+  // one workgroup per CU at a time: pick the part count with the fewest
+  // rounds of workgroups per unit of work, at least 8 key tiles per part
+  int best = 1;
+  double best_cost = (double)((units + cus - 1) / cus);
+  for (int p = 2; p <= 8; ++p) {
+    if (tiles < 8LL * p) break;
+    const double cost = (double)((units * p + cus - 1) / cus) / p;
+    if (cost < 0.9 * best_cost) {
+      best = p;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+size_t attn_split_bytes(int D, int BH, int Tq, int S, int parts) {
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)parts * BH * Tq * S;
+  return rows * D * 4 + ((rows * 2 * 4 + 255) & ~(size_t)255);
+}
 
 hipError_t launch_attn(int D, const AttnArgs& a, hipStream_t stream) {
   switch (D) {

@@ -87,6 +87,12 @@ struct AttnArgs {
   void* o;                  // [BH][Tq*S][D] bf16
   int BH, Tq, Tk, S, chunk;
   float scale_log2;         // softmax scale times log2(e)
+  // key split (split > 1): each workgroup runs split_tiles key tiles and
+  // writes its unnormalised O (fp32) and (max, sum) to the partial arrays;
+  // a merge kernel combines them
+  int split, split_tiles;
+  float* part_o;            // [split][BH][Tq*S][D] fp32
+  float* part_ml;           // [split][BH][Tq*S][2] fp32: running max (log2 units), sum
 };
 
 // Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame) (backward).
@@ -153,6 +159,10 @@ hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream);
 hipError_t launch_dvdk(int D, const DvkArgs& da, hipStream_t stream);
 hipError_t launch_tconv(const TconvArgs& ta, hipStream_t stream);
 hipError_t launch_attn(int D, const AttnArgs& aa, hipStream_t stream);
+// key split chosen for a launch on the current device: how many parts, and
+// the workspace bytes they need (0 when one part is best)
+int attn_split_parts(int D, int BH, int Tq, int Tk, int S, int chunk, int cus);
+size_t attn_split_bytes(int D, int BH, int Tq, int S, int parts);
 hipError_t launch_cdq(int D, const CdqArgs& ca, hipStream_t stream);
 hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
                                  hipStream_t stream);

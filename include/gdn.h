@@ -277,12 +277,26 @@ typedef struct gdn_attn_desc {
   float scale;         /* softmax scale, finite and >= 0; 0 selects 1/sqrt(D) */
 } gdn_attn_desc;
 
+/*
+ * workspace may be NULL.  With at least gdn_attention_workspace_size(d) bytes
+ * (256-byte aligned, overlapping no tensor) the call may split each query
+ * tile's keys over several workgroups and merge their partial softmax states
+ * (fp32) in a second kernel: for launches with few query tiles, such as a
+ * chunk of queries against a long cache.  The split changes the summation
+ * order, so results differ from the unsplit call by rounding only; without a
+ * workspace, queries of the last Tq frames give bitwise the rows of the
+ * whole-sequence call.
+ */
 gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const void* k, const void* v, void* o,
-                                 void* stream);
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for the key split gdn_attention_forward would choose on the
+ * current device; 0 when the shape does not gain from it or d is invalid. */
+size_t gdn_attention_workspace_size(const gdn_attn_desc* d);
 
 /* Host-only argument check of gdn_attention_forward (no device is touched). */
 gdn_status gdn_attention_check_args(const gdn_attn_desc* d, const void* q, const void* k, const void* v,
-                                    const void* o);
+                                    const void* o, const void* workspace, size_t workspace_bytes);
 
 /*
  * Device time of the kernels launched by calls that set GDN_FLAG_TIME_KERNELS

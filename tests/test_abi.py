@@ -342,5 +342,14 @@ def test_attention_dtype_flag_abi_null_align_alias_errors(gdn):
         a["o"] = a[other] + 16
         assert gdn.attention_check_args(d, **a) == 5, other
     import ctypes
-    assert gdn.lib().gdn_attention_forward(ctypes.byref(d), None, None, None, None, None) == 1
-    assert gdn.lib().gdn_attention_check_args(None, None, None, None, None) == 1
+    assert gdn.lib().gdn_attention_forward(ctypes.byref(d), None, None, None, None, None, 0, None) == 1
+    assert gdn.lib().gdn_attention_check_args(None, None, None, None, None, None, 0) == 1
+    a = at_args()
+    a["workspace"], a["workspace_bytes"] = addrs(5)[4], 1 << 20
+    assert gdn.attention_check_args(d, **a) == 0
+    a["workspace"] += 16
+    assert gdn.attention_check_args(d, **a) == 4
+    a["workspace"] = a["o"] + 256
+    assert gdn.attention_check_args(d, **a) == 5
+    # no device here: the size query falls back to no split; invalid descriptors give 0
+    assert gdn.attention_workspace_size(gdn.make_attn_desc(1, 1, 2, 3, 8, 24, 1)) == 0

@@ -124,3 +124,50 @@ def test_attention_720p_clip_sampled_queries(env):
             ref = (p @ v[:end]) / p.sum()
             err = np.abs(got[i] - ref).max()
             assert err <= bound, (h, i, err, bound)
+
+
+@pytest.mark.parametrize("B,H,Tq,Tk,S,D,chunk", [(1, 2, 1, 40, 64, 64, 4), (1, 1, 2, 30, 70, 112, 2),
+                                                 (2, 1, 1, 25, 100, 128, 1)])
+def test_attention_key_split_parity(env, B, H, Tq, Tk, S, D, chunk):
+    """With a workspace, launches with few query tiles split the keys over
+    workgroups and merge the partial (max, sum, O) states."""
+    torch, gdn, wl, ao = env
+    desc = gdn.make_attn_desc(B, H, Tq, Tk, S, D, chunk)
+    assert gdn.attention_workspace_size(desc) > 0, "this shape should split its keys"
+    w = wl.AttnWorkload("ks", B, H, Tq, Tk, S, D, chunk)
+    inp = {k_: v_.cuda() for k_, v_ in wl.generate_attn(w, seed=Tk).items()}
+    split = gdn.attention_forward(inp["q"], inp["k"], inp["v"], chunk, workspace="auto")
+    whole = gdn.attention_forward(inp["q"], inp["k"], inp["v"], chunk)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            check_head(f64(split[b, h]).reshape(-1, D), f64(inp["q"][b, h]).reshape(-1, D),
+                       f64(inp["k"][b, h]).reshape(-1, D), f64(inp["v"][b, h]).reshape(-1, D), S, chunk, ao)
+    d = f64(split) - f64(whole)
+    assert np.linalg.norm(d) / np.linalg.norm(f64(whole)) < 1e-2
+
+
+def test_attention_720p_stream_chunk_split_sampled(env):
+    """One 4-frame chunk of queries against the 81-frame cache with the key
+    split; oracle rows of sampled heads."""
+    torch, gdn, wl, ao = env
+    w = wl.ATTN_STREAM_720P
+    inp = wl.generate_attn(w, device="cuda")
+    assert gdn.attention_workspace_size(gdn.make_attn_desc(w.B, w.H, w.Tq, w.Tk, w.S, w.D, w.chunk)) > 0
+    o = gdn.attention_forward(inp["q"], inp["k"], inp["v"], w.chunk, workspace="auto")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all())
+    S, D = w.S, w.D
+    for h in (0, 11, 19):
+        q = f64(inp["q"][0, h]).reshape(-1, D)
+        k = f64(inp["k"][0, h]).reshape(-1, D)
+        v = f64(inp["v"][0, h]).reshape(-1, D)
+        got = f64(o[0, h]).reshape(-1, D)
+        bound = 2.0 ** -7 * np.abs(v).max() + 1e-6
+        for i in (0, 1, S - 1, S, 2 * S + 5, 4 * S - 1):
+            f = (w.Tk - w.Tq) + i // S
+            end = min(w.Tk, (f // w.chunk + 1) * w.chunk) * S
+            s = (k[:end] @ q[i]) / np.sqrt(D)
+            p = np.exp(s - s.max())
+            ref = (p @ v[:end]) / p.sum()
+            assert np.abs(got[i] - ref).max() <= bound, (h, i)
