@@ -77,8 +77,9 @@ __device__ __forceinline__ float wave_max4(float x) {
 
 // Keys visible to a query token qi of the query sequence (last Tq frames).
 __device__ __forceinline__ int key_end(int qi, const AttnArgs& a) {
-  const int fq = (a.Tk - a.Tq) + qi / a.S;
-  return min(a.Tk, (fq / a.chunk + 1) * a.chunk) * a.S;
+  const long long fq = (long long)(a.Tk - a.Tq) + qi / a.S;
+  const long long end = (fq / a.chunk + 1) * (long long)a.chunk;   // any chunk up to INT_MAX
+  return (int)(end < a.Tk ? end : (long long)a.Tk) * a.S;
 }
 
 template <int D>

@@ -64,6 +64,17 @@ def test_attention_parity(env, B, H, Tq, Tk, S, D, chunk):
     print(f"B{B} H{H} Tq{Tq} Tk{Tk} S{S} D{D} chunk{chunk}: rel {worst:.2e}")
 
 
+def test_attention_huge_chunk_is_bidirectional(env):
+    """A block length near the int32 limit means one block: full attention."""
+    torch, gdn, wl, ao = env
+    w = wl.AttnWorkload("hc", 1, 1, 3, 3, 40, 64, 1)
+    inp = {k_: v_.cuda() for k_, v_ in wl.generate_attn(w, seed=6).items()}
+    big = gdn.attention_forward(inp["q"], inp["k"], inp["v"], 2 ** 31 - 1)
+    full = gdn.attention_forward(inp["q"], inp["k"], inp["v"], 3)
+    torch.cuda.synchronize()
+    assert torch.equal(big, full)
+
+
 def test_attention_explicit_scale(env):
     torch, gdn, wl, ao = env
     w = wl.AttnWorkload("s", 1, 1, 3, 3, 40, 64, 1)
