@@ -87,8 +87,10 @@ gdn_status check_desc(const gdn_desc* d) {
   if (d->D % 16 != 0 || d->D > 128)
     return fail(GDN_ERR_UNSUPPORTED, "D=%d: supported head dims are 16, 32, ..., 128", d->D);
   const long double per_head = (long double)d->T * d->S * d->D;
-  if (per_head >= 2147483648.0L)
-    return fail(GDN_ERR_SHAPE, "T*S*D = %.0Lf exceeds the per-head 32-bit limit", per_head);
+  const int esz = d->io_dtype == GDN_F32 ? 4 : d->io_dtype == GDN_BF16 ? 2 : 1;
+  if (per_head * esz >= 2147483648.0L)
+    return fail(GDN_ERR_SHAPE, "T*S*D*%d = %.0Lf bytes: one head's q, k, v or o must stay below 2 GiB", esz,
+                per_head * esz);
   const long double bh = (long double)d->B * d->H;
   if (bh * d->T >= 2147483648.0L || bh * d->D * d->D >= 2147483648.0L * 8)
     return fail(GDN_ERR_SHAPE, "B*H too large for these T and D");

@@ -259,9 +259,13 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
   const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * 2u;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc((const uint16_t*)a.k + (size_t)bh * T * S * D, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const uint16_t*)a.v + (size_t)bh * T * S * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t snaprs = make_rsrc(a.snap, (uint32_t)((size_t)a.units / NB * a.Tc * D * D * 2));
+  // snapshots and norm partials of this head only: byte offsets within a
+  // head stay far below the out-of-range marker whatever B*H is
+  const __amdgpu_buffer_rsrc_t snaprs =
+      make_rsrc((unsigned char*)a.snap + (size_t)bh * a.Tc * D * D * 2, (uint32_t)((size_t)a.Tc * D * D * 2));
   const __amdgpu_buffer_rsrc_t normrs =
-      make_rsrc(a.norm_part, a.norm_part ? (uint32_t)((size_t)a.units * a.Tc * 4) : 0u);
+      make_rsrc(a.norm_part ? (unsigned char*)a.norm_part + (size_t)bh * a.Tc * NB * 4 : nullptr,
+                a.norm_part ? (uint32_t)((size_t)a.Tc * NB * 4) : 0u);
 
   for (int x = tid; x < a.Tc; x += kThreads)
     gb[x] = make_float2(a.gamma[(size_t)bh * T + a.t0 + x], a.beta[(size_t)bh * T + a.t0 + x]);
@@ -406,8 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
     for (int i = 0; i < 4; ++i) Mn[i] = gbt.x * Mown[i] - upd * sum[i];
     if (w < NB) Mown = Mn;
     const u32x2 pk = {pack_bf16(Mn[0], Mn[1]), pack_bf16(Mn[2], Mn[3])};
-    const uint32_t snap_off =
-        (uint32_t)((size_t)(bh * a.Tc + tl) * D * D * 2 + (size_t)((jt * NB + ob) * 64 + l) * 8);
+    const uint32_t snap_off = (uint32_t)((size_t)tl * D * D * 2 + (size_t)((jt * NB + ob) * 64 + l) * 8);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), snaprs, w < NB ? snap_off : kOOB, 0, 0);
     const float s1 = pred_scale(tl + 1 < a.Tc ? tl + 1 : tl);
     const u32x2 pm = {pack_bf16(s1 * Mn[0], s1 * Mn[1]), pack_bf16(s1 * Mn[2], s1 * Mn[3])};
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_recur_bf16_kernel(RecurArgs a
     if (a.norm_part) {
       float sq = 0.f;
       for (int kb = 0; kb < NB; ++kb) sq += normp[kb];
-      const uint32_t noff = (uint32_t)((((size_t)bh * a.Tc + tl) * NB + jt) * 4);
+      const uint32_t noff = (uint32_t)(((size_t)tl * NB + jt) * 4);
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sq), normrs, tid == 0 ? noff : kOOB, 0, 0);
     }
 #pragma unroll

@@ -41,8 +41,9 @@
  *     may not partially overlap it.
  *   - Alignment: q, k, v, o 16-byte aligned; gamma, beta, states, norms 4-byte
  *     aligned; workspace 256-byte aligned.
- *   - Shapes: B, H, T, S >= 1; D in {16, 32, 48, ..., 128}; the element counts
- *     must fit the kernels' 32-bit per-head indexing (T*S*D < 2^31).
+ *   - Shapes: B, H, T, S >= 1; D in {16, 32, 48, ..., 128}; one head's q (and
+ *     k, v, o) must stay below 2 GiB, T*S*D*element_size < 2^31 (the kernels
+ *     address a head with 32-bit byte offsets).
  *   - Determinism: results do not depend on the workspace size or on how the
  *     frames are split across calls; the same inputs and flags give the same
  *     bits.

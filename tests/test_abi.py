@@ -92,6 +92,20 @@ def test_shape_errors(gdn, shape, code):
     assert gdn.workspace_size(d) == 0
 
 
+def test_per_head_size_limit(gdn):
+    """One head's tensor must stay below 2 GiB in bytes (32-bit byte offsets)."""
+    def status(*shape):
+        d = gdn.make_desc(*shape)
+        return gdn.check_args(d, **args_ok(gdn, d))
+    assert status(1, 1, 1023, 8192, 128, "bf16") == 0
+    assert status(1, 1, 1024, 8192, 128, "bf16") == 2
+    assert b"2 GiB" in gdn.lib().gdn_last_error()
+    assert status(1, 1, 1023, 8192, 128, "f32") == 2
+    assert status(1, 1, 511, 8192, 128, "f32") == 0
+    assert status(1, 1, 2047, 8192, 128, "fp8") == 0
+    assert status(1, 1, 2048, 8192, 128, "fp8") == 2
+
+
 @pytest.mark.parametrize("field", ["q", "k", "v", "gamma", "beta", "o"])
 def test_null_errors(gdn, field):
     d = gdn.make_desc(1, 2, 3, 16, 16, "bf16")

@@ -172,6 +172,21 @@ def test_gram_and_direct_paths_agree(env):
         assert rel(to_f64(torch, x), to_f64(torch, y)) < 1e-2
 
 
+def test_direct_path_many_heads_past_2gib_of_snapshots(env):
+    """The single-pass recurrence with 72 heads of 1024 frames at D = 128 keeps
+    2.4 GB of bf16 state snapshots: head 64's start exactly at byte 2^31.
+    Every head addresses only its own snapshots, so heads past that point are
+    exact too (the out-of-range marker of masked stores is 2^31)."""
+    torch, gdn, wl, go = env
+    w = wl.Workload("direct-72h", 1, 72, 1024, 16, 128, gamma=(0.9, 1.0), beta=(0.0, 1.0))
+    inp = wl.generate(w, device="cuda")
+    out, st, norms = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True,
+                                       path="direct")
+    torch.cuda.synchronize()
+    check(env, inp, out, st, run_oracle(env, inp, heads=[(0, 0), (0, 63), (0, 64), (0, 71)], want_norms=True),
+          TOL["bf16"], norms)
+
+
 # ------------------------------------------------------------------ streaming
 @pytest.mark.parametrize("path", ["auto", "direct"])
 def test_chunked_rollout_equals_one_shot_bitwise(env, path):
