@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int u = tid + kAttnWaves * 64 * i;
-    lds_u[i] = 8 * u + 8 * (u / UPR);
+    lds_u[i] = (u / UPR) * RS + 8 * (u % UPR);
   }
   // buffer loads: a unit past the head's keys (or past the last tile) reads zeros
   const uint32_t head_bytes = (uint32_t)Nk * D * 2;
