@@ -809,11 +809,8 @@ gdn_status gdn_attention_forward(const gdn_attn_desc* d, const void* q, const vo
     const size_t need = gdn::attn_split_bytes(d->D, aa.BH, d->Tq, d->S, parts);
     if (parts > 1 && workspace_bytes >= need) {
       const long long Nq = (long long)d->Tq * d->S;
-      const long long fq = (long long)(d->Tk - d->Tq) + (Nq - 1) / d->S;
-      const long long kend = std::min<long long>(d->Tk, (fq / d->chunk + 1) * d->chunk) * d->S;
-      const long long tiles = (kend + 63) / 64;
       aa.split = parts;
-      aa.split_tiles = (int)((tiles + parts - 1) / parts);
+      aa.split_tiles = gdn::attn_split_tiles(d->Tq, d->Tk, d->S, d->chunk, parts);
       aa.part_o = (float*)workspace;
       aa.part_ml = (float*)((unsigned char*)workspace + (size_t)parts * aa.BH * Nq * d->D * 4);
     }

@@ -406,14 +406,19 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Key tiles of the longest workgroup of a launch (its last query's block end).
+static long long attn_max_tiles(int Tq, int Tk, int S, int chunk) {
+  const long long Nq = (long long)Tq * S;
+  const long long fq = (long long)(Tk - Tq) + (Nq - 1) / S;
+  const long long kend = std::min<long long>(Tk, (fq / chunk + 1) * (long long)chunk) * S;
+  return (kend + kAttnBN - 1) / kAttnBN;
+}
+
 int attn_split_parts(int D, int BH, int Tq, int Tk, int S, int chunk, int cus) {
   (void)D;
   const long long Nq = (long long)Tq * S;
   const long long units = (Nq + kAttnBM - 1) / kAttnBM * BH;        // workgroups without a split
-  // the longest workgroup's key tiles (the last query's block end)
-  const long long fq = (long long)(Tk - Tq) + (Nq - 1) / S;
-  const long long kend = std::min<long long>(Tk, (fq / chunk + 1) * chunk) * S;
-  const long long tiles = (kend + kAttnBN - 1) / kAttnBN;
+  const long long tiles = attn_max_tiles(Tq, Tk, S, chunk);
   // one workgroup per CU at a time: pick the part count with the fewest
   // rounds of workgroups per unit of work, at least 8 key tiles per part
   int best = 1;
@@ -427,6 +432,11 @@ int attn_split_parts(int D, int BH, int Tq, int Tk, int S, int chunk, int cus) {
     }
   }
   return best;
+}
+
+int attn_split_tiles(int Tq, int Tk, int S, int chunk, int parts) {
+  const long long tiles = attn_max_tiles(Tq, Tk, S, chunk);
+  return (int)((tiles + parts - 1) / parts);
 }
 
 size_t attn_split_bytes(int D, int BH, int Tq, int S, int parts) {

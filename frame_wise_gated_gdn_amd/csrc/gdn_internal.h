@@ -163,6 +163,7 @@ hipError_t launch_attn(int D, const AttnArgs& aa, hipStream_t stream);
 // the workspace bytes they need (0 when one part is best)
 int attn_split_parts(int D, int BH, int Tq, int Tk, int S, int chunk, int cus);
 size_t attn_split_bytes(int D, int BH, int Tq, int S, int parts);
+int attn_split_tiles(int Tq, int Tk, int S, int chunk, int parts);   // key tiles per part
 hipError_t launch_cdq(int D, const CdqArgs& ca, hipStream_t stream);
 hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
                                  hipStream_t stream);
