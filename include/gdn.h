@@ -1,5 +1,8 @@
 /*
- * gdn.h -- C ABI of the MI355X (gfx950) frame-wise Gated DeltaNet forward path.
+ * gdn.h -- C ABI of the MI355X (gfx950) frame-wise Gated DeltaNet: the forward
+ * (whole sequence and streaming chunks), its backward, and the two companion
+ * operations of the hybrid model (the block-causal temporal convolution of the
+ * streaming FFN, the block-causal softmax attention blocks).
  *
  * What is computed.  SANA-WM's frame-wise GDN ("NVIDIA Apresenta SANA-WM ...",
  * acheiumaia.com.br, section "1. Atencao Linear Hibrida com Gated DeltaNet
