@@ -11,7 +11,8 @@ frames per gdn_frame_step call, its per-chunk latency and back-to-back rate.
 A `variants` field times the same 720p-shaped step with OCP E4M3 Q, K, V, O
 (the low-precision I/O variant, 4*D bytes per token-head), and a `backward`
 field times gdn_frame_backward on the bf16 inputs (14*D algorithmic bytes per
-token-head).  A `temporal_conv` field times gdn_tconv_forward, the block-causal
+token-head), and a `training_step` field the pair gdn_frame_forward_train +
+gdn_frame_backward_saved (the backward without the forward replay).  A `temporal_conv` field times gdn_tconv_forward, the block-causal
 temporal convolution of the streaming FFN, on a 720p-shaped activation
 (B1 T961 S880 C2240, blocks of 4 frames, bf16: 4*C algorithmic bytes per
 token), plus one block's call latency.  An `attention` field times
@@ -296,6 +297,53 @@ def attention_variant(gdn, wl, torch, dev, steps: int, warmup: int):
     return res
 
 
+def training_variant(gdn, wl, torch, dev, inp, steps: int, warmup: int):
+    """One training step on the 720p-shaped inputs: gdn_frame_forward_train
+    (the forward that keeps G_t, B_t and the state snapshots) then
+    gdn_frame_backward_saved (no replay).  Also the saved backward alone, with
+    its roofline on 14*D algorithmic bytes per token-head."""
+    w = wl.MINUTE_720P
+    g = torch.Generator(device=dev).manual_seed(11)
+    d_out = torch.randn((w.B, w.H, w.T, w.S, w.D), generator=g, device=dev).to(torch.bfloat16)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, "bf16", w.beta_mode)
+    saved = torch.empty(gdn.saved_size(desc), dtype=torch.uint8, device=dev)
+    ws = torch.empty(gdn.backward_saved_workspace_size(desc), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(inp["q"])
+    args = (inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    fwd = lambda timed: gdn.frame_forward_train(*args, beta_mode=w.beta_mode, out=o, saved=saved,
+                                                time_kernels=timed)
+    bwd = lambda timed: gdn.frame_backward_saved(*args, saved, d_out, beta_mode=w.beta_mode, workspace=ws,
+                                                 time_kernels=timed)
+    for _ in range(warmup):
+        fwd(False)
+        bwd(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd(False)
+        bwd(False)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bwd(False)
+    torch.cuda.synchronize()
+    ms_bwd = (time.perf_counter() - t0) * 1e3 / steps
+    gdn.kernel_times(reset=True)
+    for _ in range(steps):
+        bwd(True)
+    torch.cuda.synchronize()
+    kms = {name: t / steps for name, (t, n) in gdn.kernel_times(reset=True).items() if n > 0}
+    path_bytes = w.B * w.H * w.T * w.S * 14 * w.D
+    gbs = path_bytes / (ms_bwd * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_training_step": ms_step,
+            "training_tokens_per_s": w.tokens / (ms_step * 1e-3),
+            "backward_saved": {"ms": ms_bwd, "kernels_ms": kms,
+                               "path_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                                 "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                                 "algorithmic_bytes_per_step": path_bytes}}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +460,7 @@ def main():
         rec["streaming"] = streaming_latency(gdn, wl, torch, dev, args.stream_reps)
     if args.backward and args.path == "auto":
         rec["backward"] = backward_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
+        rec["training_step"] = training_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
     if args.tconv:
         rec["temporal_conv"] = tconv_variant(gdn, wl, torch, dev, args.steps, args.warmup)
     if args.attention:

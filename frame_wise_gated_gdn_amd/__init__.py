@@ -9,11 +9,14 @@ device memory and streams.
 """
 from .binding import (ABI_VERSION, BF16, ERASE, F32, FP8, WRITE, Desc, GDNError, attention_check_args,  # noqa: F401
                       attention_forward, attention_workspace_size, check_args, make_attn_desc,
-                      backward_workspace_size, frame_backward, frame_forward, frame_step, kernel_times, lib,
+                      backward_saved_workspace_size, backward_workspace_size, frame_backward,
+                      frame_backward_saved, frame_forward, frame_forward_train, frame_step, kernel_times, lib,
+                      saved_size,
                       make_desc, make_tconv_desc, tconv_check_args, tconv_forward, workspace_min_size,
                       workspace_size)
 
-__all__ = ["frame_forward", "frame_step", "frame_backward", "backward_workspace_size", "tconv_forward",
+__all__ = ["frame_forward", "frame_step", "frame_backward", "backward_workspace_size", "frame_forward_train",
+           "frame_backward_saved", "saved_size", "backward_saved_workspace_size", "tconv_forward",
            "attention_forward", "attention_check_args", "attention_workspace_size", "make_attn_desc",
            "GDNError", "workspace_size", "workspace_min_size", "kernel_times", "check_args", "tconv_check_args",
            "make_desc", "make_tconv_desc", "lib"]

@@ -26,7 +26,9 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE"
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
            "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
-           "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward", "gdn_tconv_forward",
+           "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward", "gdn_saved_size",
+           "gdn_backward_saved_workspace_size", "gdn_frame_forward_train", "gdn_frame_backward_saved",
+           "gdn_tconv_forward",
            "gdn_tconv_check_args", "gdn_attention_forward", "gdn_attention_workspace_size",
            "gdn_attention_check_args")
 
@@ -89,6 +91,13 @@ def lib() -> ctypes.CDLL:
     L.gdn_backward_workspace_size.argtypes = [pdesc]
     L.gdn_frame_backward.restype = ctypes.c_int
     L.gdn_frame_backward.argtypes = [pdesc] + [vp] * 15 + [sz, vp]
+    for name in ("gdn_saved_size", "gdn_backward_saved_workspace_size"):
+        getattr(L, name).restype = sz
+        getattr(L, name).argtypes = [pdesc]
+    L.gdn_frame_forward_train.restype = ctypes.c_int
+    L.gdn_frame_forward_train.argtypes = [pdesc] + [vp] * 10 + [sz, vp]
+    L.gdn_frame_backward_saved.restype = ctypes.c_int
+    L.gdn_frame_backward_saved.argtypes = [pdesc] + [vp] * 6 + [sz] + [vp] * 9 + [sz, vp]
     ptd = ctypes.POINTER(TconvDesc)
     L.gdn_tconv_forward.restype = ctypes.c_int
     L.gdn_tconv_forward.argtypes = [ptd, vp, vp, vp, vp, vp, vp, vp]
@@ -278,6 +287,85 @@ def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, be
                                   _addr(out["dk"]), _addr(out["dv"]), _addr(out["dgamma"]), _addr(out["dbeta"]),
                                   _addr(out["dstate"]), _addr(workspace), workspace.numel(),
                                   ctypes.c_void_p(stream))
+    _raise(st)
+    return {k_: v_ for k_, v_ in out.items() if v_ is not None}
+
+
+def saved_size(desc: Desc) -> int:
+    return int(lib().gdn_saved_size(ctypes.byref(desc)))
+
+
+def backward_saved_workspace_size(desc: Desc) -> int:
+    return int(lib().gdn_backward_saved_workspace_size(ctypes.byref(desc)))
+
+
+def frame_forward_train(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None, state_out=None,
+                        norms=None, want_state=True, want_norms=False, saved=None, stream=None,
+                        time_kernels=False):
+    """frame_forward that also keeps, in `saved` (a uint8 device tensor of
+    saved_size bytes, allocated when None), what frame_backward_saved needs.
+    bf16, T <= 1024.  Returns (o, state_out, norms, saved)."""
+    import torch
+    B, H, T, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("beta", beta)):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise TypeError("frame_forward_train takes bfloat16 q, k and v")
+    desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
+    if saved is None:
+        n = saved_size(desc)
+        if n == 0:
+            raise GDNError(6, "frame_forward_train: unsupported shape (bf16 only, T <= 1024)")
+        saved = torch.empty(n, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    if norms is None and want_norms:
+        norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _raise(lib().gdn_frame_forward_train(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
+                                         _addr(beta), _addr(state), _addr(out), _addr(state_out), _addr(norms),
+                                         _addr(saved), saved.numel(), ctypes.c_void_p(stream)))
+    return out, state_out, norms, saved
+
+
+def frame_backward_saved(q, k, v, gamma, beta, saved, d_out, d_state_out=None, beta_mode="erase",
+                         want=("dq", "dk", "dv", "dgamma", "dbeta", "dstate"), workspace=None, stream=None,
+                         time_kernels=False):
+    """frame_backward from the `saved` buffer of frame_forward_train (no replay
+    of the forward).  Returns the same dict as frame_backward."""
+    import torch
+    B, H, T, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_out", d_out), ("gamma", gamma), ("beta", beta)):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16 or any(t.dtype != torch.bfloat16 for t in (k, v, d_out)):
+        raise TypeError("frame_backward_saved takes bfloat16 q, k, v and d_out")
+    desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
+    if workspace is None:
+        n = backward_saved_workspace_size(desc)
+        if n == 0:
+            raise GDNError(6, "frame_backward_saved: unsupported shape (bf16 only, T <= 1024)")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    out = {}
+    like = lambda: torch.empty_like(q)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    out["dq"] = like() if "dq" in want else None
+    out["dk"] = like() if "dk" in want else None
+    out["dv"] = like() if "dv" in want else None
+    out["dgamma"] = f32(B, H, T) if "dgamma" in want else None
+    out["dbeta"] = f32(B, H, T) if "dbeta" in want else None
+    out["dstate"] = f32(B, H, D, D) if "dstate" in want else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().gdn_frame_backward_saved(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
+                                        _addr(beta), _addr(saved), saved.numel(), _addr(d_out),
+                                        _addr(d_state_out), _addr(out["dq"]), _addr(out["dk"]), _addr(out["dv"]),
+                                        _addr(out["dgamma"]), _addr(out["dbeta"]), _addr(out["dstate"]),
+                                        _addr(workspace), workspace.numel(), ctypes.c_void_p(stream))
     _raise(st)
     return {k_: v_ for k_, v_ in out.items() if v_ is not None}
 

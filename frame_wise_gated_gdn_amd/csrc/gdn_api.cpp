@@ -384,7 +384,30 @@ struct BackwardPlan {
   size_t gfr, bfr, cfr, msnap, lsnap, zsnap, part, carrier, total;
 };
 
-BackwardPlan make_backward_plan(const gdn_desc* d) {
+// Layout of the saved buffer of a training forward: G_t and B_t of every
+// frame (the gram pass's staging layout), bf16 state snapshots in T+1 slots
+// (slot 0 the initial state, slot t+1 the state after frame t), and an fp32
+// state carrier.
+struct SavedPlan {
+  size_t gfr, bfr, msnap, carrier, total;
+};
+
+SavedPlan make_saved_plan(const gdn_desc* d) {
+  SavedPlan p;
+  const size_t T = (size_t)d->T, D = (size_t)d->D, bh = (size_t)d->B * (size_t)d->H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t r = off; off += round_up(bytes); return r; };
+  p.gfr = take(bh * T * gdn::gram_frame_bytes(d->D));
+  p.bfr = take(bh * T * gdn::input_frame_bytes(d->D));
+  p.msnap = take(bh * (T + 1) * D * D * 2);
+  p.carrier = take(bh * D * D * 4);
+  p.total = off;
+  return p;
+}
+
+// Workspace of the backward.  With a saved forward (`saved`), G_t, B_t and the
+// state snapshots come from it and the workspace holds the rest.
+BackwardPlan make_backward_plan(const gdn_desc* d, bool saved = false) {
   BackwardPlan b;
   const size_t T = (size_t)d->T, D = (size_t)d->D, nb = D / 16;
   b.bh = (size_t)d->B * (size_t)d->H;
@@ -397,10 +420,10 @@ BackwardPlan make_backward_plan(const gdn_desc* d) {
   b.state_bytes = b.bh * D * D * 4;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t r = off; off += round_up(bytes); return r; };
-  b.gfr = take(b.bh * T * b.gfb);
-  b.bfr = take(b.bh * T * b.bfb);
+  b.gfr = saved ? 0 : take(b.bh * T * b.gfb);
+  b.bfr = saved ? 0 : take(b.bh * T * b.bfb);
   b.cfr = take(b.bh * T * b.bfb);
-  b.msnap = take(b.bh * (T + 1) * b.sfb);
+  b.msnap = saved ? 0 : take(b.bh * (T + 1) * b.sfb);
   b.lsnap = take(b.bh * T * b.sfb);
   b.zsnap = take(b.bh * T * b.sfb);
   b.part = take(b.bh * T * b.pfb);
@@ -413,7 +436,8 @@ gdn_status check_backward(const gdn_desc* d, const void* q, const void* k, const
                           const float* beta, const float* state_in, const void* d_out, const float* d_state_out,
                           const void* dq, const void* dk, const void* dv, const float* d_gamma,
                           const float* d_beta, const float* d_state_in, const void* workspace,
-                          size_t workspace_bytes) {
+                          size_t workspace_bytes, const void* saved = nullptr, size_t saved_bytes = 0,
+                          bool saved_mode = false) {
   g_last_error.clear();
   gdn_status st = check_desc(d);
   if (st != GDN_OK) return st;
@@ -424,9 +448,16 @@ gdn_status check_backward(const gdn_desc* d, const void* q, const void* k, const
   if (!q || !k || !v || !d_out) return fail(GDN_ERR_NULL, "q, k, v and d_out are required");
   if (!gamma || !beta) return fail(GDN_ERR_NULL, "gamma and beta are required");
   if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is required (gdn_backward_workspace_size)");
-  const BackwardPlan b = make_backward_plan(d);
+  const BackwardPlan b = make_backward_plan(d, saved_mode);
   if (workspace_bytes < b.total)
     return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes < required %zu", workspace_bytes, b.total);
+  if (saved_mode) {
+    if (!saved) return fail(GDN_ERR_NULL, "saved is required (the buffer of gdn_frame_forward_train)");
+    const size_t need = make_saved_plan(d).total;
+    if (saved_bytes < need)
+      return fail(GDN_ERR_WORKSPACE, "saved buffer of %zu bytes < required %zu", saved_bytes, need);
+    if (misaligned(saved, kAlign)) return fail(GDN_ERR_ALIGN, "saved must be 256-byte aligned");
+  }
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(d_out, 16) || misaligned(dq, 16) ||
       misaligned(dk, 16) || misaligned(dv, 16))
     return fail(GDN_ERR_ALIGN, "q, k, v, d_out, dq, dk and dv must be 16-byte aligned");
@@ -437,7 +468,8 @@ gdn_status check_backward(const gdn_desc* d, const void* q, const void* k, const
   struct Buf { const void* p; size_t n; const char* name; };
   const Buf ins[] = {{q, b.io_bytes, "q"}, {k, b.io_bytes, "k"}, {v, b.io_bytes, "v"},
                      {d_out, b.io_bytes, "d_out"}, {gamma, b.gb_bytes, "gamma"}, {beta, b.gb_bytes, "beta"},
-                     {state_in, b.state_bytes, "state_in"}, {d_state_out, b.state_bytes, "d_state_out"}};
+                     {state_in, b.state_bytes, "state_in"}, {d_state_out, b.state_bytes, "d_state_out"},
+                     {saved, saved_bytes, "saved"}};
   const Buf outs[] = {{dq, b.io_bytes, "dq"}, {dk, b.io_bytes, "dk"}, {dv, b.io_bytes, "dv"},
                       {d_gamma, b.gb_bytes, "d_gamma"}, {d_beta, b.gb_bytes, "d_beta"},
                       {d_state_in, b.state_bytes, "d_state_in"}, {workspace, workspace_bytes, "workspace"}};
@@ -534,6 +566,185 @@ int attn_parts(const gdn_attn_desc* d) {
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 1;
   return gdn::attn_split_parts(d->D, d->B * d->H, d->Tq, d->Tk, d->S, d->chunk, cus);
+}
+
+// Training forward after its argument check: the forward of run_gram with
+// every frame in one gram range, G_t, B_t and the state snapshots kept in the
+// caller's saved buffer (snapshot slot t+1 holds M_t, slot 0 the initial
+// state) for gdn_frame_backward_saved.
+gdn_status run_train(const gdn_desc* d, const Ptrs& x, unsigned char* sv, hipStream_t s) {
+  const SavedPlan sp = make_saved_plan(d);
+  const int BH = d->B * d->H, T = d->T, D = d->D;
+  void* gfr = sv + sp.gfr;
+  void* bfr = sv + sp.bfr;
+  void* msnap = sv + sp.msnap;
+  float* carrier = (float*)(sv + sp.carrier);
+  const double c = 1.0 / std::sqrt((double)D * (double)d->S);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  hipError_t e = gdn::launch_state_snapshot(x.state_in, msnap, BH, D, (size_t)(T + 1) * D * D * 2, s);
+  gdn::GramArgs ga;
+  ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
+  ga.BH = BH; ga.T = T; ga.S = d->S; ga.t0 = 0; ga.Tc = T;
+  ga.kscale = (float)c; ga.kscale2 = (float)(c * c); ga.fp8 = 0;
+  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(D, ga, s); });
+  int bnd[kStateSplit + 1];
+  const int nsub = split_frames(T, bnd);
+  SideStream* ss = nullptr;
+  hipStream_t st = s;
+  if (e == hipSuccess && nsub > 1) {
+    e = side_stream(&ss);
+    if (e == hipSuccess) {
+      st = ss->stream;
+      e = hipEventRecord(ss->ev[0], s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
+    }
+  }
+  for (int i = 0; i < nsub && e == hipSuccess; ++i) {
+    gdn::StateArgs sa;
+    sa.gfr = gfr; sa.bfr = bfr; sa.gamma = x.gamma; sa.beta = x.beta;
+    sa.state_src = i == 0 ? x.state_in : carrier;
+    sa.state_dst = i == nsub - 1 ? x.state_out : carrier;
+    sa.snap = msnap;
+    sa.BH = BH; sa.T = T; sa.t0 = bnd[i]; sa.Tc = bnd[i + 1] - bnd[i]; sa.Fs = T; sa.f0 = bnd[i];
+    sa.beta_mode = d->beta_mode;
+    sa.snap_Fs = T + 1; sa.snap_f0 = 1 + bnd[i];
+    e = launch_timed(timed, GDN_KERNEL_STATE, st, [&] { return gdn::launch_state(D, sa, st); });
+    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
+  }
+  for (int i = 0; i < nsub && e == hipSuccess; ++i) {
+    if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + i], 0);
+    gdn::ReadoutArgs ro;
+    ro.q = x.q; ro.o = x.o; ro.snap = msnap; ro.norm_part = nullptr; ro.norms = x.norms;
+    ro.BH = BH; ro.T = T; ro.S = d->S; ro.t0 = bnd[i]; ro.Tc = bnd[i + 1] - bnd[i];
+    ro.Fs = T + 1; ro.f0 = 1 + bnd[i]; ro.fp8 = 0;
+    if (e == hipSuccess)
+      e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_readout(D, true, ro, s); });
+  }
+  if (e != hipSuccess) {
+    if (ss) {
+      const int last = kStateSplit + 1;
+      if (hipEventRecord(ss->ev[last], ss->stream) == hipSuccess) (void)hipStreamWaitEvent(s, ss->ev[last], 0);
+    }
+    return fail(GDN_ERR_HIP, "training forward launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
+}
+
+// The backward after its argument check.  `saved` (a training forward's
+// buffer) or nullptr: then G_t, B_t and the state snapshots are replayed
+// into the workspace first.
+gdn_status run_backward(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+                        const float* beta, const float* state_in, const void* d_out, const float* d_state_out,
+                        void* dq, void* dk, void* dv, float* d_gamma, float* d_beta, float* d_state_in,
+                        unsigned char* ws, const unsigned char* saved, hipStream_t s) {
+  const BackwardPlan b = make_backward_plan(d, saved != nullptr);
+  const int BH = (int)b.bh, T = d->T, D = d->D;
+  const double c = 1.0 / std::sqrt((double)D * (double)d->S);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const SavedPlan sp = make_saved_plan(d);
+  void* gfr = saved ? (void*)(saved + sp.gfr) : (void*)(ws + b.gfr);
+  void* bfr = saved ? (void*)(saved + sp.bfr) : (void*)(ws + b.bfr);
+  void* msnap = saved ? (void*)(saved + sp.msnap) : (void*)(ws + b.msnap);
+  float* carrier = (float*)(ws + b.carrier);
+  hipError_t e = hipSuccess;
+  if (!saved) {
+    e = gdn::launch_state_snapshot(state_in, msnap, BH, D, (size_t)(T + 1) * b.sfb, s);
+    // forward replay: G_t and B_t for every frame
+    gdn::GramArgs ga;
+    ga.k = k; ga.v = v; ga.gfr = gfr; ga.bfr = bfr;
+    ga.BH = BH; ga.T = T; ga.S = d->S; ga.t0 = 0; ga.Tc = T;
+    ga.kscale = (float)c; ga.kscale2 = (float)(c * c); ga.fp8 = 0;
+    if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(D, ga, s); });
+  }
+
+  // The two serial passes run on a side stream in frame sub-ranges, next to
+  // the HBM-bound passes over the tokens on the caller's stream (as in the
+  // forward): the state replay (M_t snapshots, frames first to last) next to
+  // C_t/dQ of the sub-range before, then the adjoint (Lambda_t, frames last
+  // to first, sub-ranges mirrored so the first one is short) next to
+  // Z_t/dV/dK of the sub-range after.  State and adjoint travel between
+  // launches through the fp32 carrier.
+  int bnd[kStateSplit + 1];
+  const int nsub = split_frames(T, bnd);
+  SideStream* ss = nullptr;
+  hipStream_t st = s;
+  if (e == hipSuccess && nsub > 1) {
+    e = side_stream(&ss);
+    if (e == hipSuccess) {
+      st = ss->stream;
+      e = hipEventRecord(ss->ev[0], s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
+    }
+  }
+  for (int i = 0; i < nsub && e == hipSuccess && !saved; ++i) {
+    gdn::StateArgs sa;
+    sa.gfr = gfr; sa.bfr = bfr; sa.gamma = gamma; sa.beta = beta;
+    sa.state_src = i == 0 ? state_in : carrier;
+    sa.state_dst = i == nsub - 1 ? nullptr : carrier;
+    sa.snap = msnap;
+    sa.BH = BH; sa.T = T; sa.t0 = bnd[i]; sa.Tc = bnd[i + 1] - bnd[i]; sa.Fs = T; sa.f0 = bnd[i];
+    sa.beta_mode = d->beta_mode;
+    sa.snap_Fs = T + 1; sa.snap_f0 = 1 + bnd[i];     // slot t+1 holds M_t
+    e = launch_timed(timed, GDN_KERNEL_STATE, st, [&] { return gdn::launch_state(D, sa, st); });
+    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
+  }
+  // C_t = ReLU(Q_t)^T dO_t and dQ_t in one pass over Q and dO: per state
+  // sub-range after a replay, else in one launch
+  for (int i = 0; i < (saved ? 1 : nsub) && e == hipSuccess; ++i) {
+    if (st != s && !saved) e = hipStreamWaitEvent(s, ss->ev[1 + i], 0);
+    gdn::CdqArgs ca;
+    ca.q = q; ca.dout = d_out; ca.msnap = msnap; ca.cfr = ws + b.cfr; ca.dq = dq; ca.BH = BH; ca.T = T;
+    ca.S = d->S; ca.t0 = saved ? 0 : bnd[i]; ca.Tc = saved ? T : bnd[i + 1] - bnd[i];
+    if (e == hipSuccess)
+      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_cdq(D, ca, s); });
+  }
+  // the adjoint needs every C_t
+  if (e == hipSuccess && st != s) {
+    e = hipEventRecord(ss->ev[0], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
+  }
+  for (int j = 0; j < nsub && e == hipSuccess; ++j) {
+    gdn::AdjointArgs aa;
+    aa.gfr = gfr; aa.bfr = bfr; aa.cfr = ws + b.cfr; aa.msnap = msnap;
+    aa.gamma = gamma; aa.beta = beta; aa.dstate_out = d_state_out;
+    aa.lam_src = j == 0 ? nullptr : carrier;
+    aa.lam_dst = j == nsub - 1 ? d_state_in : carrier;
+    aa.lsnap = ws + b.lsnap; aa.part = (float*)(ws + b.part);
+    aa.BH = BH; aa.T = T; aa.beta_mode = d->beta_mode;
+    aa.t_hi = T - bnd[j]; aa.t_lo = T - bnd[j + 1];
+    e = launch_timed(timed, GDN_KERNEL_BACKWARD, st, [&] { return gdn::launch_adjoint(D, aa, st); });
+    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + j], st);
+  }
+  // dV and dK in one pass over K and V (Z_t first, when dK is wanted)
+  for (int j = 0; j < nsub && e == hipSuccess; ++j) {
+    const int t_lo = T - bnd[j + 1], tc = bnd[j + 1] - bnd[j];
+    if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + j], 0);
+    if (e == hipSuccess && dk) {
+      gdn::ZmatArgs za;
+      za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
+      za.t0 = t_lo; za.Tc = tc;
+      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
+    }
+    if (e == hipSuccess && (dv || dk)) {
+      gdn::DvkArgs da;
+      da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.zsnap = ws + b.zsnap; da.gamma = gamma; da.beta = beta;
+      da.dv = dv; da.dk = dk; da.BH = BH; da.T = T; da.S = d->S; da.beta_mode = d->beta_mode;
+      da.kscale = (float)c; da.t0 = t_lo; da.Tc = tc;
+      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_dvdk(D, da, s); });
+    }
+  }
+  if (e == hipSuccess && (d_gamma || d_beta))
+    e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,
+                                   d->beta_mode, s);
+  if (e != hipSuccess) {
+    // keep the caller's stream ordered after anything already on the side stream
+    if (ss) {
+      const int last = kStateSplit + 1;
+      if (hipEventRecord(ss->ev[last], ss->stream) == hipSuccess) (void)hipStreamWaitEvent(s, ss->ev[last], 0);
+    }
+    return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
+  }
+  return GDN_OK;
 }
 
 }  // namespace
@@ -677,109 +888,51 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
   const gdn_status status = check_backward(d, q, k, v, gamma, beta, state_in, d_out, d_state_out, dq, dk, dv,
                                            d_gamma, d_beta, d_state_in, workspace, workspace_bytes);
   if (status != GDN_OK) return status;
-  const BackwardPlan b = make_backward_plan(d);
-  hipStream_t s = (hipStream_t)stream;
-  unsigned char* ws = (unsigned char*)workspace;
-  const int BH = (int)b.bh, T = d->T, D = d->D;
-  const double c = 1.0 / std::sqrt((double)D * (double)d->S);
-  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
-  void* msnap = ws + b.msnap;
-  float* carrier = (float*)(ws + b.carrier);
-  hipError_t e = gdn::launch_state_snapshot(state_in, msnap, BH, D, (size_t)(T + 1) * b.sfb, s);
-  // forward replay: G_t and B_t for every frame
-  gdn::GramArgs ga;
-  ga.k = k; ga.v = v; ga.gfr = ws + b.gfr; ga.bfr = ws + b.bfr;
-  ga.BH = BH; ga.T = T; ga.S = d->S; ga.t0 = 0; ga.Tc = T;
-  ga.kscale = (float)c; ga.kscale2 = (float)(c * c); ga.fp8 = 0;
-  if (e == hipSuccess) e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(D, ga, s); });
+  return run_backward(d, q, k, v, gamma, beta, state_in, d_out, d_state_out, dq, dk, dv, d_gamma, d_beta,
+                      d_state_in, (unsigned char*)workspace, nullptr, (hipStream_t)stream);
+}
 
-  // The two serial passes run on a side stream in frame sub-ranges, next to
-  // the HBM-bound passes over the tokens on the caller's stream (as in the
-  // forward): the state replay (M_t snapshots, frames first to last) next to
-  // C_t/dQ of the sub-range before, then the adjoint (Lambda_t, frames last
-  // to first, sub-ranges mirrored so the first one is short) next to
-  // Z_t/dV/dK of the sub-range after.  State and adjoint travel between
-  // launches through the fp32 carrier.
-  int bnd[kStateSplit + 1];
-  const int nsub = split_frames(T, bnd);
-  SideStream* ss = nullptr;
-  hipStream_t st = s;
-  if (e == hipSuccess && nsub > 1) {
-    e = side_stream(&ss);
-    if (e == hipSuccess) {
-      st = ss->stream;
-      e = hipEventRecord(ss->ev[0], s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
-    }
-  }
-  for (int i = 0; i < nsub && e == hipSuccess; ++i) {
-    gdn::StateArgs sa;
-    sa.gfr = ws + b.gfr; sa.bfr = ws + b.bfr; sa.gamma = gamma; sa.beta = beta;
-    sa.state_src = i == 0 ? state_in : carrier;
-    sa.state_dst = i == nsub - 1 ? nullptr : carrier;
-    sa.snap = msnap;
-    sa.BH = BH; sa.T = T; sa.t0 = bnd[i]; sa.Tc = bnd[i + 1] - bnd[i]; sa.Fs = T; sa.f0 = bnd[i];
-    sa.beta_mode = d->beta_mode;
-    sa.snap_Fs = T + 1; sa.snap_f0 = 1 + bnd[i];     // slot t+1 holds M_t
-    e = launch_timed(timed, GDN_KERNEL_STATE, st, [&] { return gdn::launch_state(D, sa, st); });
-    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + i], st);
-  }
-  // C_t = ReLU(Q_t)^T dO_t and dQ_t in one pass over Q and dO
-  for (int i = 0; i < nsub && e == hipSuccess; ++i) {
-    if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + i], 0);
-    gdn::CdqArgs ca;
-    ca.q = q; ca.dout = d_out; ca.msnap = msnap; ca.cfr = ws + b.cfr; ca.dq = dq; ca.BH = BH; ca.T = T;
-    ca.S = d->S; ca.t0 = bnd[i]; ca.Tc = bnd[i + 1] - bnd[i];
-    if (e == hipSuccess)
-      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_cdq(D, ca, s); });
-  }
-  // the adjoint needs every C_t
-  if (e == hipSuccess && st != s) {
-    e = hipEventRecord(ss->ev[0], s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->ev[0], 0);
-  }
-  for (int j = 0; j < nsub && e == hipSuccess; ++j) {
-    gdn::AdjointArgs aa;
-    aa.gfr = ws + b.gfr; aa.bfr = ws + b.bfr; aa.cfr = ws + b.cfr; aa.msnap = msnap;
-    aa.gamma = gamma; aa.beta = beta; aa.dstate_out = d_state_out;
-    aa.lam_src = j == 0 ? nullptr : carrier;
-    aa.lam_dst = j == nsub - 1 ? d_state_in : carrier;
-    aa.lsnap = ws + b.lsnap; aa.part = (float*)(ws + b.part);
-    aa.BH = BH; aa.T = T; aa.beta_mode = d->beta_mode;
-    aa.t_hi = T - bnd[j]; aa.t_lo = T - bnd[j + 1];
-    e = launch_timed(timed, GDN_KERNEL_BACKWARD, st, [&] { return gdn::launch_adjoint(D, aa, st); });
-    if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + j], st);
-  }
-  // dV and dK in one pass over K and V (Z_t first, when dK is wanted)
-  for (int j = 0; j < nsub && e == hipSuccess; ++j) {
-    const int t_lo = T - bnd[j + 1], tc = bnd[j + 1] - bnd[j];
-    if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + j], 0);
-    if (e == hipSuccess && dk) {
-      gdn::ZmatArgs za;
-      za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
-      za.t0 = t_lo; za.Tc = tc;
-      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
-    }
-    if (e == hipSuccess && (dv || dk)) {
-      gdn::DvkArgs da;
-      da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.zsnap = ws + b.zsnap; da.gamma = gamma; da.beta = beta;
-      da.dv = dv; da.dk = dk; da.BH = BH; da.T = T; da.S = d->S; da.beta_mode = d->beta_mode;
-      da.kscale = (float)c; da.t0 = t_lo; da.Tc = tc;
-      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_dvdk(D, da, s); });
-    }
-  }
-  if (e == hipSuccess && (d_gamma || d_beta))
-    e = gdn::launch_adjoint_reduce((const float*)(ws + b.part), gamma, beta, d_gamma, d_beta, BH, T, D,
-                                   d->beta_mode, s);
-  if (e != hipSuccess) {
-    // keep the caller's stream ordered after anything already on the side stream
-    if (ss) {
-      const int last = kStateSplit + 1;
-      if (hipEventRecord(ss->ev[last], ss->stream) == hipSuccess) (void)hipStreamWaitEvent(s, ss->ev[last], 0);
-    }
-    return fail(GDN_ERR_HIP, "backward kernel launch: %s", hipGetErrorString(e));
-  }
-  return GDN_OK;
+size_t gdn_saved_size(const gdn_desc* d) {
+  if (check_desc(d) != GDN_OK || d->io_dtype != GDN_BF16 || (d->flags & GDN_FLAG_DIRECT) ||
+      d->T > kMaxFramesPerLaunch)
+    return 0;
+  return make_saved_plan(d).total;
+}
+
+size_t gdn_backward_saved_workspace_size(const gdn_desc* d) {
+  if (gdn_saved_size(d) == 0) return 0;
+  return make_backward_plan(d, true).total;
+}
+
+gdn_status gdn_frame_forward_train(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                   const float* gamma, const float* beta, const float* state_in, void* o,
+                                   float* state_out, float* state_norms, void* saved, size_t saved_bytes,
+                                   void* stream) {
+  // the forward's own checks, with the saved buffer in the workspace's place
+  const gdn_status st = gdn_check_args(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, saved,
+                                       saved_bytes, 0);
+  if (st != GDN_OK) return st;
+  if (d->io_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "the training forward takes bf16 I/O only");
+  if (d->flags & GDN_FLAG_DIRECT) return fail(GDN_ERR_UNSUPPORTED, "the training forward runs the Gram pipeline");
+  if (d->T > kMaxFramesPerLaunch)
+    return fail(GDN_ERR_UNSUPPORTED, "the training forward takes at most %d frames per call", kMaxFramesPerLaunch);
+  const size_t need = make_saved_plan(d).total;
+  if (saved_bytes < need) return fail(GDN_ERR_WORKSPACE, "saved buffer of %zu bytes < required %zu", saved_bytes, need);
+  const Ptrs x{q, k, v, gamma, beta, state_in, o, state_out, state_norms};
+  return run_train(d, x, (unsigned char*)saved, (hipStream_t)stream);
+}
+
+gdn_status gdn_frame_backward_saved(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const float* beta, const void* saved, size_t saved_bytes,
+                                    const void* d_out, const float* d_state_out, void* dq, void* dk, void* dv,
+                                    float* d_gamma, float* d_beta, float* d_state_in, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const gdn_status status = check_backward(d, q, k, v, gamma, beta, nullptr, d_out, d_state_out, dq, dk, dv,
+                                           d_gamma, d_beta, d_state_in, workspace, workspace_bytes, saved,
+                                           saved_bytes, true);
+  if (status != GDN_OK) return status;
+  return run_backward(d, q, k, v, gamma, beta, nullptr, d_out, d_state_out, dq, dk, dv, d_gamma, d_beta,
+                      d_state_in, (unsigned char*)workspace, (const unsigned char*)saved, (hipStream_t)stream);
 }
 
 gdn_status gdn_attention_check_args(const gdn_attn_desc* d, const void* q, const void* k, const void* v,

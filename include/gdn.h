@@ -207,6 +207,34 @@ gdn_status gdn_frame_backward(const gdn_desc* d, const void* q, const void* k, c
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training pair: a forward that keeps what the backward would otherwise replay,
+ * and a backward that takes it.  gdn_frame_forward_train computes exactly what
+ * gdn_frame_forward computes (bitwise the same o, state_out and state_norms)
+ * and leaves, in `saved`, G_t = Kf^T Kf and B_t = Kf^T V_t of every frame and
+ * bf16 snapshots of the initial state and of the state after every frame.
+ * gdn_frame_backward_saved, given the same q, k, v, gamma, beta and that
+ * saved buffer (unchanged), computes bitwise the gradients of
+ * gdn_frame_backward (which replays the forward itself) without the replay.
+ * bf16 I/O, the Gram pipeline, T <= 1024 frames per call.
+ *   saved       device buffer of gdn_saved_size(d) bytes, 256-byte aligned,
+ *               owned by the caller between the two calls (contents opaque)
+ *   workspace   of the backward: gdn_backward_saved_workspace_size(d) bytes
+ * Both sizes are 0 when d is invalid or not supported.  Other conventions as
+ * for gdn_frame_forward and gdn_frame_backward.
+ */
+size_t gdn_saved_size(const gdn_desc* d);
+size_t gdn_backward_saved_workspace_size(const gdn_desc* d);
+gdn_status gdn_frame_forward_train(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                   const float* gamma, const float* beta, const float* state_in, void* o,
+                                   float* state_out, float* state_norms, void* saved, size_t saved_bytes,
+                                   void* stream);
+gdn_status gdn_frame_backward_saved(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                    const float* gamma, const float* beta, const void* saved, size_t saved_bytes,
+                                    const void* d_out, const float* d_state_out, void* dq, void* dk, void* dv,
+                                    float* d_gamma, float* d_beta, float* d_state_in, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Block-causal temporal convolution with a carried-token cache: the causal
  * FFN's temporal convolution in the talk "SANA-Video: Efficient Video
  * Generation with Block Linear Diffusion Transformer" (its closing part, the

@@ -367,3 +367,31 @@ def test_attention_dtype_flag_abi_null_align_alias_errors(gdn):
     assert gdn.attention_check_args(d, **a) == 5
     # no device here: the size query falls back to no split; invalid descriptors give 0
     assert gdn.attention_workspace_size(gdn.make_attn_desc(1, 1, 2, 3, 8, 24, 1)) == 0
+
+
+def test_training_pair_host_checks(gdn):
+    import ctypes
+    L = gdn.lib()
+    d = gdn.make_desc(1, 2, 30, 16, 32, "bf16")
+    n_saved, n_ws = gdn.saved_size(d), gdn.backward_saved_workspace_size(d)
+    assert 0 < n_saved and 0 < n_ws < gdn.backward_workspace_size(d)
+    for bad in (gdn.make_desc(1, 2, 30, 16, 32, "f32"), gdn.make_desc(1, 2, 30, 16, 32, "fp8"),
+                gdn.make_desc(1, 2, 1025, 16, 32, "bf16"),
+                gdn.make_desc(1, 2, 30, 16, 32, "bf16", flags=gdn.binding.FLAG_DIRECT)):
+        assert gdn.saved_size(bad) == 0 and gdn.backward_saved_workspace_size(bad) == 0
+    q, k, v, ga, be, si, o, so, nm, sv, dout, dso, dq, dk, dv, dg, db, dsi, ws = addrs(19)
+    fw = lambda desc, saved, nbytes: L.gdn_frame_forward_train(ctypes.byref(desc), q, k, v, ga, be, si, o, so, nm,
+                                                               saved, nbytes, None)
+    assert fw(d, 0, n_saved) == 8                     # no saved buffer
+    assert fw(d, sv, n_saved - 1) == 8                # too small
+    assert fw(d, sv + 64, n_saved) == 4               # misaligned
+    assert fw(d, o, n_saved) == 5                     # overlaps o
+    assert fw(gdn.make_desc(1, 2, 30, 16, 32, "f32"), sv, n_saved) == 6
+    assert fw(gdn.make_desc(1, 2, 1025, 16, 32, "bf16"), sv, 1 << 40) == 6
+    bw = lambda saved, nbytes, wsp, wsn, dq_=dq: L.gdn_frame_backward_saved(
+        ctypes.byref(d), q, k, v, ga, be, saved, nbytes, dout, dso, dq_, dk, dv, dg, db, dsi, wsp, wsn, None)
+    assert bw(0, n_saved, ws, n_ws) == 1              # no saved buffer
+    assert bw(sv, n_saved - 1, ws, n_ws) == 8
+    assert bw(sv, n_saved, ws, n_ws - 1) == 8
+    assert bw(sv + 8, n_saved, ws, n_ws) == 4
+    assert bw(sv, n_saved, ws, n_ws, dq_=sv + 256) == 5   # dq overlaps saved

@@ -131,3 +131,45 @@ def test_backward_minute_720p_sampled_head(env):
     print({k: f"{v:.2e}" for k, v in errs.items()})
     for k, v in errs.items():
         assert v < TOL, f"{k}: rel err {v:.3e}"
+
+
+@pytest.mark.parametrize("mode", ["erase", "write"])
+@pytest.mark.parametrize("B,H,T,S,D", [(1, 2, 5, 100, 64), (1, 2, 100, 40, 32), (2, 1, 7, 130, 112)])
+def test_training_pair_is_bitwise_forward_and_backward(env, B, H, T, S, D, mode):
+    """frame_forward_train gives bitwise frame_forward's outputs, and
+    frame_backward_saved from its saved buffer gives bitwise frame_backward's
+    gradients (same G_t, B_t and snapshots, no replay)."""
+    torch, gdn, wl, go, gb = env
+    w = wl.Workload("tr", B, H, T, S, D, gamma=(0.8, 1.0), beta=(0.1, 1.0))
+    inp = {k: v.to("cuda") for k, v in wl.generate(w, device="cpu", seed=4).items()}
+    g = torch.Generator().manual_seed(41)
+    d_out = torch.randn((B, H, T, S, D), generator=g).to(torch.bfloat16).cuda()
+    m0 = (0.2 * torch.randn((B, H, D, D), generator=g)).cuda()
+    ds = (0.5 * torch.randn((B, H, D, D), generator=g)).cuda()
+    args = (inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    o1, s1, n1 = gdn.frame_forward(*args, state=m0, beta_mode=mode, want_norms=True)
+    o2, s2, n2, saved = gdn.frame_forward_train(*args, state=m0, beta_mode=mode, want_norms=True)
+    ref = gdn.frame_backward(*args, d_out, state=m0, d_state_out=ds, beta_mode=mode)
+    got = gdn.frame_backward_saved(*args, saved, d_out, d_state_out=ds, beta_mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(n1, n2)
+    assert set(got) == set(ref)
+    for key in ref:
+        assert torch.equal(got[key], ref[key]), key
+
+
+def test_training_pair_minute_720p_bitwise(env):
+    torch, gdn, wl, go, gb = env
+    w = wl.MINUTE_720P
+    inp = wl.generate(w, device="cuda")
+    d_out = torch.randn((w.B, w.H, w.T, w.S, w.D), generator=torch.Generator(device="cuda").manual_seed(8),
+                        device="cuda").to(torch.bfloat16)
+    args = (inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    o1, s1, _ = gdn.frame_forward(*args)
+    o2, s2, _, saved = gdn.frame_forward_train(*args)
+    ref = gdn.frame_backward(*args, d_out, want=("dq", "dk", "dgamma"))
+    got = gdn.frame_backward_saved(*args, saved, d_out, want=("dq", "dk", "dgamma"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    for key in ref:
+        assert torch.equal(got[key], ref[key]), key
