@@ -381,7 +381,7 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
 // ---------------------------------------------------------------------------
 struct BackwardPlan {
   size_t bh, gfb, bfb, sfb, pfb, io_bytes, gb_bytes, state_bytes;
-  size_t gfr, bfr, cfr, msnap, lsnap, zsnap, part, carrier, total;
+  size_t gfr, bfr, cfr, msnap, lsnap, part, carrier, total;
 };
 
 // Layout of the saved buffer of a training forward: G_t and B_t of every
@@ -425,7 +425,6 @@ BackwardPlan make_backward_plan(const gdn_desc* d, bool saved = false) {
   b.cfr = take(b.bh * T * b.bfb);
   b.msnap = saved ? 0 : take(b.bh * (T + 1) * b.sfb);
   b.lsnap = take(b.bh * T * b.sfb);
-  b.zsnap = take(b.bh * T * b.sfb);
   b.part = take(b.bh * T * b.pfb);
   b.carrier = take(b.state_bytes);         // fp32 state / adjoint between sub-range launches
   b.total = off;
@@ -715,19 +714,13 @@ gdn_status run_backward(const gdn_desc* d, const void* q, const void* k, const v
     e = launch_timed(timed, GDN_KERNEL_BACKWARD, st, [&] { return gdn::launch_adjoint(D, aa, st); });
     if (e == hipSuccess && st != s) e = hipEventRecord(ss->ev[1 + j], st);
   }
-  // dV and dK in one pass over K and V (Z_t first, when dK is wanted)
+  // dV and dK in one pass over K and V (Z_t formed inside)
   for (int j = 0; j < nsub && e == hipSuccess; ++j) {
     const int t_lo = T - bnd[j + 1], tc = bnd[j + 1] - bnd[j];
     if (st != s) e = hipStreamWaitEvent(s, ss->ev[1 + j], 0);
-    if (e == hipSuccess && dk) {
-      gdn::ZmatArgs za;
-      za.msnap = msnap; za.lsnap = ws + b.lsnap; za.zsnap = ws + b.zsnap; za.BH = BH; za.T = T;
-      za.t0 = t_lo; za.Tc = tc;
-      e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_zmat(D, za, s); });
-    }
     if (e == hipSuccess && (dv || dk)) {
       gdn::DvkArgs da;
-      da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.zsnap = ws + b.zsnap; da.gamma = gamma; da.beta = beta;
+      da.k = k; da.v = v; da.lsnap = ws + b.lsnap; da.msnap = msnap; da.gamma = gamma; da.beta = beta;
       da.dv = dv; da.dk = dk; da.BH = BH; da.T = T; da.S = d->S; da.beta_mode = d->beta_mode;
       da.kscale = (float)c; da.t0 = t_lo; da.Tc = tc;
       e = launch_timed(timed, GDN_KERNEL_BACKWARD, s, [&] { return gdn::launch_dvdk(D, da, s); });

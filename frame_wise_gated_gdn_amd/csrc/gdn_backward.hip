@@ -1,5 +1,6 @@
 // Frame-wise Gated DeltaNet backward on gfx950: the initial-state snapshot,
-// Z_t, the fused dV/dK pass and the dgamma/dbeta reduction.  The forward
+// the fused dV/dK pass (which forms Z_t itself) and the dgamma/dbeta
+// reduction.  The forward
 // replay, the fused C_t/dQ pass and the adjoint state pass live in
 // gdn_gram.hip beside the forward passes they mirror.
 //
@@ -45,71 +46,17 @@ __global__ void gdn_state_snapshot_kernel(const float* state, uint16_t* snap, in
 }
 
 // ----------------------------------------------------------------------------
-// Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame), written as a
-// bf16 block snapshot.  One workgroup of 4 waves per (head, frame): both
-// snapshots are staged in LDS; block (R, C) of Z is
-//   sum_kc MFMA(rows(M, R, kc), rows(L, C, kc)) + MFMA(rows(L, R, kc), rows(M, C, kc))
-// where rows(X, b, kc) gives lane (i, g) the row 16 b + i of X at columns
-// 32 kc + 4 g .. + 3 and 32 kc + 16 + 4 g .. + 3 (the k-slot order of the
-// state pass), read from the block snapshot with a transposed LDS read: in
-// block [jt][I] the 8 bytes at (16 (x / 4) + y) * 8 hold rows 4 (x / 4) ..
-// + 3 of column y, and ds_read_b64_tr_b16 with lane j of each 16-lane group
-// supplying unit (16 (j % 4) + 4 g + j / 4) hands lane n the row n, columns
-// 4 g .. 4 g + 3.  The accumulator of block (R, C) holds, in lane (n, g),
-// Z[16 R + 4 g + r][16 C + n]: exactly block [C][R] of the snapshot layout.
-// ----------------------------------------------------------------------------
-constexpr int kZWaves = 4;
-
-template <int D>
-__global__ __launch_bounds__(kZWaves * 64) void gdn_zmat_kernel(ZmatArgs a) {
-  constexpr int NB = D / 16, NKC = (NB + 1) / 2;
-  constexpr size_t SB = (size_t)D * D * 2;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int fh = blockIdx.x;                       // over BH * Tc
-  const int bh = fh / a.Tc, t = a.t0 + fh % a.Tc;
-  const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  unsigned char* ms = smem;
-  unsigned char* ls = smem + SB;
-  const __amdgpu_buffer_rsrc_t mrs =
-      make_rsrc((const unsigned char*)a.msnap + ((size_t)bh * (a.T + 1) + t) * SB, (uint32_t)SB);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc((const unsigned char*)a.lsnap + ((size_t)bh * a.T + t) * SB,
-                                               (uint32_t)SB);
-  for (int u = tid; u < (int)(SB / 16); u += kZWaves * 64) {
-    *(u32x4*)(ms + (size_t)u * 16) = buf_load16(mrs, (uint32_t)u * 16u);
-    *(u32x4*)(ls + (size_t)u * 16) = buf_load16(lrs, (uint32_t)u * 16u);
-  }
-  __syncthreads();
-  const uint32_t trofs = (uint32_t)(((n & 3) * 16 + 4 * g + (n >> 2)) * 8);
-  auto rows = [&](const unsigned char* x, int b, int kc) -> u32x4 {
-    const u32x2 lo = lds_tr16((const uint16_t*)(x + (size_t)((2 * kc) * NB + b) * 512 + trofs));
-    const u32x2 hi = (2 * kc + 1 < NB) ? lds_tr16((const uint16_t*)(x + (size_t)((2 * kc + 1) * NB + b) * 512 + trofs))
-                                       : u32x2{0u, 0u};
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-  };
-  unsigned char* zout = (unsigned char*)a.zsnap + ((size_t)bh * a.T + t) * SB;
-  for (int blk = w; blk < NB * NB; blk += kZWaves) {
-    const int R = blk / NB, C = blk % NB;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      acc = mfma_bf16(rows(ms, R, kc), rows(ls, C, kc), acc);
-      acc = mfma_bf16(rows(ls, R, kc), rows(ms, C, kc), acc);
-    }
-    const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-    *(u32x2*)(zout + ((size_t)(C * NB + R) * 64 + l) * 8) = pk;
-  }
-}
-
-// ----------------------------------------------------------------------------
 // dV_t and dK_t in one pass over K_t and V_t.  One workgroup of 4 waves per
 // (head, frame).  The frame's 32-token chunks of K and V are loaded once,
 // cooperatively (1 KB pieces spread over the waves, kDvkRing chunks ahead in
 // registers), and staged in a double-buffered LDS tile, K through ReLU.  Wave
 // w owns the output column blocks jb = w, w + 4 (< D/16) of both gradients and
-// holds, for them, the MFMA A operands of Lambda_t, of Lambda_t^T and of Z_t
-// (the readout's operand layout; Lambda_t^T by transposed LDS reads of the
-// staged snapshot).  Per chunk and 16-token half it forms
+// holds, for them, the MFMA A operands of Lambda_t, of Lambda_t^T and of
+// Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T (the readout's operand
+// layout).  Lambda_t^T and Z_t come from the Lambda_t and M_{t-1} snapshots
+// staged in LDS before the token loop: transposed LDS reads for the row
+// operands and two MFMA chains per Z block, whose output layout is already
+// the operand layout.  Per chunk and 16-token half it forms
 //   dV = c w ReLU(K) Lambda,   dK = (c w V Lambda^T - c^2 b g ReLU(K) Z) * [K > 0]
 // (the mask read from the staged ReLU(K)), assembles both in LDS tiles and
 // stores them with the same coalesced 1 KB pieces.
@@ -126,7 +73,10 @@ struct DvkShape {
   static constexpr int JPW = (NB + kDvkWaves - 1) / kDvkWaves;        // column blocks per wave
   static constexpr int RS = D + 8;                                    // LDS row stride (elements)
   static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
-  static constexpr size_t lds_bytes = 6 * tile_bytes;                 // K, V x 2 buffers; dV, dK tiles
+  // K, V x 2 buffers and the dV, dK tiles; before the token loop the same
+  // space holds the Lambda_t and M_{t-1} snapshots
+  static constexpr size_t snap_bytes = (size_t)D * D * 2;
+  static constexpr size_t lds_bytes = 6 * tile_bytes > 2 * snap_bytes ? 6 * tile_bytes : 2 * snap_bytes;
 };
 
 template <int D, bool WRITE>
@@ -134,7 +84,7 @@ __global__ __launch_bounds__(kDvkWaves * 64, 2) void gdn_dvdk_kernel(DvkArgs a) 
   using Sh = DvkShape<D>;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, UPR = Sh::UPR, NLD = Sh::NLD, LPW = Sh::LPW, JPW = Sh::JPW;
   constexpr int RS = Sh::RS;
-  static_assert((size_t)D * D * 2 <= Sh::lds_bytes, "the Lambda snapshot is staged in the tiles' space");
+  static_assert(2 * Sh::snap_bytes <= Sh::lds_bytes, "the Lambda and M snapshots are staged in the tiles' space");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int T = a.T, S = a.S;
   const int fh = blockIdx.x, bh = fh / a.Tc, t = a.t0 + fh % a.Tc;
@@ -150,32 +100,63 @@ __global__ __launch_bounds__(kDvkWaves * 64, 2) void gdn_dvdk_kernel(DvkArgs a) 
   const float bt = a.beta[(size_t)bh * T + t], gm = a.gamma[(size_t)bh * T + t];
   const float cw = a.kscale * (WRITE ? bt : 1.f), cz = -a.kscale * a.kscale * bt * gm;
 
-  // weights of this wave's column blocks
+  // weights of this wave's column blocks: Lambda_t and Lambda_t^T from the
+  // Lambda snapshot, Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T computed
+  // here from both snapshots staged in LDS
   const size_t snb = ((size_t)bh * T + t) * D * D * 2;
   const unsigned char* lsn = (const unsigned char*)a.lsnap + snb;
-  const unsigned char* zsn = (const unsigned char*)a.zsnap + snb;
-  for (int u = tid; u < D * D * 2 / 16; u += kDvkWaves * 64)
-    *(u32x4*)(smem + (size_t)u * 16) = *(const u32x4*)(lsn + (size_t)u * 16);
+  const unsigned char* msn = (const unsigned char*)a.msnap + ((size_t)bh * (T + 1) + t) * D * D * 2;
+  unsigned char* const ls = smem;                                  // Lambda_t
+  unsigned char* const ms = smem + Sh::snap_bytes;                 // M_{t-1}
+  for (int u = tid; u < D * D * 2 / 16; u += kDvkWaves * 64) {
+    *(u32x4*)(ls + (size_t)u * 16) = *(const u32x4*)(lsn + (size_t)u * 16);
+    *(u32x4*)(ms + (size_t)u * 16) = *(const u32x4*)(msn + (size_t)u * 16);
+  }
   __syncthreads();
   const uint32_t trofs = (uint32_t)(((n & 3) * 16 + 4 * g + (n >> 2)) * 8);
+  // rows 16 b .. 16 b + 15 of a staged snapshot X as an MFMA operand over the
+  // 32-wide k-step kc (lane n: row 16 b + n, columns 32 kc + 8 g' ..)
+  auto rows = [&](const unsigned char* x, int b, int kc) -> u32x4 {
+    const u32x2 lo = lds_tr16((const uint16_t*)(x + (size_t)((2 * kc) * NB + b) * 512 + trofs));
+    const u32x2 hi = (2 * kc + 1 < NB) ? lds_tr16((const uint16_t*)(x + (size_t)((2 * kc + 1) * NB + b) * 512 + trofs))
+                                       : u32x2{0u, 0u};
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
   u32x4 AL[JPW][NKC], AT[JPW][NKC], AZ[JPW][NKC];
 #pragma unroll
   for (int i = 0; i < JPW; ++i) {
     const int jb = w + kDvkWaves * i;
     const bool has = jb < NB;
     const int jj = has ? jb : 0;
+    u32x4 MT[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const bool h2 = 2 * kc + 1 < NB;
       const size_t b0 = (size_t)(jj * NB + 2 * kc) * 512 + l * 8, b1 = b0 + 512;
       const u32x2 llo = *(const u32x2*)(lsn + b0), lhi = h2 ? *(const u32x2*)(lsn + b1) : u32x2{0u, 0u};
-      const u32x2 zlo = *(const u32x2*)(zsn + b0), zhi = h2 ? *(const u32x2*)(zsn + b1) : u32x2{0u, 0u};
-      const u32x2 tlo = lds_tr16((const uint16_t*)(smem + (size_t)((2 * kc) * NB + jj) * 512 + trofs));
-      const u32x2 thi = h2 ? lds_tr16((const uint16_t*)(smem + (size_t)((2 * kc + 1) * NB + jj) * 512 + trofs))
-                           : u32x2{0u, 0u};
       AL[i][kc] = u32x4{llo[0], llo[1], lhi[0], lhi[1]};
-      AZ[i][kc] = u32x4{zlo[0], zlo[1], zhi[0], zhi[1]};
-      AT[i][kc] = u32x4{tlo[0], tlo[1], thi[0], thi[1]};
+      AT[i][kc] = rows(ls, jj, kc);          // Lambda rows of block jb = Lambda^T columns
+      MT[kc] = rows(ms, jj, kc);
+    }
+    // Z block (R, jb) in the MFMA output layout is the snapshot block layout
+    // that AZ takes: lane (n, g) holds Z[16 R + 4 g + r][16 jb + n]
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      u32x2 half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int R = 2 * kc + hh;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (R < NB) {
+#pragma unroll
+          for (int k2 = 0; k2 < NKC; ++k2) {
+            acc = mfma_bf16(rows(ms, R, k2), AT[i][k2], acc);
+            acc = mfma_bf16(rows(ls, R, k2), MT[k2], acc);
+          }
+        }
+        half[hh] = u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+      }
+      AZ[i][kc] = u32x4{half[0][0], half[0][1], half[1][0], half[1][1]};
     }
   }
   __syncthreads();
@@ -330,33 +311,6 @@ __global__ void gdn_adjoint_reduce_kernel(const float* part, const float* gamma,
   if (dbeta) dbeta[idx] = (float)(-g * s2 + (write_mode ? s3 : 0.0));
 }
 
-template <int D>
-static hipError_t launch_zmat_t(const ZmatArgs& za, hipStream_t stream) {
-  static bool attr_set = false;
-  const size_t lds = (size_t)2 * D * D * 2;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_zmat_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((gdn_zmat_kernel<D>), dim3((unsigned)(za.BH * za.Tc)), dim3(kZWaves * 64), lds, stream, za);
-  return hipGetLastError();
-}
-
-hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream) {
-  switch (D) {
-    case 16: return launch_zmat_t<16>(za, stream);
-    case 32: return launch_zmat_t<32>(za, stream);
-    case 48: return launch_zmat_t<48>(za, stream);
-    case 64: return launch_zmat_t<64>(za, stream);
-    case 80: return launch_zmat_t<80>(za, stream);
-    case 96: return launch_zmat_t<96>(za, stream);
-    case 112: return launch_zmat_t<112>(za, stream);
-    case 128: return launch_zmat_t<128>(za, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 hipError_t launch_state_snapshot(const float* state, void* snap, int BH, int D, size_t slot_stride_bytes,
                                  hipStream_t stream) {

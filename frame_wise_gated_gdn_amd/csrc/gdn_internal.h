@@ -55,7 +55,7 @@ struct DvkArgs {
   const void* k;            // [BH][T][S][D] bf16
   const void* v;            // [BH][T][S][D] bf16
   const void* lsnap;        // bf16 snapshots of Lambda_t: [BH][T]
-  const void* zsnap;        // bf16 snapshots of Z_t: [BH][T]
+  const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
   const float* gamma;       // [BH][T]
   const float* beta;        // [BH][T]
   void* dv;                 // [BH][T][S][D] bf16 or nullptr
@@ -93,15 +93,6 @@ struct AttnArgs {
   int split, split_tiles;
   float* part_o;            // [split][BH][Tq*S][D] fp32
   float* part_ml;           // [split][BH][Tq*S][2] fp32: running max (log2 units), sum
-};
-
-// Z_t = M_{t-1} Lambda_t^T + Lambda_t M_{t-1}^T per (head, frame) (backward).
-struct ZmatArgs {
-  const void* msnap;        // bf16 snapshots of M_{t-1}: [BH][T+1], slot t holds M_{t-1}
-  const void* lsnap;        // bf16 snapshots of Lambda_t: [BH][T]
-  void* zsnap;              // out: bf16 snapshots of Z_t: [BH][T]
-  int BH, T;
-  int t0, Tc;               // this launch's frames: t0 .. t0+Tc-1
 };
 
 // Gram pass (bf16 or e4m3 I/O): per (head, frame) G = Kf^T Kf and B = Kf^T V.
@@ -155,7 +146,6 @@ hipError_t launch_readout(int D, bool bf16, const ReadoutArgs& ro, hipStream_t s
 hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream);
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream);
 hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream);
-hipError_t launch_zmat(int D, const ZmatArgs& za, hipStream_t stream);
 hipError_t launch_dvdk(int D, const DvkArgs& da, hipStream_t stream);
 hipError_t launch_tconv(const TconvArgs& ta, hipStream_t stream);
 hipError_t launch_attn(int D, const AttnArgs& aa, hipStream_t stream);
