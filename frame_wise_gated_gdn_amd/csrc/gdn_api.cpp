@@ -376,8 +376,8 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
 // ---------------------------------------------------------------------------
 // Backward.  Workspace, per head and frame (bf16 blocks unless noted): the
 // forward replay's G_t and B_t, the snapshots of M_{t-1} (T + 1 slots, slot 0
-// the initial state), C_t = ReLU(Q_t)^T dO_t, the snapshots of Lambda_t and
-// Z_t, and the adjoint pass's fp32 partial sums.
+// the initial state), C_t = ReLU(Q_t)^T dO_t, the snapshots of Lambda_t, the
+// adjoint pass's fp32 partial sums and an fp32 carrier.
 // ---------------------------------------------------------------------------
 struct BackwardPlan {
   size_t bh, gfb, bfb, sfb, pfb, io_bytes, gb_bytes, state_bytes;
@@ -661,7 +661,7 @@ gdn_status run_backward(const gdn_desc* d, const void* q, const void* k, const v
   // forward): the state replay (M_t snapshots, frames first to last) next to
   // C_t/dQ of the sub-range before, then the adjoint (Lambda_t, frames last
   // to first, sub-ranges mirrored so the first one is short) next to
-  // Z_t/dV/dK of the sub-range after.  State and adjoint travel between
+  // dV/dK of the sub-range after.  State and adjoint travel between
   // launches through the fp32 carrier.
   int bnd[kStateSplit + 1];
   const int nsub = split_frames(T, bnd);
