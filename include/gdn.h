@@ -196,6 +196,9 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
  * replayed inside the call (its per-frame states are not kept by
  * gdn_frame_forward).  T <= 1024 frames per call; the workspace must hold
  * gdn_backward_workspace_size(d) bytes (0 if d is invalid or unsupported).
+ * Longer sequences run in chunks, last chunk first: each chunk takes the
+ * forward state at its start as state_in and the next chunk's d_state_in as
+ * its d_state_out, which gives bitwise the gradients of one call.
  * Same conventions as gdn_frame_forward (device pointers, stream, errors);
  * no output may overlap an input or another output.
  */

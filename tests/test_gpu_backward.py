@@ -173,3 +173,32 @@ def test_training_pair_minute_720p_bitwise(env):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     for key in ref:
         assert torch.equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("mode", ["erase", "write"])
+def test_backward_over_chunks_equals_one_call(env, mode):
+    """Frames in two calls, last chunk first: the state at the boundary (from a
+    forward over the first chunk) goes in as state_in, and the first chunk takes
+    the second's d_state_in as its d_state_out.  Gradients are bitwise those of
+    one call over all frames; this is how sequences past 1024 frames run."""
+    torch, gdn, wl, go, gb = env
+    B, H, T, S, D, T1 = 1, 2, 12, 60, 48, 5
+    w = wl.Workload("ch", B, H, T, S, D, gamma=(0.8, 1.0), beta=(0.1, 1.0))
+    inp = {k: v.to("cuda") for k, v in wl.generate(w, device="cpu", seed=9).items()}
+    g = torch.Generator().manual_seed(19)
+    d_out = torch.randn((B, H, T, S, D), generator=g).to(torch.bfloat16).cuda()
+    m0 = (0.2 * torch.randn((B, H, D, D), generator=g)).cuda()
+    ds = (0.5 * torch.randn((B, H, D, D), generator=g)).cuda()
+    full = gdn.frame_backward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], d_out, state=m0,
+                              d_state_out=ds, beta_mode=mode)
+    part = lambda x, a, b: x[:, :, a:b].contiguous()
+    _, m_mid, _ = gdn.frame_forward(*(part(inp[n], 0, T1) for n in ("q", "k", "v", "gamma", "beta")), state=m0,
+                                    beta_mode=mode)
+    second = gdn.frame_backward(*(part(inp[n], T1, T) for n in ("q", "k", "v", "gamma", "beta")),
+                                part(d_out, T1, T), state=m_mid, d_state_out=ds, beta_mode=mode)
+    first = gdn.frame_backward(*(part(inp[n], 0, T1) for n in ("q", "k", "v", "gamma", "beta")),
+                               part(d_out, 0, T1), state=m0, d_state_out=second["dstate"], beta_mode=mode)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dgamma", "dbeta"):
+        assert torch.equal(torch.cat([first[key], second[key]], dim=2), full[key]), key
+    assert torch.equal(first["dstate"], full["dstate"])
