@@ -71,7 +71,8 @@ def run_case(env, B, H, T, S, D, mode, with_states=True, seed=0):
 
 @pytest.mark.parametrize("mode", ["erase", "write"])
 @pytest.mark.parametrize("B,H,T,S,D", [(1, 2, 5, 100, 64), (1, 2, 4, 77, 16), (2, 1, 6, 130, 112),
-                                        (1, 2, 3, 64, 128), (1, 3, 7, 40, 48)])
+                                        (1, 2, 3, 64, 128), (1, 3, 7, 40, 48), (1, 2, 1, 33, 64),
+                                        (1, 1, 6, 1, 32), (1, 1, 1, 1, 16)])
 def test_backward_parity(env, B, H, T, S, D, mode):
     run_case(env, B, H, T, S, D, mode)
 
