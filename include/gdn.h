@@ -133,7 +133,7 @@ const char* gdn_last_error(void);
 /*
  * Workspace bytes the library would like for `d` (all T frames staged at once,
  * capped at 1024 frames; the bf16 and e4m3 paths stage G_t, B_t and a bf16 state
- * snapshot per frame, about 3*D*D*2 bytes per head and frame); 0 if `d` is
+ * snapshot per frame, between 2.5*D*D*2 and 3*D*D*2 bytes per head and frame); 0 if `d` is
  * invalid.  Any workspace of at
  * least gdn_workspace_min_size(d) bytes works: a smaller one makes the library
  * process the frames in more pieces, with bitwise the same results.
