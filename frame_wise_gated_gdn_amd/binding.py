@@ -158,6 +158,43 @@ def _addr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check(device, name, t, shape=None, dtype=None):
+    """An optional tensor argument (None passes) must be contiguous, on
+    `device`, and of the given shape and dtype: the library takes raw device
+    addresses and cannot tell a host tensor or a short buffer from a good one."""
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+
+
+def _check_gdn_inputs(entry, q, k, v, gamma, beta, state, extra=()):
+    """q, k, v [B,H,T,S,D] on one device, gamma and beta fp32 [B,H,T], the
+    initial state fp32 [B,H,D,D] or None; `extra` holds (name, tensor) pairs
+    shaped and typed like q."""
+    import torch
+    if q.dim() != 5:
+        raise ValueError(f"{entry}: q, k, v must be [B, H, T, S, D]")
+    if not q.is_cuda:
+        raise ValueError(f"{entry}: q must be a device tensor")
+    B, H, T, S, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)) + tuple(extra):
+        _check(q.device, name, t, q.shape, q.dtype)
+    _check(q.device, "gamma", gamma, (B, H, T), torch.float32)
+    _check(q.device, "beta", beta, (B, H, T), torch.float32)
+    _check(q.device, "state", state, (B, H, D, D), torch.float32)
+
+
 def _flags(path: str, time_kernels: bool) -> int:
     if path not in ("auto", "direct"):
         raise ValueError('path must be "auto" or "direct"')
@@ -167,8 +204,7 @@ def _flags(path: str, time_kernels: bool) -> int:
 def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out, norms, workspace,
           stream, flags: int):
     import torch
-    if q.dim() != 5:
-        raise ValueError("q, k, v must be [B, H, T, S, D]")
+    _check_gdn_inputs(entry, q, k, v, gamma, beta, state_in, (("o", out),))
     B, H, T, S, D = q.shape
     if q.dtype == torch.bfloat16:
         io = BF16
@@ -178,17 +214,9 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
         io = FP8
     else:
         raise TypeError("q, k, v must be bfloat16, float32 or float8_e4m3fn")
-    for name, t in (("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
-    for name, t in (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("beta", beta)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-    if gamma.shape != (B, H, T) or beta.shape != (B, H, T) or gamma.dtype != torch.float32 \
-            or beta.dtype != torch.float32:
-        raise ValueError("gamma and beta must be float32 [B, H, T]")
+    _check(q.device, "state_out", state_out, (B, H, D, D), torch.float32)
+    _check(q.device, "norms", norms, (B, H, T), torch.float32)
+    _check(q.device, "workspace", workspace)
     desc = make_desc(B, H, T, S, D, io, beta_mode, flags)
     if out is None:
         out = torch.empty_like(q)
@@ -201,7 +229,7 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     fn = getattr(lib(), entry)
     st = fn(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma), _addr(beta), _addr(state_in),
-            _addr(out), _addr(state_out), _addr(norms), _addr(workspace), workspace.numel(),
+            _addr(out), _addr(state_out), _addr(norms), _addr(workspace), _nbytes(workspace),
             ctypes.c_void_p(stream))
     _raise(st)
     return out
@@ -259,12 +287,12 @@ def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, be
     Returns a dict with the requested gradients (dq, dk, dv bf16; dgamma, dbeta
     [B,H,T] and dstate [B,H,D,D] fp32)."""
     import torch
+    _check_gdn_inputs("frame_backward", q, k, v, gamma, beta, state, (("d_out", d_out),))
     B, H, T, S, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("d_out", d_out), ("gamma", gamma), ("beta", beta)):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if q.dtype != torch.bfloat16 or any(t.dtype != torch.bfloat16 for t in (k, v, d_out)):
+    if q.dtype != torch.bfloat16:
         raise TypeError("frame_backward takes bfloat16 q, k, v and d_out")
+    _check(q.device, "d_state_out", d_state_out, (B, H, D, D), torch.float32)
+    _check(q.device, "workspace", workspace)
     desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
     if workspace is None:
         n = backward_workspace_size(desc)
@@ -285,7 +313,7 @@ def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, be
     st = lib().gdn_frame_backward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma), _addr(beta),
                                   _addr(state), _addr(d_out), _addr(d_state_out), _addr(out["dq"]),
                                   _addr(out["dk"]), _addr(out["dv"]), _addr(out["dgamma"]), _addr(out["dbeta"]),
-                                  _addr(out["dstate"]), _addr(workspace), workspace.numel(),
+                                  _addr(out["dstate"]), _addr(workspace), _nbytes(workspace),
                                   ctypes.c_void_p(stream))
     _raise(st)
     return {k_: v_ for k_, v_ in out.items() if v_ is not None}
@@ -306,12 +334,13 @@ def frame_forward_train(q, k, v, gamma, beta, state=None, beta_mode="erase", out
     saved_size bytes, allocated when None), what frame_backward_saved needs.
     bf16, T <= 1024.  Returns (o, state_out, norms, saved)."""
     import torch
+    _check_gdn_inputs("frame_forward_train", q, k, v, gamma, beta, state, (("o", out),))
     B, H, T, S, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("beta", beta)):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+    if q.dtype != torch.bfloat16:
         raise TypeError("frame_forward_train takes bfloat16 q, k and v")
+    _check(q.device, "state_out", state_out, (B, H, D, D), torch.float32)
+    _check(q.device, "norms", norms, (B, H, T), torch.float32)
+    _check(q.device, "saved", saved)
     desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
     if saved is None:
         n = saved_size(desc)
@@ -328,7 +357,7 @@ def frame_forward_train(q, k, v, gamma, beta, state=None, beta_mode="erase", out
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _raise(lib().gdn_frame_forward_train(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
                                          _addr(beta), _addr(state), _addr(out), _addr(state_out), _addr(norms),
-                                         _addr(saved), saved.numel(), ctypes.c_void_p(stream)))
+                                         _addr(saved), _nbytes(saved), ctypes.c_void_p(stream)))
     return out, state_out, norms, saved
 
 
@@ -338,12 +367,15 @@ def frame_backward_saved(q, k, v, gamma, beta, saved, d_out, d_state_out=None, b
     """frame_backward from the `saved` buffer of frame_forward_train (no replay
     of the forward).  Returns the same dict as frame_backward."""
     import torch
+    _check_gdn_inputs("frame_backward_saved", q, k, v, gamma, beta, None, (("d_out", d_out),))
     B, H, T, S, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("d_out", d_out), ("gamma", gamma), ("beta", beta)):
-        if not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if q.dtype != torch.bfloat16 or any(t.dtype != torch.bfloat16 for t in (k, v, d_out)):
+    if q.dtype != torch.bfloat16:
         raise TypeError("frame_backward_saved takes bfloat16 q, k, v and d_out")
+    if saved is None:
+        raise ValueError("frame_backward_saved needs the saved buffer of frame_forward_train")
+    _check(q.device, "saved", saved)
+    _check(q.device, "d_state_out", d_state_out, (B, H, D, D), torch.float32)
+    _check(q.device, "workspace", workspace)
     desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
     if workspace is None:
         n = backward_saved_workspace_size(desc)
@@ -362,10 +394,10 @@ def frame_backward_saved(q, k, v, gamma, beta, saved, d_out, d_state_out=None, b
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib().gdn_frame_backward_saved(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
-                                        _addr(beta), _addr(saved), saved.numel(), _addr(d_out),
+                                        _addr(beta), _addr(saved), _nbytes(saved), _addr(d_out),
                                         _addr(d_state_out), _addr(out["dq"]), _addr(out["dk"]), _addr(out["dv"]),
                                         _addr(out["dgamma"]), _addr(out["dbeta"]), _addr(out["dstate"]),
-                                        _addr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+                                        _addr(workspace), _nbytes(workspace), ctypes.c_void_p(stream))
     _raise(st)
     return {k_: v_ for k_, v_ in out.items() if v_ is not None}
 
@@ -395,15 +427,18 @@ def tconv_forward(x, w, bias=None, chunk: int = 1, cache=None, out=None, cache_o
         raise TypeError(f"x must be bf16 or fp32, not {x.dtype}")
     if w.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
         raise TypeError("w and bias must be fp32")
-    for t in (x, w, bias, cache, out):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
-    if cache is not None and cache.dtype != x.dtype:
-        raise TypeError("cache must have the dtype of x")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    _check(x.device, "x", x)
+    _check(x.device, "w", w, (3, C), torch.float32)
+    _check(x.device, "bias", bias, (C,), torch.float32)
+    _check(x.device, "cache", cache, (B, S, C), x.dtype)
+    _check(x.device, "out", out, x.shape, x.dtype)
     if isinstance(cache_out, str):
         if cache_out != "inplace" or cache is None:
             raise ValueError('cache_out="inplace" needs a cache')
         cache_out = cache
+    _check(x.device, "cache_out", cache_out, (B, S, C), x.dtype)
     if out is None:
         out = torch.empty_like(x)
     desc = make_tconv_desc(B, T, S, C, chunk, dt, FLAG_TIME_KERNELS if time_kernels else 0)
@@ -445,9 +480,14 @@ def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, workspa
     Tk = k.shape[2]
     if k.shape[:2] != (B, H) or k.shape[3:] != (S, D):
         raise ValueError("k and v must match q in B, H, S and D")
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise TypeError("q, k and v must be contiguous bf16")
+    if not q.is_cuda:
+        raise ValueError("q must be a device tensor")
+    _check(q.device, "q", q, dtype=torch.bfloat16)
+    _check(q.device, "k", k, dtype=torch.bfloat16)
+    _check(q.device, "v", v, dtype=torch.bfloat16)
+    _check(q.device, "out", out, q.shape, torch.bfloat16)
+    if not isinstance(workspace, str):
+        _check(q.device, "workspace", workspace)
     if out is None:
         out = torch.empty_like(q)
     desc = make_attn_desc(B, H, Tq, Tk, S, D, chunk, BF16, FLAG_TIME_KERNELS if time_kernels else 0, scale)
@@ -459,6 +499,6 @@ def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, workspa
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _raise(lib().gdn_attention_forward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(out),
-                                       _addr(workspace), 0 if workspace is None else workspace.numel(),
+                                       _addr(workspace), _nbytes(workspace),
                                        ctypes.c_void_p(stream)))
     return out

@@ -377,6 +377,38 @@ def test_device_argument_errors(env):
     assert e.value.status == 4
 
 
+def test_binding_rejects_host_and_misshaped_tensors(env):
+    """The C ABI takes raw addresses, so the binding refuses, before any
+    launch, optional tensors that live on the host or are too short."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.Workload("bind", 1, 2, 3, 16, 16))
+    q, k, v, g, b = inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"]
+    host_state = torch.zeros((1, 2, 16, 16))
+    with pytest.raises(ValueError, match="state must be on"):
+        gdn.frame_forward(q, k, v, g, b, state=host_state)
+    with pytest.raises(ValueError, match="state_out must be on"):
+        gdn.frame_forward(q, k, v, g, b, state_out=host_state)
+    with pytest.raises(ValueError, match="gamma must have shape"):
+        gdn.frame_forward(q, k, v, g[:, :, :2].contiguous(), b)
+    with pytest.raises(ValueError, match="norms must have shape"):
+        gdn.frame_forward(q, k, v, g, b, norms=torch.empty((1, 2, 2), device="cuda"))
+    with pytest.raises(ValueError, match="workspace must be on"):
+        gdn.frame_forward(q, k, v, g, b, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="d_out must have shape"):
+        gdn.frame_backward(q, k, v, g, b, q[:, :, :2].contiguous())
+    with pytest.raises(ValueError, match="beta must have shape"):
+        gdn.frame_backward(q, k, v, g, b[:, :1].contiguous(), q)
+    x = torch.zeros((1, 3, 4, 8), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((3, 8), device="cuda")
+    with pytest.raises(ValueError, match="cache must be on"):
+        gdn.tconv_forward(x, w, cache=torch.zeros((1, 4, 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="w must have shape"):
+        gdn.tconv_forward(x, w[:2].contiguous())
+    with pytest.raises(ValueError, match="out must be on"):
+        gdn.attention_forward(q, k, v, 1, out=torch.empty(q.shape, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ OCP E4M3 I/O
 # O is rounded once from fp32 to E4M3.  For a normal value that rounding moves
 # it by at most half a unit in the last place, 2^-4 of its magnitude, so the
