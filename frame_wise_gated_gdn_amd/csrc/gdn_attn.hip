@@ -13,9 +13,11 @@
 // brought into a CU serves 256 queries: at 128 the kernel was bound by these
 // re-reads (about 5 TB/s of K/V per call at the 720p clip).
 //
-// The eight waves form two groups that run each tile's phases in different
-// orders (see the main loop), so that the softmax of one wave overlaps the
-// matrix products of the other wave on the same SIMD.
+// Each wave pipelines its own tiles: while it runs the softmax of key tile t
+// it issues the score products of tile t+1, interleaved instruction by
+// instruction (a second set of score registers), then the P V products of
+// tile t.  Its VALU and matrix pipe work together, and the other wave on the
+// SIMD fills what is left.
 //
 // Transposed formulation.  The wave computes S^T = K Q^T (keys as MFMA rows,
 // queries as columns) and O^T = V^T P^T, so that in every accumulator a lane
@@ -180,11 +182,13 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   };
 
   const float sl2 = a.scale_log2;
-  f32x4 S[NKT][NQ];
-  // S^T = K Q^T for one key tile: S[k16][qt], lane: query 16 qt + n, keys 16 k16 + 4 g + r
-  auto scores = [&](const uint16_t* kt) {
-    // K operands of the next 16-key group are read while the current group's
-    // products run
+  // Scores of two key tiles live at once: Sx of the tile whose softmax runs
+  // now, Sy of the next tile, whose products are issued in the same basic
+  // block as the exponentials of Sx so that one wave keeps its matrix pipe
+  // and its VALU busy together.
+  f32x4 S0[NKT][NQ], S1[NKT][NQ];
+  // S^T = K Q^T for one key tile: Sx[k16][qt], lane: query 16 qt + n, keys 16 k16 + 4 g + r
+  auto scores = [&](const uint16_t* kt, f32x4 (&Sx)[NKT][NQ]) {
     u32x4 A[2][NKC];
     auto read_a = [&](int buf, int k16) {
 #pragma unroll
@@ -198,19 +202,18 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
     for (int k16 = 0; k16 < NKT; ++k16) {
       if (k16 + 1 < NKT) read_a((k16 + 1) & 1, k16 + 1);
 #pragma unroll
-      for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < NQ; ++qt) Sx[k16][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) S[k16][qt] = mfma_bf16(A[k16 & 1][kc], QB[qt][kc], S[k16][qt]);
+        for (int qt = 0; qt < NQ; ++qt) Sx[k16][qt] = mfma_bf16(A[k16 & 1][kc], QB[qt][kc], Sx[k16][qt]);
     }
   };
-  // online softmax of the tile at key kb, then O += V^T P^T with the tile's V.
-  // Scores are masked only in the tiles that reach past the block end of the
-  // wave's first query (the smallest key end of the wave); the max is taken
-  // on raw scores and the scale folded into the exponent (scale > 0); when no
-  // lane's running max moved, the rescale factor is exactly 1 and is skipped.
-  auto softmax_pv = [&](int kb, const uint16_t* vt) {
+
+  // One key tile t (keys from kb): softmax of Sx, the next tile's scores into
+  // Sy (from the K tile at ktn), then O += V^T P^T with the tile's V (vt).
+  auto tile = [&](int kb, const uint16_t* vt, const uint16_t* ktn, f32x4 (&Sx)[NKT][NQ],
+                  f32x4 (&Sy)[NKT][NQ]) {
     if (kb + kAttnBN > kend_lo) {
 #pragma unroll
       for (int qt = 0; qt < NQ; ++qt)
@@ -218,38 +221,59 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
         for (int k16 = 0; k16 < NKT; ++k16)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (kb + 16 * k16 + 4 * g + r >= kend[qt]) S[k16][qt][r] = -INFINITY;
+            if (kb + 16 * k16 + 4 * g + r >= kend[qt]) Sx[k16][qt][r] = -INFINITY;
     }
-    u32x4 PB[NQ][NK2];
+    float mold[NQ], mnew[NQ];
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
       for (int k16 = 0; k16 < NKT; ++k16)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[k16][qt][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, Sx[k16][qt][r]);
       mx = wave_max4(mx);
-      const float mold = m[qt];
-      const float mnew = fmaxf(mold, mx * sl2);
-      m[qt] = mnew;
+      mold[qt] = m[qt];
+      mnew[qt] = fmaxf(mold[qt], mx * sl2);
+      m[qt] = mnew[qt];
+    }
+    // rescale before the products of the next tile, so that they, the
+    // exponentials and P V share one basic block
 #pragma unroll
-      for (int k16 = 0; k16 < NKT; ++k16)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[k16][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[k16][qt][r], sl2, -mnew));
-      if (__any(mnew > mold)) {
-        const float alpha = __builtin_amdgcn_exp2f(mold - mnew);
+    for (int qt = 0; qt < NQ; ++qt) {
+      if (__any(mnew[qt] > mold[qt])) {
+        const float alpha = __builtin_amdgcn_exp2f(mold[qt] - mnew[qt]);
         L[qt] *= alpha;
 #pragma unroll
         for (int db = 0; db < NB; ++db) O[qt][db] *= alpha;
       }
+    }
+    scores(ktn, Sy);
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt)
+#pragma unroll
+      for (int k16 = 0; k16 < NKT; ++k16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Sx[k16][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sx[k16][qt][r], sl2, -mnew[qt]));
+    // issue order: each product of the next tile followed by VALU
+    // instructions of this tile's exponentials (an fma and an exp per score),
+    // so the wave issues VALU work while its products run
+    constexpr int NSC = NKT * NKC * NQ;                  // products of one tile's scores
+    constexpr int VPS = (2 * NKT * 4 * NQ + NSC - 1) / NSC;
+#pragma unroll
+    for (int i = 0; i < NSC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, VPS, 0); // then VPS VALU instructions
+    }
+    u32x4 PB[NQ][NK2];
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt)
 #pragma unroll
       for (int k2 = 0; k2 < NK2; ++k2) {
-        const f32x4 lo = S[2 * k2][qt], hi = S[2 * k2 + 1][qt];
+        const f32x4 lo = Sx[2 * k2][qt], hi = Sx[2 * k2 + 1][qt];
         PB[qt][k2] = u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
                            pack_bf16(hi[2], hi[3])};
       }
-    }
     // A operand = V columns 16 db + n at keys 32 k2 + {4g..4g+3, 16+4g..16+4g+3};
     // the next column block's operands are read while the current one's run
     u32x4 VA[2][NK2];
@@ -270,8 +294,6 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
 #pragma unroll
         for (int qt = 0; qt < NQ; ++qt) O[qt][db] = mfma_bf16(VA[db & 1][k2], PB[qt][k2], O[qt][db]);
     }
-    // the softmax denominator on the matrix cores: a 16-row block of bf16 ones
-    // times P^T sums the same bf16 probabilities that weight V
     const u32x4 ONES = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 #pragma unroll
     for (int k2 = 0; k2 < NK2; ++k2)
@@ -279,16 +301,12 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
       for (int qt = 0; qt < NQ; ++qt) L[qt] = mfma_bf16(ONES, PB[qt][k2], L[qt]);
   };
 
-  // Two wave groups in opposite phase.  At the top of iteration t the LDS
-  // holds K tiles t and t+1 and V tile t.  Group A (waves 0-3) computes the
-  // scores of tile t, then its softmax and P V; group B (waves 4-7) has the
-  // scores of tile t from the previous iteration, does the softmax and P V
-  // first and the scores of tile t+1 last.  A SIMD runs one wave of each
-  // group, so one wave's softmax (VALU) meets the other's products (MFMA).
-  // Staging keeps K one tile ahead of V: iteration t stores K tile t+2
-  // (buffer (t+2)%3, last read for tile t-1) and V tile t+1 (buffer (t+1)%2,
-  // last read for tile t-1), then prefetches K t+3 and V t+2.
-  const bool grpB = w >= kAttnWaves / 2;
+  // At the top of iteration t the LDS holds K tiles t and t+1 and V tile t;
+  // the wave holds the scores of tile t.  Iteration t stores K tile t+2
+  // (buffer (t+2)%3, last read in iteration t-1) and V tile t+1 (buffer
+  // (t+1)%2, last read in iteration t-1), then prefetches K t+3 and V t+2.
+  // Past the last tile the loads read zeros and the stores stage them, so the
+  // next-tile scores of the last iteration (never used) read defined LDS.
   load_k(tb);
   load_v(tb);
   store_k(0);
@@ -298,29 +316,24 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   load_k(tb + 2);
   load_v(tb + 1);
   lds_barrier();
-  if (grpB && nt > 0) scores(kbuf_ptr(0));
-  int kb0 = 0, kb1 = 1, kb2 = 2;          // K buffers of tiles t, t+1, t+2
-  for (int it = 0; it < nt; ++it) {
+  if (nt > 0) scores(kbuf_ptr(0), S0);
+  int kb1 = 1, kb2 = 2;                   // K buffers of tiles t+1, t+2
+  auto iteration = [&](int it, f32x4 (&Sx)[NKT][NQ], f32x4 (&Sy)[NKT][NQ]) {
     const int t = tb + it;
     lds_barrier();
-    const uint16_t* vt = vbuf_ptr(it & 1);
-    if (!grpB) {
-      scores(kbuf_ptr(kb0));
-      softmax_pv(t * kAttnBN, vt);
-    } else {
-      softmax_pv(t * kAttnBN, vt);
-      if (it + 1 < nt) scores(kbuf_ptr(kb1));
-    }
-    if (it + 2 < nt) store_k(kb2);
-    if (it + 1 < nt) store_v((it + 1) & 1);
+    tile(t * kAttnBN, vbuf_ptr(it & 1), kbuf_ptr(kb1), Sx, Sy);
+    store_k(kb2);
+    store_v((it + 1) & 1);
     load_k(t + 3);
     load_v(t + 2);
-    const int kfree = kb0;
-    kb0 = kb1;
+    const int kfree = 3 - kb1 - kb2;      // buffer of tile t, free after this iteration
     kb1 = kb2;
     kb2 = kfree;
+  };
+  for (int it = 0; it < nt; it += 2) {
+    iteration(it, S0, S1);
+    if (it + 1 < nt) iteration(it + 1, S1, S0);
   }
-
   // lane holds O[query 16 qt + n][16 db + 4 g + r]
   if (a.split > 1) {
     // partial state of this key range: unnormalised O, running max and sum
