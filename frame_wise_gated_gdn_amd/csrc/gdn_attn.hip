@@ -67,9 +67,16 @@ struct AttnShape {
   static constexpr int UPR = D / 8;                // 16-byte units per token row
   static constexpr int UNITS = kAttnBN * UPR;      // units per K (or V) tile
   static constexpr int LPT = (UNITS + kAttnWaves * 64 - 1) / (kAttnWaves * 64);   // units per thread
-  static constexpr int RS = D + 8;                 // LDS row stride (elements)
+  // LDS row strides (elements).  K rows are read 16 bytes per lane, eight
+  // lanes (rows n..n+7) per pass: a stride of 112 modulo 128 bytes puts them
+  // on distinct banks.  V rows are read by the transposing 8-byte read, four
+  // rows of 32 bytes per 16 lanes: the stride must be 32 or 96 modulo 128
+  // bytes (and eight rows distinct modulo 256).
+  static constexpr int RS = D + 8;
+  static constexpr int RSV = (D % 64 == 16 || D % 64 == 48) ? D : D + 16;
   static constexpr size_t tile_bytes = (size_t)kAttnBN * RS * 2;
-  static constexpr size_t lds_bytes = 5 * tile_bytes;       // K x 3 buffers, V x 2 buffers
+  static constexpr size_t vtile_bytes = (size_t)kAttnBN * RSV * 2;
+  static constexpr size_t lds_bytes = 3 * tile_bytes + 2 * vtile_bytes;   // K x 3 buffers, V x 2 buffers
 };
 
 __device__ __forceinline__ float wave_max4(float x) {
@@ -88,7 +95,7 @@ template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a) {
   using Sh = AttnShape<D>;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, NQ = Sh::NQ, NKT = Sh::NKT, NK2 = Sh::NK2;
-  constexpr int UPR = Sh::UPR, UNITS = Sh::UNITS, LPT = Sh::LPT, RS = Sh::RS;
+  constexpr int UPR = Sh::UPR, UNITS = Sh::UNITS, LPT = Sh::LPT, RS = Sh::RS, RSV = Sh::RSV;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int Nq = a.Tq * a.S, Nk = a.Tk * a.S;
@@ -142,13 +149,15 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
 
   // K/V tile staging through registers.  A tile's rows are contiguous in HBM,
   // so unit u (16 bytes) sits 8u elements after the tile's first key; in LDS
-  // the rows are padded to RS elements (offset hoisted out of the tile loop).
+  // the rows are padded to RS (K) or RSV (V) elements (offsets hoisted out of
+  // the tile loop).
   u32x4 RK[LPT], RV[LPT];
-  int lds_u[LPT];
+  int lds_u[LPT], lds_v[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int u = tid + kAttnWaves * 64 * i;
     lds_u[i] = (u / UPR) * RS + 8 * (u % UPR);
+    lds_v[i] = (u / UPR) * RSV + 8 * (u % UPR);
   }
   // buffer loads: a unit past the head's keys (or past the last tile) reads zeros
   const uint32_t head_bytes = (uint32_t)Nk * D * 2;
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
   };
   // LDS: K buffers 0..2, then V buffers 0..1
   auto kbuf_ptr = [&](int b) { return (uint16_t*)(smem + (size_t)b * Sh::tile_bytes); };
-  auto vbuf_ptr = [&](int b) { return (uint16_t*)(smem + (size_t)(3 + b) * Sh::tile_bytes); };
+  auto vbuf_ptr = [&](int b) { return (uint16_t*)(smem + 3 * Sh::tile_bytes + (size_t)b * Sh::vtile_bytes); };
   auto store_k = [&](int b) {
     uint16_t* dst = kbuf_ptr(b);
 #pragma unroll
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
     uint16_t* dst = vbuf_ptr(b);
 #pragma unroll
     for (int i = 0; i < LPT; ++i)
-      if (tid + kAttnWaves * 64 * i < UNITS) *(u32x4*)(dst + lds_u[i]) = RV[i];
+      if (tid + kAttnWaves * 64 * i < UNITS) *(u32x4*)(dst + lds_v[i]) = RV[i];
   };
 
   const float sl2 = a.scale_log2;
@@ -280,8 +289,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void gdn_attn_kernel(AttnArgs a
     auto read_v = [&](int buf, int db) {
 #pragma unroll
       for (int k2 = 0; k2 < NK2; ++k2) {
-        const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RS + 16 * db + 4 * (n & 3);
-        const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
+        const uint16_t* p0 = vt + (32 * k2 + 4 * g + (n >> 2)) * RSV + 16 * db + 4 * (n & 3);
+        const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RSV);
         VA[buf][k2] = u32x4{x[0], x[1], y[0], y[1]};
       }
     };
