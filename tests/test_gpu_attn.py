@@ -48,7 +48,8 @@ def check_head(o, q, k, v, S, chunk, ao, scale=None):
                                                  (2, 1, 4, 4, 64, 128, 4), (1, 2, 3, 3, 50, 16, 100),
                                                  (1, 1, 2, 9, 33, 48, 3), (1, 3, 1, 1, 200, 32, 1),
                                                  (1, 1, 7, 7, 19, 80, 2), (1, 1, 4, 4, 128, 96, 1),
-                                                 (1, 1, 1, 6, 70, 112, 4)])
+                                                 (1, 1, 1, 6, 70, 112, 4), (1, 1, 2, 2, 20, 64, 1),
+                                                 (1, 2, 1, 1, 64, 112, 1), (1, 1, 3, 3, 1, 128, 2)])
 def test_attention_parity(env, B, H, Tq, Tk, S, D, chunk):
     torch, gdn, wl, ao = env
     w = wl.AttnWorkload("a", B, H, Tq, Tk, S, D, chunk)
