@@ -139,10 +139,12 @@ def test_attention_720p_clip_sampled_queries(env):
 
 
 @pytest.mark.parametrize("B,H,Tq,Tk,S,D,chunk", [(1, 2, 1, 40, 64, 64, 4), (1, 1, 2, 30, 70, 112, 2),
-                                                 (2, 1, 1, 25, 100, 128, 1)])
+                                                 (2, 1, 1, 25, 100, 128, 1), (1, 1, 16, 40, 64, 64, 1)])
 def test_attention_key_split_parity(env, B, H, Tq, Tk, S, D, chunk):
     """With a workspace, launches with few query tiles split the keys over
-    workgroups and merge the partial (max, sum, O) states."""
+    workgroups and merge the partial (max, sum, O) states.  In the last case
+    (5 parts of 8 key tiles on 256 CUs) the first query tile sees 28 tiles,
+    so its last part has none and must merge with weight zero."""
     torch, gdn, wl, ao = env
     desc = gdn.make_attn_desc(B, H, Tq, Tk, S, D, chunk)
     assert gdn.attention_workspace_size(desc) > 0, "this shape should split its keys"
