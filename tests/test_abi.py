@@ -395,3 +395,15 @@ def test_training_pair_host_checks(gdn):
     assert bw(sv, n_saved, ws, n_ws - 1) == 8
     assert bw(sv + 8, n_saved, ws, n_ws) == 4
     assert bw(sv, n_saved, ws, n_ws, dq_=sv + 256) == 5   # dq overlaps saved
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it says so and exits non-zero
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout + r.stderr
