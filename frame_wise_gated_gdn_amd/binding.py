@@ -195,6 +195,23 @@ def _check_gdn_inputs(entry, q, k, v, gamma, beta, state, extra=()):
     _check(q.device, "state", state, (B, H, D, D), torch.float32)
 
 
+def _stream_and_alloc(stream, device):
+    """(stream handle, context for the call's allocations).
+
+    Workspaces and outputs that the binding allocates are made while the
+    call's stream is torch's current stream, so that the caching allocator
+    ties them to that stream: when the binding drops a workspace, its memory
+    goes back to that stream's pool and is handed out again only in stream
+    order, never while the library's kernels on that stream still use it.
+    With stream=None the call runs on the current stream and nothing changes."""
+    import contextlib
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream, contextlib.nullcontext()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return handle, torch.cuda.stream(torch.cuda.ExternalStream(handle, device=device))
+
+
 def _flags(path: str, time_kernels: bool) -> int:
     if path not in ("auto", "direct"):
         raise ValueError('path must be "auto" or "direct"')
@@ -218,15 +235,15 @@ def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out,
     _check(q.device, "norms", norms, (B, H, T), torch.float32)
     _check(q.device, "workspace", workspace)
     desc = make_desc(B, H, T, S, D, io, beta_mode, flags)
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        n = workspace_size(desc)
-        if n == 0:
-            _raise(lib().gdn_check_args(ctypes.byref(desc), *([None] * 10), 0, 0))
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream, on_stream = _stream_and_alloc(stream, q.device)
+    with on_stream:
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            n = workspace_size(desc)
+            if n == 0:
+                _raise(lib().gdn_check_args(ctypes.byref(desc), *([None] * 10), 0, 0))
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     fn = getattr(lib(), entry)
     st = fn(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma), _addr(beta), _addr(state_in),
             _addr(out), _addr(state_out), _addr(norms), _addr(workspace), _nbytes(workspace),
@@ -243,10 +260,11 @@ def frame_forward(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None,
     recurrence for bf16 (GDN_FLAG_DIRECT).  Returns (o, state_out, norms)."""
     import torch
     B, H, T, S, D = q.shape
-    if state_out is None and want_state:
-        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
-    if norms is None and want_norms:
-        norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    with _stream_and_alloc(stream, q.device)[1]:
+        if state_out is None and want_state:
+            state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if norms is None and want_norms:
+            norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     out = _call("gdn_frame_forward", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
                 workspace, stream, _flags(path, time_kernels))
     return out, state_out, norms
@@ -269,7 +287,8 @@ def frame_step(q, k, v, gamma, beta, state, beta_mode="erase", out=None, state_o
     elif commit == "peek":
         state_out = None
     elif state_out is None:
-        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        with _stream_and_alloc(stream, q.device)[1]:
+            state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     out = _call("gdn_frame_step", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
                 workspace, stream, _flags(path, time_kernels))
     return out, state_out, norms
@@ -294,22 +313,14 @@ def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, be
     _check(q.device, "d_state_out", d_state_out, (B, H, D, D), torch.float32)
     _check(q.device, "workspace", workspace)
     desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
-    if workspace is None:
-        n = backward_workspace_size(desc)
-        if n == 0:
-            raise GDNError(6, "frame_backward: unsupported shape (bf16 only, T <= 1024)")
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    out = {}
-    like = lambda: torch.empty_like(q)
-    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
-    out["dq"] = like() if "dq" in want else None
-    out["dk"] = like() if "dk" in want else None
-    out["dv"] = like() if "dv" in want else None
-    out["dgamma"] = f32(B, H, T) if "dgamma" in want else None
-    out["dbeta"] = f32(B, H, T) if "dbeta" in want else None
-    out["dstate"] = f32(B, H, D, D) if "dstate" in want else None
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream, on_stream = _stream_and_alloc(stream, q.device)
+    with on_stream:
+        if workspace is None:
+            n = backward_workspace_size(desc)
+            if n == 0:
+                raise GDNError(6, "frame_backward: unsupported shape (bf16 only, T <= 1024)")
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+        out = _grad_outputs(q, want)
     st = lib().gdn_frame_backward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma), _addr(beta),
                                   _addr(state), _addr(d_out), _addr(d_state_out), _addr(out["dq"]),
                                   _addr(out["dk"]), _addr(out["dv"]), _addr(out["dgamma"]), _addr(out["dbeta"]),
@@ -317,6 +328,18 @@ def frame_backward(q, k, v, gamma, beta, d_out, state=None, d_state_out=None, be
                                   ctypes.c_void_p(stream))
     _raise(st)
     return {k_: v_ for k_, v_ in out.items() if v_ is not None}
+
+
+def _grad_outputs(q, want):
+    """Gradient tensors of the backward calls (None for those not wanted)."""
+    import torch
+    B, H, T, S, D = q.shape
+    like = lambda: torch.empty_like(q)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
+    return {"dq": like() if "dq" in want else None, "dk": like() if "dk" in want else None,
+            "dv": like() if "dv" in want else None, "dgamma": f32(B, H, T) if "dgamma" in want else None,
+            "dbeta": f32(B, H, T) if "dbeta" in want else None,
+            "dstate": f32(B, H, D, D) if "dstate" in want else None}
 
 
 def saved_size(desc: Desc) -> int:
@@ -342,19 +365,19 @@ def frame_forward_train(q, k, v, gamma, beta, state=None, beta_mode="erase", out
     _check(q.device, "norms", norms, (B, H, T), torch.float32)
     _check(q.device, "saved", saved)
     desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
-    if saved is None:
-        n = saved_size(desc)
-        if n == 0:
-            raise GDNError(6, "frame_forward_train: unsupported shape (bf16 only, T <= 1024)")
-        saved = torch.empty(n, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if state_out is None and want_state:
-        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
-    if norms is None and want_norms:
-        norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream, on_stream = _stream_and_alloc(stream, q.device)
+    with on_stream:
+        if saved is None:
+            n = saved_size(desc)
+            if n == 0:
+                raise GDNError(6, "frame_forward_train: unsupported shape (bf16 only, T <= 1024)")
+            saved = torch.empty(n, dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty_like(q)
+        if state_out is None and want_state:
+            state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        if norms is None and want_norms:
+            norms = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     _raise(lib().gdn_frame_forward_train(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
                                          _addr(beta), _addr(state), _addr(out), _addr(state_out), _addr(norms),
                                          _addr(saved), _nbytes(saved), ctypes.c_void_p(stream)))
@@ -377,22 +400,14 @@ def frame_backward_saved(q, k, v, gamma, beta, saved, d_out, d_state_out=None, b
     _check(q.device, "d_state_out", d_state_out, (B, H, D, D), torch.float32)
     _check(q.device, "workspace", workspace)
     desc = make_desc(B, H, T, S, D, BF16, beta_mode, FLAG_TIME_KERNELS if time_kernels else 0)
-    if workspace is None:
-        n = backward_saved_workspace_size(desc)
-        if n == 0:
-            raise GDNError(6, "frame_backward_saved: unsupported shape (bf16 only, T <= 1024)")
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
-    out = {}
-    like = lambda: torch.empty_like(q)
-    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=q.device)
-    out["dq"] = like() if "dq" in want else None
-    out["dk"] = like() if "dk" in want else None
-    out["dv"] = like() if "dv" in want else None
-    out["dgamma"] = f32(B, H, T) if "dgamma" in want else None
-    out["dbeta"] = f32(B, H, T) if "dbeta" in want else None
-    out["dstate"] = f32(B, H, D, D) if "dstate" in want else None
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    stream, on_stream = _stream_and_alloc(stream, q.device)
+    with on_stream:
+        if workspace is None:
+            n = backward_saved_workspace_size(desc)
+            if n == 0:
+                raise GDNError(6, "frame_backward_saved: unsupported shape (bf16 only, T <= 1024)")
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+        out = _grad_outputs(q, want)
     st = lib().gdn_frame_backward_saved(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
                                         _addr(beta), _addr(saved), _nbytes(saved), _addr(d_out),
                                         _addr(d_state_out), _addr(out["dq"]), _addr(out["dk"]), _addr(out["dv"]),
@@ -439,11 +454,11 @@ def tconv_forward(x, w, bias=None, chunk: int = 1, cache=None, out=None, cache_o
             raise ValueError('cache_out="inplace" needs a cache')
         cache_out = cache
     _check(x.device, "cache_out", cache_out, (B, S, C), x.dtype)
-    if out is None:
-        out = torch.empty_like(x)
+    stream, on_stream = _stream_and_alloc(stream, x.device)
+    with on_stream:
+        if out is None:
+            out = torch.empty_like(x)
     desc = make_tconv_desc(B, T, S, C, chunk, dt, FLAG_TIME_KERNELS if time_kernels else 0)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
     st = lib().gdn_tconv_forward(ctypes.byref(desc), _addr(x), _addr(w), _addr(bias), _addr(cache), _addr(out),
                                  _addr(cache_out), ctypes.c_void_p(stream))
     _raise(st)
@@ -488,16 +503,16 @@ def attention_forward(q, k, v, chunk: int, scale: float = 0.0, out=None, workspa
     _check(q.device, "out", out, q.shape, torch.bfloat16)
     if not isinstance(workspace, str):
         _check(q.device, "workspace", workspace)
-    if out is None:
-        out = torch.empty_like(q)
     desc = make_attn_desc(B, H, Tq, Tk, S, D, chunk, BF16, FLAG_TIME_KERNELS if time_kernels else 0, scale)
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError('workspace must be None, "auto" or a tensor')
-        nbytes = attention_workspace_size(desc)
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if isinstance(workspace, str) and workspace != "auto":
+        raise ValueError('workspace must be None, "auto" or a tensor')
+    stream, on_stream = _stream_and_alloc(stream, q.device)
+    with on_stream:
+        if out is None:
+            out = torch.empty_like(q)
+        if isinstance(workspace, str):
+            nbytes = attention_workspace_size(desc)
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     _raise(lib().gdn_attention_forward(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(out),
                                        _addr(workspace), _nbytes(workspace),
                                        ctypes.c_void_p(stream)))

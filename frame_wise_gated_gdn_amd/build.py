@@ -16,22 +16,40 @@ DEV_HEADERS = [os.path.join(CSRC, "gdn_device.h")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_internal.h"), *DEV_HEADERS]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+OBJ_DIR = os.path.join(PKG, "_build")
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *SOURCES, "-o", LIB + ".tmp"]
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+    def compile_one(src):
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *inc, "-c", src, "-o", obj]
+        return cmd, subprocess.run(cmd, capture_output=True, text=True), obj
+
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    for cmd, r, _ in results:
+        if verbose or r.returncode != 0:
+            sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
+    if any(r.returncode != 0 for _, r, _ in results):
+        raise RuntimeError("hipcc failed building libgdn.so")
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, _, o in results], "-o", LIB + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or r.returncode != 0:
         sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed building libgdn.so")
+        raise RuntimeError("hipcc failed linking libgdn.so")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

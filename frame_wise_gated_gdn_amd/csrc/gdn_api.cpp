@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -121,6 +122,9 @@ std::vector<TimedKernel> g_timed;          // recorded, not read yet
 std::vector<hipEvent_t> g_free_events;     // timing events ready for reuse
 double g_time_ms[GDN_KERNEL_SLOTS] = {};
 int64_t g_time_n[GDN_KERNEL_SLOTS] = {};
+// Unread records are capped: past this many, timed calls launch their kernels
+// untimed until gdn_kernel_times has read the record.
+constexpr size_t kMaxTimed = size_t(1) << 16;
 
 hipError_t take_timing_event(hipEvent_t* e) {
   {
@@ -143,6 +147,10 @@ void give_timing_event(hipEvent_t e) {
 // `timed`.
 template <class Fn>
 hipError_t launch_timed(bool timed, int slot, hipStream_t s, Fn&& fn) {
+  if (timed) {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    if (g_timed.size() >= kMaxTimed) timed = false;
+  }
   if (!timed) return fn();
   TimedKernel tk{slot, {nullptr, nullptr}};
   hipError_t e = take_timing_event(&tk.ev[0]);
@@ -194,6 +202,17 @@ constexpr double kStateGrow = 1.4;      // size ratio of consecutive sub-ranges
 struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t ev[kStateSplit + 2] = {};
+  SideStream() = default;
+  SideStream(const SideStream&) = delete;
+  SideStream& operator=(const SideStream&) = delete;
+  // Released when the owning thread exits.  Work already enqueued is not
+  // affected: a stream or event destroyed while in use is freed by the
+  // runtime once that work completes.
+  ~SideStream() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    if (stream) (void)hipStreamDestroy(stream);
+  }
 };
 
 // Sub-range boundaries bnd[0] = 0 < ... < bnd[n] = tc of a gram range, sizes
@@ -213,22 +232,22 @@ int split_frames(int tc, int bnd[kStateSplit + 1]) {
   bnd[n] = tc;
   return n;
 }
-thread_local std::vector<SideStream*> t_side;   // by device id
+thread_local std::vector<std::unique_ptr<SideStream>> t_side;   // by device id
 
 hipError_t side_stream(SideStream** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if ((int)t_side.size() <= dev) t_side.resize(dev + 1, nullptr);
+  if ((int)t_side.size() <= dev) t_side.resize(dev + 1);
   if (!t_side[dev]) {
-    SideStream* ss = new SideStream();
+    std::unique_ptr<SideStream> ss(new SideStream());
     e = hipStreamCreateWithFlags(&ss->stream, hipStreamNonBlocking);
     for (hipEvent_t& ev : ss->ev)
       if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) return e;   // a partly built side stream is not kept
-    t_side[dev] = ss;
+    if (e != hipSuccess) return e;   // a partly built side stream is released here
+    t_side[dev] = std::move(ss);
   }
-  *out = t_side[dev];
+  *out = t_side[dev].get();
   return hipSuccess;
 }
 

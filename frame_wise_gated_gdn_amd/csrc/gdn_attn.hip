@@ -411,13 +411,13 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const long long nqt = (Nq + kAttnBM - 1) / kAttnBM;
   const long long blocks = nqt * a.BH * a.split;
   if (blocks > 0x7fffffffLL || a.split < 1) return hipErrorInvalidConfiguration;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gdn_attn_kernel<D>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
+    return hipFuncSetAttribute((const void*)gdn_attn_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)Sh::lds_bytes);
+  }, &li);
+  if (ie != hipSuccess) return ie;
   hipLaunchKernelGGL(gdn_attn_kernel<D>, dim3((unsigned)blocks), dim3(kAttnWaves * 64), Sh::lds_bytes, stream, a);
   if (a.split > 1) {
     const long long threads = (long long)a.BH * Nq * (D / 8);

@@ -259,16 +259,17 @@ __global__ __launch_bounds__(kDvkWaves * 64, 2) void gdn_dvdk_kernel(DvkArgs a) 
 
 template <int D>
 static hipError_t launch_dvdk_t(const DvkArgs& da, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
     hipError_t e = hipFuncSetAttribute((const void*)gdn_dvdk_kernel<D, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)DvkShape<D>::lds_bytes);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gdn_dvdk_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)DvkShape<D>::lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
   const dim3 grid((unsigned)(da.BH * da.Tc)), block(kDvkWaves * 64);
   if (da.beta_mode == 0)
     hipLaunchKernelGGL((gdn_dvdk_kernel<D, false>), grid, block, DvkShape<D>::lds_bytes, stream, da);

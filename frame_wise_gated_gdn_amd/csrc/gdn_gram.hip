@@ -1009,10 +1009,9 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_adjoint_bf16_kernel(Adjoin
 template <int D, bool FP8>
 static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
   constexpr int NW = GramShape<D>::NW;
-  static bool attr_set = false;   // benign race: every setter writes the same value
-  static int slots = 0;            // resident workgroups of the streaming kernel on the device
-  static int cus = 0;
-  if (!attr_set) {
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int dev, LaunchInfo& info) {
     hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
     if (e == hipSuccess)
@@ -1021,16 +1020,16 @@ static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gdn_gram_stream_kernel<D, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramStream<D>::lds_bytes);
-    int dev = 0, per_cu = 0;
-    if (e == hipSuccess) e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int per_cu = 0;
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)gdn_gram_stream_kernel<D, FP8>,
                                                        GramShape<D>::NW * 64, GramStream<D>::lds_bytes);
-    if (e != hipSuccess) return e;
-    slots = std::max(1, per_cu) * cus;
-    attr_set = true;
-  }
+    info.slots = std::max(1, per_cu) * info.cus;
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
+  const int cus = li.cus, slots = li.slots;
   const long long nfh = (long long)ga.BH * ga.Tc;
   const int nch = (ga.S + 31) / 32;
   if (nfh <= 2 * cus) {
@@ -1057,16 +1056,17 @@ static hipError_t launch_gram_t(const GramArgs& ga, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_state_t(const StateArgs& sa, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
     hipError_t e = hipFuncSetAttribute((const void*)gdn_state_bf16_kernel<D, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)gdn_state_bf16_kernel<D, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gdn_state_bf16_kernel<D, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
   const int units = sa.BH * (D / 16);
   const int grid = 8 * ((units + 7) / 8);
   if (sa.beta_mode == 0)
@@ -1080,15 +1080,14 @@ static hipError_t launch_state_t(const StateArgs& sa, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_cdq_t(const CdqArgs& ca, hipStream_t stream) {
-  static bool attr_set = false;
-  const size_t lds = 5 * GramShape<D>::tile_bytes;   // Q, dO x 2 buffers; dQ tile
+  constexpr size_t lds = 5 * GramShape<D>::tile_bytes;   // Q, dO x 2 buffers; dQ tile
   static_assert((size_t)D * D * 2 <= 4 * GramShape<D>::tile_bytes, "snapshot staged in the tiles' space");
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gdn_cdq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
+    return hipFuncSetAttribute((const void*)gdn_cdq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  }, &li);
+  if (ie != hipSuccess) return ie;
   hipLaunchKernelGGL((gdn_cdq_kernel<D>), dim3((unsigned)(ca.BH * ca.Tc)), dim3(GramShape<D>::NW * 64), lds, stream,
                      ca);
   return hipGetLastError();
@@ -1096,16 +1095,17 @@ static hipError_t launch_cdq_t(const CdqArgs& ca, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_adjoint_t(const AdjointArgs& aa, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
     hipError_t e = hipFuncSetAttribute((const void*)gdn_adjoint_bf16_kernel<D, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gdn_adjoint_bf16_kernel<D, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)StateShape<D>::lds_bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
   const int units = aa.BH * (D / 16);
   const int grid = 8 * ((units + 7) / 8);
   if (aa.beta_mode == 0)

@@ -5,7 +5,42 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <map>
+#include <mutex>
+
 namespace gdn {
+
+// One-time, per-device setup of a kernel launcher (function attributes,
+// occupancy, CU count), safe when several host threads make their first
+// call at once: the first caller on a device runs `init(dev, info)` under the
+// lock; later callers get the cached result.  A failed init is not cached.
+struct LaunchInfo {
+  int cus = 0;     // compute units of the device
+  int slots = 0;   // resident workgroups of the launcher's persistent kernel, if any
+};
+class DeviceOnce {
+ public:
+  template <class Init>
+  hipError_t get(Init&& init, LaunchInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu_);
+    auto it = done_.find(dev);
+    if (it == done_.end()) {
+      LaunchInfo info;
+      e = init(dev, info);
+      if (e != hipSuccess) return e;
+      it = done_.emplace(dev, info).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+  }
+
+ private:
+  std::mutex mu_;
+  std::map<int, LaunchInfo> done_;
+};
 
 // Frames per launch are capped so that per-frame scalars fit in LDS.
 constexpr int kMaxFramesPerLaunch = 1024;

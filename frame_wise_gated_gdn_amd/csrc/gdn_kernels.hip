@@ -717,22 +717,23 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
 // ----------------------------------------------------------------------------
 template <int D, bool BF16>
 static hipError_t launch_recurrence_t(const RecurArgs& ra, hipStream_t stream) {
-  static bool attr_set = false;   // benign race: every setter writes the same value
-  if (!attr_set) {
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
     hipError_t e = hipSuccess;
     if constexpr (BF16) {
       e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)BfShape<D>::lds_bytes);
-      if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)BfShape<D>::lds_bytes);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)gdn_recur_bf16_kernel<D, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)BfShape<D>::lds_bytes);
     } else {
       e = hipFuncSetAttribute((const void*)gdn_recur_f32_kernel<D>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)RecurShapeF32<D>::lds_bytes);
     }
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
   const int grid = 8 * ((ra.units + 7) / 8);
   if constexpr (BF16) {
     if (ra.beta_mode == 0)
@@ -751,29 +752,27 @@ static hipError_t launch_recurrence_t(const RecurArgs& ra, hipStream_t stream) {
 template <int D, bool BF16>
 static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
   constexpr int RW = kReadWaves;
-  static bool attr_set = false;
-  static int cus = 0;
-  if (!attr_set) {
-    hipError_t e;
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int dev, LaunchInfo& info) {
+    hipError_t e = hipSuccess;
     if constexpr (BF16) {
       const void* fns[4] = {(const void*)gdn_readout_kernel<D, false, RW>, (const void*)gdn_readout_kernel<D, true, RW>,
                             (const void*)gdn_readout_kernel<D, false, 2 * RW>,
                             (const void*)gdn_readout_kernel<D, true, 2 * RW>};
       const size_t lds[4] = {ReadShape<D>::lds_bytes(RW), ReadShape<D>::lds_bytes(RW),
                              ReadShape<D>::lds_bytes(2 * RW), ReadShape<D>::lds_bytes(2 * RW)};
-      e = hipSuccess;
       for (int i = 0; i < 4 && e == hipSuccess; ++i)
         e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i]);
     } else {
       e = hipFuncSetAttribute((const void*)gdn_readout_f32_kernel<D>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, D * (D + 1) * 4);
     }
-    int dev = 0;
-    if (e == hipSuccess) e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
+  const int cus = li.cus;
   const unsigned grid = (unsigned)(ro.BH * ro.Tc);
   if constexpr (BF16) {
     // bf16 snapshots: bf16 or e4m3 Q and O; a launch with fewer frames than

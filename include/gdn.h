@@ -33,9 +33,18 @@
  * Conventions.
  *   - Ownership: the caller owns every buffer.  The library never allocates
  *     device memory; scratch space comes in through `workspace`.
- *   - Streams: every call only enqueues work on `stream` (a hipStream_t;
- *     NULL = the default stream) and returns without synchronising.
- *     Device faults surface at the caller's next synchronisation.
+ *   - Streams: every call enqueues work and returns without synchronising;
+ *     `stream` is a hipStream_t (NULL = the default stream).  Device faults
+ *     surface at the caller's next synchronisation.  The bf16/e4m3 forward,
+ *     the training pair and the backward also run part of their kernels on
+ *     a side stream of the library's own: one non-blocking stream at default
+ *     priority per (host thread, device), created on the thread's first such
+ *     call and released when the thread exits.  Its work starts after
+ *     everything enqueued on `stream` before the call and is finished before
+ *     anything enqueued on `stream` after the call returns (event waits on
+ *     both sides), so the call behaves as if it ran on `stream` alone.  Two
+ *     calls on different caller streams from one host thread share that side
+ *     stream, which orders their side-stream parts one after the other.
  *   - Errors: arguments are checked on the host before anything is launched;
  *     a failing check returns a status and launches nothing.  The library
  *     never aborts.  gdn_last_error() gives a per-thread message.
@@ -338,6 +347,8 @@ gdn_status gdn_attention_check_args(const gdn_attn_desc* d, const void* q, const
  * since the last reset: per kernel kind (GDN_KERNEL_*) the total milliseconds
  * and the number of launches.  Either pointer may be NULL.  Synchronises with
  * the recorded events.  `reset` != 0 clears the record after reading.
+ * At most 65536 timed launches are kept unread; past that, timed calls launch
+ * their kernels untimed until this call has read the record.
  * Returns GDN_OK or GDN_ERR_HIP.
  */
 gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_out[GDN_KERNEL_SLOTS],

@@ -587,3 +587,24 @@ def test_fp8_minute_720p_sampled_heads(env):
     out, st, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
     torch.cuda.synchronize()
     check_fp8(env, out, st, run_oracle(env, inp, heads=[(0, 0), (0, 19)]))
+
+
+def test_call_on_a_separate_stream(env):
+    """A call on a stream other than torch's current one: the binding allocates
+    the workspace and outputs on that stream, so memory it frees right after the
+    call is not handed to work on the current stream while the call's kernels
+    still run.  The current stream then allocates and fills memory at once;
+    the result must equal a call made on the current stream."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.Workload("side", 1, 4, 40, 300, 64, gamma=(0.9, 1.0), beta=(0.2, 1.0)))
+    ref = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True,
+                            stream=side)
+    junk = [torch.full((1 << 22,), 7, dtype=torch.int32, device="cuda") for _ in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
