@@ -18,8 +18,9 @@ F32, BF16, FP8 = 0, 1, 2          # gdn_dtype; FP8 = OCP E4M3
 ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
 FLAG_DIRECT = 0x2
+FLAG_THREE_PASS = 0x4
 # kernel kinds of gdn_kernel_times, in slot order
-KERNELS = ("recurrence", "readout", "gram", "state", "backward", "tconv", "attention")
+KERNELS = ("recurrence", "readout", "gram", "state", "backward", "tconv", "attention", "fused")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
           5: "GDN_ERR_ALIAS", 6: "GDN_ERR_UNSUPPORTED", 7: "GDN_ERR_ABI", 8: "GDN_ERR_WORKSPACE",
           9: "GDN_ERR_HIP"}
@@ -213,9 +214,13 @@ def _stream_and_alloc(stream, device):
 
 
 def _flags(path: str, time_kernels: bool) -> int:
-    if path not in ("auto", "direct"):
-        raise ValueError('path must be "auto" or "direct"')
-    return (FLAG_TIME_KERNELS if time_kernels else 0) | (FLAG_DIRECT if path == "direct" else 0)
+    """path: "auto" (the one-launch forward where the device allows it),
+    "three_pass" (the Gram pipeline as three launches) or "direct" (the
+    single-pass recurrence)."""
+    if path not in ("auto", "direct", "three_pass"):
+        raise ValueError('path must be "auto", "three_pass" or "direct"')
+    return ((FLAG_TIME_KERNELS if time_kernels else 0) | (FLAG_DIRECT if path == "direct" else 0) |
+            (FLAG_THREE_PASS if path == "three_pass" else 0))
 
 
 def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out, norms, workspace,

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_api.cpp"), os.path.join(CSRC, "gdn_kernels.hip"),
            os.path.join(CSRC, "gdn_gram.hip"), os.path.join(CSRC, "gdn_backward.hip"),
-           os.path.join(CSRC, "gdn_tconv.hip"), os.path.join(CSRC, "gdn_attn.hip")]
+           os.path.join(CSRC, "gdn_tconv.hip"), os.path.join(CSRC, "gdn_attn.hip"),
+           os.path.join(CSRC, "gdn_fused.hip")]
 DEV_HEADERS = [os.path.join(CSRC, "gdn_device.h")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_internal.h"), *DEV_HEADERS]
 

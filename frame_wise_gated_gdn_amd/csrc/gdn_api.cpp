@@ -79,7 +79,7 @@ gdn_status check_desc(const gdn_desc* d) {
     return fail(GDN_ERR_DTYPE, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_FP8_E4M3", d->io_dtype);
   if (d->beta_mode != GDN_BETA_ERASE && d->beta_mode != GDN_BETA_WRITE)
     return fail(GDN_ERR_DTYPE, "beta_mode %d is not GDN_BETA_ERASE or GDN_BETA_WRITE", d->beta_mode);
-  if (d->flags & ~(GDN_FLAG_TIME_KERNELS | GDN_FLAG_DIRECT))
+  if (d->flags & ~(GDN_FLAG_TIME_KERNELS | GDN_FLAG_DIRECT | GDN_FLAG_THREE_PASS))
     return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
   if ((d->flags & GDN_FLAG_DIRECT) && d->io_dtype == GDN_FP8_E4M3)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_FLAG_DIRECT is for bf16 I/O; e4m3 I/O runs the Gram pipeline only");
@@ -379,6 +379,74 @@ gdn_status run_direct(const gdn_desc* d, const Plan& p, const Ptrs& x, void* wor
   return GDN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// One-launch forward (gdn_fused.hip).  Heads are dealt to the XCDs (head h on
+// XCD h mod NX); two workgroups per CU; each XCD needs at least as many stream
+// workgroups as chain workgroups.  Ring sizes follow from how many frame
+// blocks the XCD's stream workgroups keep in flight: the readout lag L covers
+// them (so that a readout rarely waits for its state), the gram ring a few
+// frames more (so that a finished gram item rarely waits for its slot).
+// ---------------------------------------------------------------------------
+struct FusedPlan {
+  bool ok = false;
+  int nx = 0, grid = 0, RG = 0, RM = 0, L = 0;
+  size_t ctl = 0, gring = 0, mring = 0, total = 0;
+};
+
+FusedPlan make_fused_plan(const gdn_desc* d) {
+  FusedPlan f;
+  if (d->io_dtype == GDN_F32 || (d->flags & (GDN_FLAG_DIRECT | GDN_FLAG_THREE_PASS))) return f;
+  static gdn::DeviceOnce once;
+  gdn::LaunchInfo li;
+  const hipError_t e = once.get([](int dev, gdn::LaunchInfo& info) {
+    hipError_t r = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (r == hipSuccess) r = hipDeviceGetAttribute(&info.slots, hipDeviceAttributeNumberOfXccs, dev);
+    int coop = 0;
+    if (r == hipSuccess) r = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (r == hipSuccess && !coop) info.slots = 0;
+    return r;
+  }, &li);
+  if (e != hipSuccess || li.slots < 1 || li.slots > 16 || li.cus < 2 * li.slots || li.cus % li.slots != 0) return f;
+  const int nx = li.slots, per_x = 2 * li.cus / nx;                // two workgroups per CU
+  const long long bh = (long long)d->B * d->H;
+  const int cw = (d->D / 16 + gdn::kFusedWaves - 1) / gdn::kFusedWaves;   // chain workgroups per head
+  const int nh = (int)((bh + nx - 1) / nx);                  // heads on the fullest XCD
+  if (nh * cw > per_x / 2) return f;
+  const int ns = per_x - nh * cw;                            // its stream workgroups
+  const int fly = (ns + 2 * nh - 1) / (2 * nh);              // frame blocks they keep in flight
+  f.nx = nx;
+  f.grid = 2 * li.cus;
+  f.RM = std::min(gdn::kFusedMaxRM, 8);
+  f.RG = std::min(gdn::kFusedMaxRG, std::max(10, fly + 6 - f.RM + 2));
+  f.L = std::min(fly + 6, f.RG + f.RM - 1);                 // progress needs L < RG + RM
+  f.ctl = round_up(gdn::fused_ctl_bytes((int)bh));
+  f.gring = round_up((size_t)bh * f.RG * gdn::fused_slot_bytes(d->D));
+  f.mring = round_up((size_t)bh * f.RM * (size_t)d->D * d->D * 2);
+  f.total = f.ctl + f.gring + f.mring;
+  f.ok = true;
+  return f;
+}
+
+gdn_status run_fused(const gdn_desc* d, const FusedPlan& f, const Ptrs& x, void* workspace, hipStream_t s) {
+  unsigned char* ws = (unsigned char*)workspace;
+  gdn::FusedArgs fa;
+  fa.q = x.q; fa.k = x.k; fa.v = x.v; fa.o = x.o;
+  fa.gamma = x.gamma; fa.beta = x.beta; fa.state_in = x.state_in; fa.state_out = x.state_out; fa.norms = x.norms;
+  fa.ctl = ws;
+  fa.gring = ws + f.ctl;
+  fa.mring = ws + f.ctl + f.gring;
+  fa.BH = d->B * d->H; fa.T = d->T; fa.S = d->S;
+  fa.NX = f.nx; fa.RG = f.RG; fa.RM = f.RM; fa.L = f.L; fa.grid = f.grid;
+  const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
+  fa.kscale = (float)c; fa.kscale2 = (float)(c * c);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const hipError_t e = launch_timed(timed, GDN_KERNEL_FUSED, s, [&] {
+    return gdn::launch_fused(d->D, fa, d->io_dtype == GDN_FP8_E4M3, d->beta_mode == GDN_BETA_ERASE, s);
+  });
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "one-launch forward: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
 gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
                const float* beta, const float* state_in, void* o, float* state_out, float* norms,
                void* workspace, size_t workspace_bytes, void* stream, int is_step) {
@@ -388,8 +456,12 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
   const Plan p = make_plan(d);
   const Ptrs x{q, k, v, gamma, beta, state_in, o, state_out, norms};
   hipStream_t s = (hipStream_t)stream;
-  return p.gram ? run_gram(d, p, x, workspace, workspace_bytes, s)
-                : run_direct(d, p, x, workspace, workspace_bytes, s);
+  if (p.gram) {
+    const FusedPlan f = make_fused_plan(d);
+    if (f.ok && workspace_bytes >= f.total) return run_fused(d, f, x, workspace, s);
+    return run_gram(d, p, x, workspace, workspace_bytes, s);
+  }
+  return run_direct(d, p, x, workspace, workspace_bytes, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -790,8 +862,11 @@ size_t gdn_workspace_min_size(const gdn_desc* d) {
 
 size_t gdn_workspace_size(const gdn_desc* d) {
   if (check_desc(d) != GDN_OK) return 0;
+  const Plan p = make_plan(d);
+  const FusedPlan f = p.gram ? make_fused_plan(d) : FusedPlan();
+  if (f.ok) return std::max(f.total, ws_bytes_for(p, 1));
   const size_t frames = std::min<size_t>((size_t)d->T, (size_t)kMaxFramesPerLaunch);
-  return ws_bytes_for(make_plan(d), frames);
+  return ws_bytes_for(p, frames);
 }
 
 gdn_status gdn_check_args(const gdn_desc* d, const void* q, const void* k, const void* v,

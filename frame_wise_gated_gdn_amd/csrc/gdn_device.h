@@ -29,6 +29,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+// f(Int<0>{}), ..., f(Int<N-1>{}): compile-time loop (every index a constant)
+template <int N, int K = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(Int<K>{});
+    static_for<N, K + 1>(f);
+  }
+}
+
 // ReLU on two packed bf16: a negative bf16 has its sign bit set, i.e. it is a
 // negative int16, so an int16 max with 0 zeroes it and keeps the rest.
 __device__ __forceinline__ uint32_t relu2(uint32_t x) {
@@ -63,6 +76,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One state update of the Gram form, gm*m - bg*p + w, as two fused
+// multiply-adds in a fixed order, so that every kernel running it (the state
+// pass and the one-launch forward) rounds the same way.
+__device__ __forceinline__ float state_update(float gm, float m, float bg, float p, float w) {
+  return __builtin_fmaf(gm, m, __builtin_fmaf(-bg, p, w));
+}
+// Adds the squares of the two bf16 of a packed word to sq, in a fixed order.
+__device__ __forceinline__ float add_sq_bf16x2(float sq, uint32_t w) {
+  const float x = __builtin_bit_cast(float, w << 16), y = __builtin_bit_cast(float, w & 0xffff0000u);
+  return __builtin_fmaf(y, y, __builtin_fmaf(x, x, sq));
 }
 
 // Pack two floats into two bf16 (round to nearest even).

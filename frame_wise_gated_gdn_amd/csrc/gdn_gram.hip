@@ -49,19 +49,6 @@
 
 namespace gdn {
 
-template <int V>
-struct Int {
-  static constexpr int value = V;
-};
-// f(Int<0>{}), ..., f(Int<N-1>{})
-template <int N, int K = 0, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (K < N) {
-    f(Int<K>{});
-    static_for<N, K + 1>(f);
-  }
-}
-
 // ----------------------------------------------------------------------------
 // Gram pass.  One workgroup per (head, frame).  Its output is the NB*NB blocks
 // of B = Kf^T V and the NB(NB+1)/2 stored blocks (I >= L) of G = Kf^T Kf, in
@@ -591,7 +578,7 @@ __device__ __forceinline__ void state_wave(const StateArgs& a, unsigned char* sm
       const bool ok = f < Tc;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float nv = gm * m[e] - bg * p[e] + (ERASE ? bin[e] : bt * bin[e]);
+        const float nv = state_update(gm, m[e], bg, p[e], ERASE ? bin[e] : bt * bin[e]);
         m[e] = ok ? nv : m[e];
       }
       // G of the next frame into the other LDS slot (read by everyone after the barrier)

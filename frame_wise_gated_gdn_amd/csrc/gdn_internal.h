@@ -175,6 +175,44 @@ struct AdjointArgs {
   int t_lo, t_hi;           // this launch's frames, run from t_hi-1 down to t_lo
 };
 
+// One-launch forward (gdn_fused.hip): gram, state and readout roles of the
+// Gram pipeline in one persistent cooperative launch, handing G_t, B_t and
+// the bf16 states over through rings that stay in one XCD's L2.
+constexpr int kFusedWaves = 4;            // waves per workgroup; two workgroups per CU
+constexpr int kFusedMaxRG = 48;           // gram ring slots per head (at most)
+constexpr int kFusedMaxRM = 16;           // state ring slots per head (at most)
+constexpr int kFusedMaxCW = 2;            // chain workgroups per head (one per 4 value tiles)
+constexpr size_t kFusedCtlTicket = 64;    // control block: abort word at 0, per-XCD tickets from here
+constexpr size_t kFusedCtlHead = 2048;    // (64 bytes apart, up to 16 XCDs), then per-head flags
+constexpr size_t kFusedCtlPerHead = 8192;
+inline size_t fused_ctl_bytes(int BH) { return kFusedCtlHead + (size_t)BH * kFusedCtlPerHead; }
+// per head: the chain workgroups' progress words, then gready per gram slot,
+// then rdone per state slot, 64 bytes apart
+static_assert((kFusedMaxCW + kFusedMaxRG + kFusedMaxRM) * 64 <= (int)kFusedCtlPerHead, "per-head flags");
+size_t fused_slot_bytes(int D);           // one gram ring slot: G_t (stored blocks) and B_t
+
+struct FusedArgs {
+  const void* q;            // [BH][T][S][D] bf16, or OCP e4m3
+  const void* k;
+  const void* v;
+  void* o;
+  const float* gamma;       // [BH][T]
+  const float* beta;        // [BH][T]
+  const float* state_in;    // [BH][D][D] or nullptr (zero state)
+  float* state_out;         // [BH][D][D] or nullptr
+  float* norms;             // [BH][T] or nullptr
+  unsigned char* ctl;       // fused_ctl_bytes(BH), cleared by the launcher
+  unsigned char* gring;     // [BH][RG] x fused_slot_bytes(D)
+  unsigned char* mring;     // [BH][RM] x D*D*2 (bf16 state, snapshot block layout)
+  int BH, T, S;
+  int NX;                   // XCDs; head h lives on XCD h % NX
+  int RG, RM, L;            // ring slots per head; readout lag in frames (L < RG + RM)
+  int grid;                 // workgroups (two per CU, a multiple of NX)
+  float kscale, kscale2;    // 1/sqrt(D*S) and 1/(D*S), each rounded once to fp32
+};
+// Clears the control block and launches; fp8: e4m3 I/O; erase: beta mode.
+hipError_t launch_fused(int D, const FusedArgs& fa, int fp8, int erase, hipStream_t stream);
+
 // Kernel launchers (enqueue only).  D in {16, ..., 128}.
 hipError_t launch_recurrence(int D, bool bf16, const RecurArgs& ra, hipStream_t stream);
 hipError_t launch_readout(int D, bool bf16, const ReadoutArgs& ro, hipStream_t stream);

@@ -644,10 +644,7 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = bf16_lo_f32(A[jb][kc][e]), y = bf16_hi_f32(A[jb][kc][e]);
-          sq += x * x + y * y;
-        }
+        for (int e = 0; e < 4; ++e) sq = add_sq_bf16x2(sq, A[jb][kc][e]);
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) sq += __shfl_xor(sq, s, 64);
     if (l == 0) a.norms[(size_t)bh * T + t] = sqrtf(sq);

@@ -111,6 +111,16 @@ typedef enum gdn_status {
  * always runs the single-pass recurrence.
  */
 #define GDN_FLAG_DIRECT 0x2u
+/*
+ * bf16/e4m3 I/O: run the Gram pipeline as its three launches (gram pass,
+ * state pass, readout; G_t, B_t and the bf16 states go through the
+ * workspace in HBM) instead of the default one-launch form, in which every
+ * head lives on one XCD and those per-frame terms stay in that XCD's L2.  The
+ * two forms compute the same operations in the same order: the results are
+ * bitwise equal.  The one-launch form also falls back to this one when the
+ * device or the workspace does not allow it.
+ */
+#define GDN_FLAG_THREE_PASS 0x4u
 
 /* Kernel kinds booked by gdn_kernel_times. */
 #define GDN_KERNEL_RECURRENCE 0 /* single-pass recurrence */
@@ -120,7 +130,8 @@ typedef enum gdn_status {
 #define GDN_KERNEL_BACKWARD 4   /* the backward's own kernels (its forward replay books as GRAM/STATE) */
 #define GDN_KERNEL_TCONV 5      /* block-causal temporal convolution */
 #define GDN_KERNEL_ATTN 6       /* block-causal softmax attention */
-#define GDN_KERNEL_SLOTS 7
+#define GDN_KERNEL_FUSED 7      /* one-launch forward (gram, state and readout roles in one kernel) */
+#define GDN_KERNEL_SLOTS 8
 
 typedef struct gdn_desc {
   int32_t abi_version; /* GDN_ABI_VERSION */
