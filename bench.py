@@ -54,7 +54,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFS = 2500.0    # dense bf16 MFMA, TFLOP/s
 KERNEL_SRCS = [os.path.join(ROOT, "frame_wise_gated_gdn_amd", "csrc", f)
-               for f in ("gdn_device.h", "gdn_kernels.hip", "gdn_gram.hip")]
+               for f in ("gdn_device.h", "gdn_kernels.hip", "gdn_gram.hip", "gdn_fused.hip")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_minute720p.json")
 
 
@@ -79,31 +79,112 @@ def pmc_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, heads: int):
-    """Oracle (as it stands) on `heads` whole heads of the same workload."""
-    import numpy as np
+    """Oracle (as it stands, compiled -O3 -march=native on this host) on `heads`
+    whole heads of the same workload, OpenMP over all host threads."""
+    import tempfile
     from oracle import gdn_oracle
     from frame_wise_gated_gdn_amd import workloads as wl
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    gdn_oracle.load()
+    # built here, for this host's CPU (a library built elsewhere may use
+    # instructions this CPU lacks); same arithmetic as the -O2 build
+    lib = gdn_oracle.build(os.path.join(tempfile.gettempdir(), f"liboracle_gdn_native_{os.getpid()}.so"),
+                           native=True)
     tok = 0
     t0 = time.perf_counter()
     for h in range(heads):
         q, k, v = (wl.to_numpy_io(inp[n][0, h]) for n in ("q", "k", "v"))
         g = inp["gamma"][0, h].cpu().numpy()
         b = inp["beta"][0, h].cpu().numpy()
-        gdn_oracle.head(q, k, v, g, b, beta_mode=w.beta_mode, want_out=True, threads=threads)
+        gdn_oracle.head(q, k, v, g, b, beta_mode=w.beta_mode, want_out=True, threads=threads, lib_path=lib)
         tok += w.T * w.S
     dt = time.perf_counter() - t0
     return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "build": "gcc -O3 -march=native -fopenmp -fno-fast-math -ffp-contract=off",
             "sample": f"{heads} whole head(s) (b=0, h=0..{heads - 1}) of {w.name}: {tok} tokens, "
                       f"{dt:.1f} s wall, fp64, OpenMP {threads} threads"}
+
+
+def one_shot_ms(gdn, torch, dev, w, reps: int, flush_bytes: int = 512 << 20):
+    """Median and minimum device time of one whole-sequence gdn_frame_forward on
+    workload `w` (HIP events on the call's stream), with a 512 MB buffer
+    overwritten between the calls so that the 256 MB Infinity Cache holds none
+    of the inputs."""
+    from frame_wise_gated_gdn_amd import workloads as wl
+    inp = wl.generate(w, device=dev)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode)
+    ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["q"])
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    call = lambda: gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
+                                     beta_mode=w.beta_mode, out=out, state_out=st, workspace=ws)
+    for _ in range(3):
+        call()
+    ts = []
+    for _ in range(reps):
+        flush.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    alg = w.B * w.H * w.T * (w.S * 4 * w.D * {"bf16": 2, "f32": 4, "fp8": 1}[w.dtype] + 8)
+    med = ts[len(ts) // 2]
+    return {"workload": w.name, "io_dtype": w.dtype, "ms_median": med, "ms_min": ts[0], "reps": reps,
+            "tokens_per_s": w.tokens / (med * 1e-3), "algorithmic_bytes": alg,
+            "hbm_frac": alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def stress_variant(gdn, wl, torch, dev, steps: int):
+    """The stability/throughput stress shape (B2 H20 T961 S3600 D128, beta = 1,
+    K ~ N(0, 4)): tokens/s and the path roofline (8*D bytes per token-head)."""
+    w = wl.STRESS
+    inp = wl.generate(w, device=dev)
+    desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode)
+    ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp["q"])
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    nm = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    call = lambda: gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
+                                     beta_mode=w.beta_mode, out=out, state_out=st, norms=nm, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    path_bytes = w.tokens * 8 * w.D
+    gbs = path_bytes / (ms * 1e-3) / 1e9
+    finite = bool(torch.isfinite(nm).all()) and bool(torch.isfinite(st).all())
+    res = {"workload": w.name, "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+           "steps": steps, "norms_and_state_finite": finite, "max_state_norm": float(nm.max()),
+           "path_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes}}
+    del inp, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def streaming_latency(gdn, wl, torch, dev, reps: int):
     """Chunk-causal rollout of the short-clip shape, 4 frames per gdn_frame_step call
     with the state committed in place: per-chunk latency (enqueue to completion,
-    one chunk at a time) and the per-chunk time of back-to-back chunks."""
+    one chunk at a time), the per-chunk time of back-to-back chunks and the
+    whole rollout."""
     w = wl.CHUNKED
     inp = wl.generate(w, device=dev)
     T, c = w.T, w.chunk
@@ -134,9 +215,11 @@ def streaming_latency(gdn, wl, torch, dev, reps: int):
         rollout(False)
     torch.cuda.synchronize()
     per_chunk = (time.perf_counter() - t0) / (reps * len(chunks))
+    pct = lambda p: lat[min(len(lat) - 1, int(round(p * (len(lat) - 1))))] * 1e6
     return {"workload": w.name, "frames_per_chunk": c, "chunks_per_rollout": len(chunks), "rollouts": reps,
-            "latency_us_median": lat[len(lat) // 2] * 1e6, "latency_us_p90": lat[int(len(lat) * 0.9)] * 1e6,
+            "latency_us_p50": pct(0.5), "latency_us_p99": pct(0.99), "latency_samples": len(lat),
             "back_to_back_us_per_chunk": per_chunk * 1e6,
+            "whole_rollout_ms": per_chunk * len(chunks) * 1e3,
             "back_to_back_tokens_per_s": w.B * w.H * w.T * w.S / (per_chunk * len(chunks))}
 
 
@@ -360,8 +443,13 @@ def main():
                     help="skip the E4M3 I/O variant of the step")
     ap.add_argument("--stream-reps", type=int, default=5,
                     help="rollouts of the chunk-causal streaming latency check (0 = skip)")
-    ap.add_argument("--path", choices=("auto", "direct"), default="auto",
-                    help="bf16 path: Gram pipeline (auto) or single-pass recurrence (direct)")
+    ap.add_argument("--path", choices=("auto", "three_pass", "direct"), default="auto",
+                    help="bf16 path: one-launch forward (auto), the Gram pipeline as three launches, "
+                         "or the single-pass recurrence")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the one-shot timings of the tiny and short-clip workloads")
+    ap.add_argument("--stress-steps", type=int, default=3,
+                    help="steps of the stress workload (B2 H20 T961 S3600 D128; 0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (for rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -380,7 +468,8 @@ def main():
     torch.cuda.set_device(dev)
     inp = wl.generate(w, device=dev)
     desc = gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode,
-                         gdn.binding.FLAG_DIRECT if args.path == "direct" else 0)
+                         {"auto": 0, "direct": gdn.binding.FLAG_DIRECT,
+                          "three_pass": gdn.binding.FLAG_THREE_PASS}[args.path])
     ws = torch.empty(gdn.workspace_size(desc), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp["q"])
     st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
@@ -420,7 +509,8 @@ def main():
     kms = {name: ms / args.steps for name, (ms, n) in ktimes.items() if n > 0}
     klaunch = {name: n // args.steps for name, (ms, n) in ktimes.items() if n > 0}
     alg_bytes = {"gram": BH * T * S * 4 * D, "recurrence": BH * T * S * 4 * D + BH * T * 8,
-                 "state": BH * T * 8, "readout": BH * T * S * 4 * D}
+                 "state": BH * T * 8, "readout": BH * T * S * 4 * D,
+                 "fused": BH * T * S * 8 * D + BH * T * 8 + BH * D * D * 4}
     dom = max(kms, key=kms.get)
     launches_per_step = max(klaunch[dom], 1)
     dom_bytes, dom_ms = alg_bytes[dom], kms[dom]
@@ -443,7 +533,8 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V, uniform gamma/beta; no dataset)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "S": w.S, "D": w.D,
                    "io_dtype": w.dtype, "state_dtype": "f32", "beta_mode": w.beta_mode,
-                   "path": "gram" if args.path == "auto" else "direct",
+                   "path": {"auto": "one-launch", "three_pass": "gram three-launch",
+                            "direct": "direct"}[args.path],
                    "calls_per_step": 1, "launches_per_kernel_per_step": launches_per_step},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -456,8 +547,30 @@ def main():
         "kernels_ms_per_step": kms,
         "ms_per_step_with_kernel_events": dt_ev * 1e3 / args.steps,
     }
+    if args.path == "auto":
+        # the same step as three launches (same bits), for context
+        ws3 = torch.empty(gdn.workspace_size(gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode,
+                                                           gdn.binding.FLAG_THREE_PASS)),
+                          dtype=torch.uint8, device=dev)
+        call3 = lambda: gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
+                                          beta_mode=w.beta_mode, out=out, state_out=st, workspace=ws3,
+                                          path="three_pass")
+        call3()
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        for _ in range(args.steps):
+            call3()
+        torch.cuda.synchronize()
+        rec["three_launch_ms_per_step"] = (time.perf_counter() - t3) * 1e3 / args.steps
+        del ws3
+    if args.configs:
+        rec["configs"] = {"tiny": one_shot_ms(gdn, torch, dev, wl.TINY, 50),
+                          "short_clip": one_shot_ms(gdn, torch, dev, wl.SHORT, 50)}
+        rec["configs"]["short_clip"]["bar_us_60pct_roofline"] = 122.0
     if args.stream_reps > 0:
         rec["streaming"] = streaming_latency(gdn, wl, torch, dev, args.stream_reps)
+        if args.configs:
+            rec["streaming"]["one_shot_ms_same_shape"] = rec["configs"]["short_clip"]["ms_median"]
     if args.backward and args.path == "auto":
         rec["backward"] = backward_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
         rec["training_step"] = training_variant(gdn, wl, torch, dev, inp, max(1, args.steps // 4), 1)
@@ -467,6 +580,8 @@ def main():
         rec["attention"] = attention_variant(gdn, wl, torch, dev, max(1, args.steps // 4), 1)
     if args.fp8 and args.path == "auto":
         rec["variants"] = {"fp8_e4m3_io": fp8_variant(gdn, wl, torch, dev, args.steps, args.warmup)}
+    if args.stress_steps > 0:
+        rec["stress"] = stress_variant(gdn, wl, torch, dev, args.stress_steps)
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
     print(json.dumps(rec), flush=True)

@@ -57,6 +57,28 @@ def attention_head(q, k, v, S: int, chunk: int, scale=None) -> np.ndarray:
     return p @ v
 
 
+def attention_rows(q, k, v, S: int, chunk: int, rows, Tq: int, scale=None) -> np.ndarray:
+    """The rows `rows` of attention_head's output, computed one query at a
+    time (for long sequences whose whole logit matrix would not fit).  q holds
+    all Tq*S query rows [Tq*S, D]; k, v: [Tk*S, D].  Returns [len(rows), D]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Nk, D = k.shape
+    if Nk % S or q.shape[0] != Tq * S or Tq * S > Nk or chunk < 1:
+        raise ValueError("need whole frames, Tq <= Tk and chunk >= 1")
+    Tk = Nk // S
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((len(rows), D))
+    for n, i in enumerate(rows):
+        end = int(key_end((Tk - Tq) + i // S, Tk, S, chunk))
+        logits = (k[:end] @ q[i]) * scale
+        p = np.exp(logits - logits.max())
+        out[n] = (p / p.sum()) @ v[:end]
+    return out
+
+
 def attention(q, k, v, chunk: int, scale=None) -> np.ndarray:
     """q: [B, H, Tq, S, D]; k, v: [B, H, Tk, S, D].  Returns O like q."""
     q = np.asarray(q, np.float64)

@@ -25,7 +25,7 @@ x <= 0.  Everything is float64; inputs are the exact values the GPU sees.
 """
 from __future__ import annotations
 
-from typing import Dict, Optional
+from typing import Dict
 
 import numpy as np
 
@@ -98,13 +98,3 @@ def backward_head(q, k, v, gamma, beta, d_out, d_state_out=None, state_in=None,
         dq[t] = dqf * (q[t] > 0)
         dk[t] = c * d_kf * (k[t] > 0)
     return {"dq": dq, "dk": dk, "dv": dv, "dgamma": dgamma, "dbeta": dbeta, "dstate_in": lam}
-
-
-def loss(out: np.ndarray, state_out: np.ndarray, d_out: np.ndarray,
-         d_state_out: Optional[np.ndarray] = None) -> float:
-    """The linear functional whose gradient backward_head returns:
-    L = sum_t <d_out_t, O_t> + <d_state_out, M_final>."""
-    val = float(np.sum(np.asarray(d_out, np.float64) * out))
-    if d_state_out is not None:
-        val += float(np.sum(np.asarray(d_state_out, np.float64) * state_out))
-    return val

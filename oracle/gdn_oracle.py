@@ -29,9 +29,13 @@ ERASE, WRITE = 0, 1
 _MODES = {"erase": ERASE, "write": WRITE, ERASE: ERASE, WRITE: WRITE}
 
 
-def build(out: str = LIB, mutant: int = 0, quiet: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math). Returns the path."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+def build(out: str = LIB, mutant: int = 0, quiet: bool = True, native: bool = False) -> str:
+    """Compile the oracle with gcc (OpenMP, no fast-math, no floating-point
+    contraction).  native=True builds it -O3 -march=native for timing on the
+    host it runs on; the arithmetic is the same (every sum keeps its order:
+    without -ffast-math gcc neither reassociates nor contracts)."""
+    opt = ["-O3", "-march=native"] if native else ["-O2"]
+    cmd = ["gcc", *opt, "-fopenmp", "-fPIC", "-shared", "-std=c11",
            "-fno-fast-math", "-ffp-contract=off",
            f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True, capture_output=quiet)
@@ -125,11 +129,6 @@ def forward(q, k, v, gamma, beta, state_in=None, beta_mode="erase", want_out=Tru
             if want_norms:
                 norms[bi, hi] = n
     return out, sout, norms
-
-
-def bf16_bits_to_f64(x: np.ndarray) -> np.ndarray:
-    """Exact widening of bf16 bit patterns (uint16) to float64."""
-    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def e4m3_to_f64(codes: np.ndarray, lib_path: str = LIB) -> np.ndarray:

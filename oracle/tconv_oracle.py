@@ -67,17 +67,6 @@ def tconv_forward(x, w, bias=None, chunk: int = 1, cache_in=None) -> Tuple[np.nd
     return y, x[T - 1].copy()
 
 
-def tconv_forward_batched(x, w, bias=None, chunk: int = 1, cache_in=None):
-    """x: [B, T, S, C]; cache_in: [B, S, C] or None.  Per batch element."""
-    x = np.asarray(x, np.float64)
-    ys, cs = [], []
-    for b in range(x.shape[0]):
-        y, c = tconv_forward(x[b], w, bias, chunk, None if cache_in is None else cache_in[b])
-        ys.append(y)
-        cs.append(c)
-    return np.stack(ys), np.stack(cs)
-
-
 def tconv_terms_abs(x, w, bias=None, chunk: int = 1, cache_in=None) -> np.ndarray:
     """Sum of the magnitudes of the terms of every output element:
     |w0 left| + |w1 x| + |w2 right| + |bias| (bounds the rounding error of

@@ -49,6 +49,25 @@ def test_matches_torch_sdpa_with_explicit_mask(Tq, Tk, S, D, chunk):
     np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("Tq,Tk,S,D,chunk", [(6, 6, 3, 8, 2), (3, 7, 4, 8, 2), (1, 9, 6, 4, 4), (4, 4, 5, 8, 9)])
+def test_row_subset_matches_torch_sdpa(Tq, Tk, S, D, chunk):
+    """attention_rows (one query at a time, for the long 720p-shaped checks)
+    against torch's scaled_dot_product_attention with a token-by-token mask,
+    on rows at frame and block edges; and against the whole-matrix form."""
+    import torch
+    rng = np.random.default_rng(7 * Tq + Tk + 31 * chunk)
+    q, k, v = rand(rng, Tq, S, D, Tk)
+    rows = sorted(r for r in {0, 1, S - 1, S, Tq * S - 1, (Tq * S) // 2} if r < Tq * S)
+    got = ao.attention_rows(q, k, v, S, chunk, rows, Tq)
+    mask = torch.from_numpy(mask_from_indices(Tq, Tk, S, chunk))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None], attn_mask=mask[None])[0]
+    np.testing.assert_allclose(got, ref.numpy()[rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got, ao.attention_head(q, k, v, S, chunk)[rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ao.attention_rows(q, k, v, S, chunk, rows, Tq, scale=0.3),
+                               ao.attention_head(q, k, v, S, chunk, scale=0.3)[rows], rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("chunk", [1, 2, 3, 100])
 def test_uniform_attention_is_cumulative_block_mean(chunk):
     rng = np.random.default_rng(chunk)
