@@ -27,6 +27,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE"
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_workspace_size",
            "gdn_workspace_min_size", "gdn_check_args", "gdn_frame_forward", "gdn_frame_step",
+           "gdn_frame_forward_noalloc",
            "gdn_kernel_times", "gdn_backward_workspace_size", "gdn_frame_backward", "gdn_saved_size",
            "gdn_backward_saved_workspace_size", "gdn_frame_forward_train", "gdn_frame_backward_saved",
            "gdn_tconv_forward",
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.gdn_frame_forward_noalloc.restype = ctypes.c_int
+    L.gdn_frame_forward_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_backward_workspace_size.restype = sz
     L.gdn_backward_workspace_size.argtypes = [pdesc]
     L.gdn_frame_backward.restype = ctypes.c_int
@@ -296,6 +299,29 @@ def frame_step(q, k, v, gamma, beta, state, beta_mode="erase", out=None, state_o
             state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     out = _call("gdn_frame_step", q, k, v, gamma, beta, state, beta_mode, out, state_out, norms,
                 workspace, stream, _flags(path, time_kernels))
+    return out, state_out, norms
+
+
+def frame_forward_noalloc(q, k, v, gamma, beta, state=None, beta_mode="erase", out=None, state_out=None,
+                          norms=None, stream=None):
+    """frame_forward on the library's static scratch (gdn_frame_forward_noalloc):
+    no workspace; the caller passes every output tensor it wants (out is
+    required).  Returns (out, state_out, norms)."""
+    import torch
+    _check_gdn_inputs("frame_forward_noalloc", q, k, v, gamma, beta, state, (("o", out),))
+    if out is None:
+        raise ValueError("frame_forward_noalloc needs `out` (it allocates nothing)")
+    B, H, T, S, D = q.shape
+    io = {torch.bfloat16: BF16, torch.float32: F32, torch.float8_e4m3fn: FP8}.get(q.dtype)
+    if io is None:
+        raise TypeError("q, k, v must be bfloat16, float32 or float8_e4m3fn")
+    _check(q.device, "state_out", state_out, (B, H, D, D), torch.float32)
+    _check(q.device, "norms", norms, (B, H, T), torch.float32)
+    desc = make_desc(B, H, T, S, D, io, beta_mode)
+    handle = _stream_and_alloc(stream, q.device)[0]
+    _raise(lib().gdn_frame_forward_noalloc(ctypes.byref(desc), _addr(q), _addr(k), _addr(v), _addr(gamma),
+                                           _addr(beta), _addr(state), _addr(out), _addr(state_out), _addr(norms),
+                                           ctypes.c_void_p(handle)))
     return out, state_out, norms
 
 

@@ -259,7 +259,7 @@ hipError_t side_stream(SideStream** out) {
 // i+1 runs on the CUs next to the HBM-bound readout of sub-range i.  The state
 // crosses sub-ranges and ranges in fp32, so any split gives the same bits.
 gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* workspace, size_t wb,
-                    hipStream_t s) {
+                    hipStream_t s, bool side_ok = true) {
   const size_t F = frames_per_launch(p, d->T, wb);
   unsigned char* ws = (unsigned char*)workspace;
   size_t off = 0;
@@ -283,7 +283,7 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
     failed_t0 = t0;
     const int tc = (int)std::min<size_t>(F, (size_t)(d->T - t0));
     int bnd[kStateSplit + 1];
-    const int nsub = split_frames(tc, bnd);
+    const int nsub = side_ok ? split_frames(tc, bnd) : (bnd[0] = 0, bnd[1] = tc, 1);
     gdn::GramArgs ga;
     ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
     ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = t0; ga.Tc = tc;
@@ -449,7 +449,7 @@ gdn_status run_fused(const gdn_desc* d, const FusedPlan& f, const Ptrs& x, void*
 
 gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
                const float* beta, const float* state_in, void* o, float* state_out, float* norms,
-               void* workspace, size_t workspace_bytes, void* stream, int is_step) {
+               void* workspace, size_t workspace_bytes, void* stream, int is_step, bool side_ok = true) {
   gdn_status st = gdn_check_args(d, q, k, v, gamma, beta, state_in, o, state_out, norms, workspace,
                                  workspace_bytes, is_step);
   if (st != GDN_OK) return st;
@@ -459,7 +459,7 @@ gdn_status run(const gdn_desc* d, const void* q, const void* k, const void* v, c
   if (p.gram) {
     const FusedPlan f = make_fused_plan(d);
     if (f.ok && workspace_bytes >= f.total) return run_fused(d, f, x, workspace, s);
-    return run_gram(d, p, x, workspace, workspace_bytes, s);
+    return run_gram(d, p, x, workspace, workspace_bytes, s, side_ok);
   }
   return run_direct(d, p, x, workspace, workspace_bytes, s);
 }
@@ -924,6 +924,29 @@ gdn_status gdn_frame_step(const gdn_desc* d, const void* q, const void* k, const
                           void* workspace, size_t workspace_bytes, void* stream) {
   return run(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, workspace, workspace_bytes,
              stream, 1);
+}
+
+gdn_status gdn_frame_forward_noalloc(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                     const float* gamma, const float* beta, const float* state_in, void* o,
+                                     float* state_out, float* state_norms, void* stream) {
+  g_last_error.clear();
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  if (d->flags & GDN_FLAG_TIME_KERNELS)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_frame_forward_noalloc records no kernel times (their events are created "
+                                     "on demand)");
+  const Plan p = make_plan(d);
+  const FusedPlan f = p.gram ? make_fused_plan(d) : FusedPlan();
+  const size_t need = f.ok ? f.total : ws_bytes_for(p, 1);
+  if (need > gdn::kNoAllocScratchBytes)
+    return fail(GDN_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", need,
+                gdn::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = gdn::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  // the three-launch form, when it runs here, stays on `stream` (no side stream to create)
+  return run(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, scratch, gdn::kNoAllocScratchBytes,
+             stream, 0, false);
 }
 
 gdn_status gdn_kernel_times(double ms_out[GDN_KERNEL_SLOTS], int64_t launches_out[GDN_KERNEL_SLOTS],

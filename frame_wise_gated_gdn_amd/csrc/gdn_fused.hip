@@ -52,6 +52,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -741,7 +744,33 @@ hipError_t launch_fused_t(const FusedArgs& fa, int fp8, int erase, hipStream_t s
   return erase ? launch_fused_t3<D, false, true>(fa, fa.grid, stream) : launch_fused_t3<D, false, false>(fa, fa.grid, stream);
 }
 
+// Static scratch of the allocation-free forward (gdn_frame_forward_noalloc):
+// every GPU the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel: its address on a
+// device comes from hipGetSymbolAddress, taken once per device below.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> address of that device's copy of `scratch`
+
 }  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));   // with the device current: this device's copy
+    if (e != hipSuccess) return e;
+    if (!ptr || ((uintptr_t)ptr % 256) != 0) return hipErrorInvalidSymbol;
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
 
 size_t fused_slot_bytes(int D) {
   const size_t nb = (size_t)D / 16;

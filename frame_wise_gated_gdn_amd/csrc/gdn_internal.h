@@ -210,6 +210,12 @@ struct FusedArgs {
   int grid;                 // workgroups (two per CU, a multiple of NX)
   float kscale, kscale2;    // 1/sqrt(D*S) and 1/(D*S), each rounded once to fp32
 };
+// Static device scratch of the allocation-free forward: its size, and its
+// address on the current device (taken once per device with
+// hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** out);
+
 // Clears the control block and launches; fp8: e4m3 I/O; erase: beta mode.
 hipError_t launch_fused(int D, const FusedArgs& fa, int fp8, int erase, hipStream_t stream);
 

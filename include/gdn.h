@@ -187,6 +187,24 @@ gdn_status gdn_frame_forward(const gdn_desc* d, const void* q, const void* k, co
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_frame_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid device allocation.  It
+ * takes no workspace: it runs on a static device array of the library
+ * (64 MiB, one copy on every GPU the library runs on, held until the process
+ * ends), and calls nothing that allocates.  Same arguments, results (bitwise)
+ * and stream behaviour as gdn_frame_forward, except: shapes whose workspace
+ * would exceed the 64 MiB return GDN_ERR_WORKSPACE; GDN_FLAG_TIME_KERNELS
+ * returns GDN_ERR_UNSUPPORTED; and the three-launch form, when it runs here,
+ * stays on `stream` (no side stream).  All calls on one GPU share that GPU's
+ * array, which keeps the last call's contents: calls that overlap on one GPU
+ * (two streams, or two host threads) race and give undefined results; calls
+ * in one stream's order do not.
+ */
+gdn_status gdn_frame_forward_noalloc(const gdn_desc* d, const void* q, const void* k, const void* v,
+                                     const float* gamma, const float* beta, const float* state_in, void* o,
+                                     float* state_out, float* state_norms, void* stream);
+
+/*
  * One chunk of a chunk-causal streaming rollout (the article's chunk-causal
  * autoregressive variant; the cached-state hand-off of SANA-Video's block
  * KV cache): T = frames in this chunk (>= 1).  state_in is REQUIRED; state_out
