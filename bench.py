@@ -253,7 +253,8 @@ def fp8_variant(gdn, wl, torch, dev, steps: int, warmup: int):
     return {"io_dtype": "fp8_e4m3 (OCP)", "workload": w.name, "value": w.tokens / (ms * 1e-3),
             "unit": "tokens/s", "ms_per_step": ms, "kernels_ms_per_step": kms,
             "path_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes}}
+                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_step": path_bytes,
+                              "traffic": pmc_traffic("fused_fp8")}}
 
 
 def backward_variant(gdn, wl, torch, dev, inp, steps: int, warmup: int):
