@@ -19,6 +19,7 @@ ERASE, WRITE = 0, 1
 FLAG_TIME_KERNELS = 0x1
 FLAG_DIRECT = 0x2
 FLAG_THREE_PASS = 0x4
+FLAG_ONE_LAUNCH = 0x8
 # kernel kinds of gdn_kernel_times, in slot order
 KERNELS = ("recurrence", "readout", "gram", "state", "backward", "tconv", "attention", "fused")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE", 4: "GDN_ERR_ALIGN",
@@ -217,13 +218,13 @@ def _stream_and_alloc(stream, device):
 
 
 def _flags(path: str, time_kernels: bool) -> int:
-    """path: "auto" (the one-launch forward where the device allows it),
-    "three_pass" (the Gram pipeline as three launches) or "direct" (the
-    single-pass recurrence)."""
-    if path not in ("auto", "direct", "three_pass"):
-        raise ValueError('path must be "auto", "three_pass" or "direct"')
-    return ((FLAG_TIME_KERNELS if time_kernels else 0) | (FLAG_DIRECT if path == "direct" else 0) |
-            (FLAG_THREE_PASS if path == "three_pass" else 0))
+    """path: "auto" (the library's choice by size and dtype), "one_launch" or
+    "three_pass" (the two forms of the Gram pipeline, same bits) or "direct"
+    (the single-pass recurrence)."""
+    flags = {"auto": 0, "direct": FLAG_DIRECT, "three_pass": FLAG_THREE_PASS, "one_launch": FLAG_ONE_LAUNCH}
+    if path not in flags:
+        raise ValueError('path must be "auto", "one_launch", "three_pass" or "direct"')
+    return (FLAG_TIME_KERNELS if time_kernels else 0) | flags[path]
 
 
 def _call(entry: str, q, k, v, gamma, beta, state_in, beta_mode, out, state_out, norms, workspace,

@@ -79,8 +79,10 @@ gdn_status check_desc(const gdn_desc* d) {
     return fail(GDN_ERR_DTYPE, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_FP8_E4M3", d->io_dtype);
   if (d->beta_mode != GDN_BETA_ERASE && d->beta_mode != GDN_BETA_WRITE)
     return fail(GDN_ERR_DTYPE, "beta_mode %d is not GDN_BETA_ERASE or GDN_BETA_WRITE", d->beta_mode);
-  if (d->flags & ~(GDN_FLAG_TIME_KERNELS | GDN_FLAG_DIRECT | GDN_FLAG_THREE_PASS))
+  if (d->flags & ~(GDN_FLAG_TIME_KERNELS | GDN_FLAG_DIRECT | GDN_FLAG_THREE_PASS | GDN_FLAG_ONE_LAUNCH))
     return fail(GDN_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if ((d->flags & GDN_FLAG_THREE_PASS) && (d->flags & GDN_FLAG_ONE_LAUNCH))
+    return fail(GDN_ERR_UNSUPPORTED, "GDN_FLAG_THREE_PASS and GDN_FLAG_ONE_LAUNCH exclude each other");
   if ((d->flags & GDN_FLAG_DIRECT) && d->io_dtype == GDN_FP8_E4M3)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_FLAG_DIRECT is for bf16 I/O; e4m3 I/O runs the Gram pipeline only");
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->S < 1 || d->D < 1)
@@ -393,9 +395,22 @@ struct FusedPlan {
   size_t ctl = 0, gring = 0, mring = 0, total = 0;
 };
 
+// Work below which the one-launch form is not the default: its fixed cost
+// (a cooperative launch of every workgroup, the clear of the control block,
+// the serial chain filling and draining the pipeline, about 35-45 us) only
+// pays off on long sequences; on a 4-frame streaming chunk or a tiny call the
+// three launches finish first, and with e4m3 I/O the gram items of the
+// one-launch form are compute-bound (measured on MI355X: 720p bf16 3.01 vs
+// 3.39 ms; short clip 161 vs 165 us; 4-frame chunk 47 vs 22 us; e4m3 720p 2.34
+// vs 2.28 ms).  GDN_FLAG_ONE_LAUNCH asks for it whatever the size.
+constexpr double kOneLaunchMinElems = 67108864.0;   // B*H*T*S*D
+
 FusedPlan make_fused_plan(const gdn_desc* d) {
   FusedPlan f;
   if (d->io_dtype == GDN_F32 || (d->flags & (GDN_FLAG_DIRECT | GDN_FLAG_THREE_PASS))) return f;
+  if (!(d->flags & GDN_FLAG_ONE_LAUNCH) &&
+      (d->io_dtype != GDN_BF16 || (double)d->B * d->H * d->T * d->S * d->D < kOneLaunchMinElems))
+    return f;
   static gdn::DeviceOnce once;
   gdn::LaunchInfo li;
   const hipError_t e = once.get([](int dev, gdn::LaunchInfo& info) {

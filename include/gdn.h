@@ -112,15 +112,21 @@ typedef enum gdn_status {
  */
 #define GDN_FLAG_DIRECT 0x2u
 /*
- * bf16/e4m3 I/O: run the Gram pipeline as its three launches (gram pass,
- * state pass, readout; G_t, B_t and the bf16 states go through the
- * workspace in HBM) instead of the default one-launch form, in which every
- * head lives on one XCD and those per-frame terms stay in that XCD's L2.  The
- * two forms compute the same operations in the same order: the results are
- * bitwise equal.  The one-launch form also falls back to this one when the
- * device or the workspace does not allow it.
+ * bf16/e4m3 I/O, the two forms of the Gram pipeline.  Three launches: gram
+ * pass, state pass, readout; G_t, B_t and the bf16 states go through the
+ * workspace in HBM.  One launch: the three roles in one persistent kernel,
+ * every head on one XCD, those per-frame terms handed over in that XCD's L2.
+ * Both compute the same operations in the same order: the results are
+ * bitwise equal.  By default bf16 calls with B*H*T*S*D >= 2^26 take the one
+ * launch (it needs a cooperative launch, at most 16 XCDs, every XCD's
+ * workgroups at least twice its heads' chain workgroups, and the workspace
+ * gdn_workspace_size gives), the rest the three.  GDN_FLAG_THREE_PASS forces
+ * the three launches; GDN_FLAG_ONE_LAUNCH asks for the one launch whatever
+ * the size or dtype (it still falls back where the device or the workspace
+ * does not allow it).  The two flags exclude each other.
  */
 #define GDN_FLAG_THREE_PASS 0x4u
+#define GDN_FLAG_ONE_LAUNCH 0x8u
 
 /* Kernel kinds booked by gdn_kernel_times. */
 #define GDN_KERNEL_RECURRENCE 0 /* single-pass recurrence */

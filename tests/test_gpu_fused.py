@@ -38,7 +38,7 @@ def run(env, inp, path, mode="erase", state=None, ws=None):
     B, H, T, S, D = inp["q"].shape
     if ws is None:
         dt = {torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}[inp["q"].dtype]
-        flags = gdn.binding.FLAG_THREE_PASS if path == "three_pass" else 0
+        flags = {"three_pass": gdn.binding.FLAG_THREE_PASS, "one_launch": gdn.binding.FLAG_ONE_LAUNCH}[path]
         ws = torch.zeros(gdn.workspace_size(gdn.make_desc(B, H, T, S, D, dt, mode, flags)), dtype=torch.uint8,
                          device="cuda")
     out = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], state=state,
@@ -60,7 +60,7 @@ def same(torch, a, b):
 def compare(env, inp, mode="erase", state=None, oracle_heads=None):
     torch, gdn, wl, go = env
     gdn.kernel_times(reset=True)
-    (o1, s1, n1), ws = run(env, inp, "auto", mode, state)
+    (o1, s1, n1), ws = run(env, inp, "one_launch", mode, state)
     kt = gdn.kernel_times(reset=True)
     assert kt["fused"][1] == 1 and kt["gram"][1] == 0, f"the one-launch kernel did not run: {kt}"
     assert abort_word(torch, ws) == 0
@@ -135,7 +135,7 @@ def test_chunked_steps_equal_one_shot(env):
     torch, gdn, wl, go = env
     w = wl.CHUNKED
     inp = {k: v.cuda() for k, v in wl.generate(w).items()}
-    o1, s1, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"])
+    o1, s1, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], path="three_pass")
     B, H, T, S, D = inp["q"].shape
     state = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
     outs = []
@@ -143,7 +143,7 @@ def test_chunked_steps_equal_one_shot(env):
     for t0 in range(0, T, w.chunk):
         sl = slice(t0, min(T, t0 + w.chunk))
         o, _, _ = gdn.frame_step(*(inp[n][:, :, sl].contiguous() for n in ("q", "k", "v", "gamma", "beta")),
-                                 state, commit="inplace", time_kernels=True)
+                                 state, commit="inplace", time_kernels=True, path="one_launch")
         outs.append(o)
     torch.cuda.synchronize()
     assert gdn.kernel_times(reset=True)["fused"][1] == (T + w.chunk - 1) // w.chunk
@@ -151,7 +151,13 @@ def test_chunked_steps_equal_one_shot(env):
 
 
 def test_minute_720p_equals_three_pass(env):
-    """The benchmarked launch: bitwise the three-launch pipeline on every head."""
+    """The benchmarked launch: bitwise the three-launch pipeline on every head
+    (the default path takes the one launch at this size)."""
     torch, gdn, wl, go = env
     inp = wl.generate(wl.MINUTE_720P, device="cuda")
-    compare(env, inp)
+    o1, s1, _ = compare(env, inp)
+    gdn.kernel_times(reset=True)
+    o, s, _ = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], time_kernels=True)
+    torch.cuda.synchronize()
+    assert gdn.kernel_times(reset=True)["fused"][1] == 1, "the default path should take the one launch here"
+    assert torch.equal(o, o1) and torch.equal(s, s1)
