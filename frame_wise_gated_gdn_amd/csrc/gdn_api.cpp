@@ -391,7 +391,7 @@ gdn_status run_direct(const gdn_desc* d, const Plan& p, const Ptrs& x, void* wor
 // ---------------------------------------------------------------------------
 struct FusedPlan {
   bool ok = false;
-  int nx = 0, grid = 0, RG = 0, RM = 0, L = 0;
+  int nx = 0, grid = 0, RG = 0, RM = 0, L = 0, balance = 0;
   size_t ctl = 0, gring = 0, mring = 0, total = 0;
 };
 
@@ -427,13 +427,25 @@ FusedPlan make_fused_plan(const gdn_desc* d) {
   const int cw = (d->D / 16 + gdn::kFusedWaves - 1) / gdn::kFusedWaves;   // chain workgroups per head
   const int nh = (int)((bh + nx - 1) / nx);                  // heads on the fullest XCD
   if (nh * cw > per_x / 2) return f;
-  const int ns = per_x - nh * cw;                            // its stream workgroups
-  const int fly = (ns + 2 * nh - 1) / (2 * nh);              // frame blocks they keep in flight
+  // The readouts of the extra head of XCD x < rem run on XCD x + rem (the
+  // kernel's head placement); per XCD: ng heads with gram items and chain,
+  // nr readout heads, per_x - ng cw stream workgroups.  fly: the frame blocks
+  // the stream workgroups of the busiest XCD keep in flight.
+  f.balance = 1;
+  const int rem = (int)(bh % nx);
+  int fly = 1;
+  for (int x = 0; x < nx; ++x) {
+    const int ng = x < bh ? (int)((bh - x + nx - 1) / nx) : 0;
+    const int nr = ng - (x < rem && x + rem < nx ? 1 : 0) + (x >= rem && x < 2 * rem ? 1 : 0);
+    if (ng + nr == 0) continue;
+    const int ns = per_x - ng * cw;
+    fly = std::max(fly, (ns + ng + nr - 1) / (ng + nr));
+  }
   f.nx = nx;
   f.grid = 2 * li.cus;
   f.RM = std::min(gdn::kFusedMaxRM, 8);
-  f.RG = std::min(gdn::kFusedMaxRG, std::max(10, fly + 6 - f.RM + 2));
-  f.L = std::min(fly + 6, f.RG + f.RM - 1);                 // progress needs L < RG + RM
+  f.RG = std::min(gdn::kFusedMaxRG, std::max(10, fly + 6 - f.RM + 3));
+  f.L = std::min(fly + 6, f.RG + f.RM - 2);                 // progress needs 4 <= L <= RG + RM - 2
   f.ctl = round_up(gdn::fused_ctl_bytes((int)bh));
   f.gring = round_up((size_t)bh * f.RG * gdn::fused_slot_bytes(d->D));
   f.mring = round_up((size_t)bh * f.RM * (size_t)d->D * d->D * 2);
@@ -451,7 +463,7 @@ gdn_status run_fused(const gdn_desc* d, const FusedPlan& f, const Ptrs& x, void*
   fa.gring = ws + f.ctl;
   fa.mring = ws + f.ctl + f.gring;
   fa.BH = d->B * d->H; fa.T = d->T; fa.S = d->S;
-  fa.NX = f.nx; fa.RG = f.RG; fa.RM = f.RM; fa.L = f.L; fa.grid = f.grid;
+  fa.NX = f.nx; fa.RG = f.RG; fa.RM = f.RM; fa.L = f.L; fa.grid = f.grid; fa.balance = f.balance;
   const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
   fa.kscale = (float)c; fa.kscale2 = (float)(c * c);
   const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;

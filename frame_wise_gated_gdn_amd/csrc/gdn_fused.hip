@@ -37,10 +37,16 @@
 // of those frames are free), `gready[s]` (1 + frame of the G_t, B_t in gram
 // slot s) and `rdone[s]` (1 + frame whose state slot s has been read).
 //
-// Progress.  All workgroups are resident (cooperative launch).  An item only
-// waits for chain steps of frames earlier than the ones it produces, and the
-// chain step t only waits for items placed before block max(t, t - RM + L)
-// in the item order; with L < RG + RM no wait closes a cycle.  Every wait is
+// Progress.  All workgroups are resident (cooperative launch).  The chain
+// reads a frame's G three frames ahead and publishes `cdone` a frame late:
+// in its step t it waits for the readout of frame t - RM (block t - RM + L)
+// and the gram item of frame t + 3 (block t + 3), and cdone reaches t + 1 at
+// the end of step t + 1.  So the readout R(h, t) (block t + L) waits on items
+// of blocks up to t + 4 and t + 1 - RM + L, and the gram item G(h, u) (block
+// u) on items of blocks up to u - RG + 4 and u - RG + 1 - RM + L.  Gram items
+// precede the readouts of their block, so with 4 <= L, 5 <= RG and
+// L <= RG + RM - 2 every wait is on an earlier item and the earliest
+// unfinished item can always run.  Every wait is
 // bounded: past kSpinLimit polls, or once another workgroup has given up,
 // the workgroup sets the abort word (the first word of the control block)
 // and leaves; the outputs of that launch are then incomplete.
@@ -66,6 +72,7 @@ constexpr int kFW = kFusedWaves;          // waves per workgroup
 constexpr int kRingChunks = 2;            // gram item: 32-token chunks in flight per wave (even)
 constexpr uint32_t kSpinLimit = 1u << 22; // polls before a wait gives up (far beyond any real wait)
 constexpr int kCoherent = 16;             // cache bits of a device-scope load: miss L1, read L2
+constexpr size_t kPairLds = 56 * 1024;    // LDS that keeps a CU at two workgroups
 
 template <int D>
 struct FShape {
@@ -85,10 +92,13 @@ struct FShape {
   static constexpr size_t gram_lds = 4 * tile_bytes;  // (K, V) x 2 buffers
   static constexpr size_t read_lds = (size_t)kFW * tile_bytes;       // per wave a Q (then O) tile
   static constexpr size_t read_all = read_lds + (size_t)D * D * 2;  // + M_t
-  static constexpr size_t chain_lds = 2 * g_bytes;    // two G slots
+  static constexpr size_t chain_lds = 3 * g_bytes;    // three G slots
   static constexpr size_t lds_bytes = (gram_lds > read_all ? (gram_lds > chain_lds ? gram_lds : chain_lds)
                                                            : (read_all > chain_lds ? read_all : chain_lds)) +
                                       64;             // + broadcast words
+  // requested at launch: at least a third of the CU's 160 KB, so that a CU
+  // holds two workgroups and never three
+  static constexpr size_t launch_lds = lds_bytes > kPairLds ? lds_bytes : kPairLds;
 };
 
 // stored G block k = I(I+1)/2 + L (I >= L) -> I, L
@@ -138,6 +148,10 @@ __device__ __forceinline__ uint32_t poll(const uint32_t* p) {
 __device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);  // a plain store: stays in L2
 }
+// A flag read on other XCDs: a device-scope store, written through the L2
+__device__ __forceinline__ void flag_store_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Wait until *p >= target, polled by the calling wave (all lanes see the
 // same values).  Returns false when the wait gave up (abort word set here or
 // by another workgroup).
@@ -148,7 +162,7 @@ __device__ __forceinline__ bool wait_geq(const FusedArgs& a, const uint32_t* p, 
     if (v >= target) return true;
     if ((n & 31) == 31 && __builtin_amdgcn_readfirstlane(poll(abort_word)) != 0) return false;
     if (n >= kSpinLimit) {
-      flag_store(abort_word, 1u);
+      flag_store_dev(abort_word, 1u);
       return false;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -174,14 +188,21 @@ __device__ __forceinline__ uint32_t poll_chain(const FusedArgs& a, int h) {
 }
 // Waits for this wave's outstanding memory operations (stores included).
 __device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Workgroup barrier that also publishes wave 0's verdict to every wave.
-__device__ __forceinline__ bool barrier_ok(uint32_t* bcast, bool ok_wave0) {
-  if ((threadIdx.x >> 6) == 0 && lane_id() == 0) *bcast = ok_wave0 ? 1u : 0u;
-  __syncthreads();
-  const bool ok = *(volatile uint32_t*)bcast != 0;
-  __syncthreads();
-  return ok;
-}
+// Workgroup barrier that also hands wave 0's verdict to every wave, with one
+// s_barrier per call: the word written alternates between two, and a word is
+// written again only two calls later, once every wave has passed the barrier
+// in between (and so has read it).  Every wave makes the same calls.
+struct Bcast {
+  uint32_t* w;     // two words in LDS
+  uint32_t n;
+  __device__ __forceinline__ bool sync(bool ok_wave0) {
+    uint32_t* p = w + (n & 1u);
+    ++n;
+    if ((threadIdx.x >> 6) == 0 && lane_id() == 0) *p = ok_wave0 ? 1u : 0u;
+    __syncthreads();
+    return *(volatile uint32_t*)p != 0;
+  }
+};
 
 __device__ __forceinline__ unsigned char* gslot(const FusedArgs& a, int h, int s, size_t slot_bytes) {
   return a.gring + ((size_t)h * a.RG + s) * slot_bytes;
@@ -197,7 +218,7 @@ __device__ __forceinline__ unsigned char* mslot(const FusedArgs& a, int h, int s
 // chunks in order, one MFMA per chunk.
 // ---------------------------------------------------------------------------
 template <int D, bool FP8, int W>
-__device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char* smem, uint32_t* bcast, int h,
+__device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char* smem, Bcast& bc, int h,
                                                int t) {
   using Sh = FShape<D>;
   using IO = IoFmt<FP8>;
@@ -289,7 +310,7 @@ __device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char
   const int s = t % a.RG;
   bool ok = true;
   if (W == 0 && t >= a.RG && pslot < (uint32_t)(t - a.RG + 1)) ok = wait_chain<CW>(a, h, (uint32_t)(t - a.RG + 1));
-  if (!barrier_ok(bcast, ok)) return false;
+  if (!bc.sync(ok)) return false;
   unsigned char* gout = gslot(a, h, s, Sh::slot_bytes);
   unsigned char* bout = gout + Sh::g_bytes;
   const float c2 = a.kscale2, c1 = a.kscale;
@@ -319,8 +340,8 @@ __device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char
 // output element the MFMA chain over the k-steps is the readout kernel's.
 // ---------------------------------------------------------------------------
 template <int D, bool FP8>
-__device__ __forceinline__ bool readout_item(const FusedArgs& a, unsigned char* smem, uint32_t* bcast, int h,
-                                             int t) {
+__device__ __forceinline__ bool readout_item(const FusedArgs& a, unsigned char* smem, Bcast& bc, int h,
+                                             int t, bool remote) {
   using Sh = FShape<D>;
   using IO = IoFmt<FP8>;
   using raw = typename IO::raw;
@@ -358,7 +379,7 @@ __device__ __forceinline__ bool readout_item(const FusedArgs& a, unsigned char* 
   for (int r = 0; r < RING; ++r) load_chunk(r, X[r]);
   bool ok = true;
   if (w == 0 && pc < (uint32_t)(t + 1)) ok = wait_chain<CW>(a, h, (uint32_t)(t + 1));
-  if (!barrier_ok(bcast, ok)) return false;
+  if (!bc.sync(ok)) return false;
   const int s = t % a.RM;
   {
     constexpr int NU = D * D * 2 / 16;                                    // 16-byte units of M_t
@@ -370,7 +391,10 @@ __device__ __forceinline__ bool readout_item(const FusedArgs& a, unsigned char* 
     }
   }
   __syncthreads();                                   // M_t in LDS: the loads are done, the slot may be refilled
-  if (w == 0 && l == 0) flag_store(rdone_flag(a, h, s), (uint32_t)(t + 1));
+  if (w == 0 && l == 0) {
+    if (remote) flag_store_dev(rdone_flag(a, h, s), (uint32_t)(t + 1));
+    else flag_store(rdone_flag(a, h, s), (uint32_t)(t + 1));
+  }
   // A operand (jb, kc) of this lane: blocks (jb, 2kc) and (jb, 2kc + 1)
   auto a_frag = [&](int jb, int kc) -> u32x4 {
     const u32x2 lo = *(const u32x2*)(msm + ((size_t)(jb * NB + 2 * kc) * 64 + l) * 8);
@@ -466,8 +490,8 @@ __device__ __forceinline__ bool readout_item(const FusedArgs& a, unsigned char* 
 // (I, j).  Value tiles evolve independently, so the chain workgroups of a
 // head only share their inputs.
 // ---------------------------------------------------------------------------
-template <int D, bool ERASE, int J>
-__device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* smem, uint32_t* bcast, int h, int c) {
+template <int D, bool ERASE, int J, bool REMOTE>
+__device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* smem, int h, int c) {
   using Sh = FShape<D>;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, NGL = Sh::NGL;
   constexpr int LPG = (NGL + kFW - 1) / kFW;         // G pieces loaded per wave
@@ -475,7 +499,7 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
   const int T = a.T;
   const int j = kFW * c + J;                         // value tile of this wave
   const bool own = j < NB;                           // waves past NB only help with G
-  unsigned char* const gsl = smem;                   // two G slots
+  unsigned char* const gsl = smem;                   // three G slots
 
   f32x4 m[NB];
   const int col = 16 * (own ? j : 0) + n;
@@ -490,35 +514,50 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
   }
   const __amdgpu_buffer_rsrc_t gars = make_rsrc(a.gamma + (size_t)h * T, (uint32_t)(T * 4));
   const __amdgpu_buffer_rsrc_t bers = make_rsrc(a.beta + (size_t)h * T, (uint32_t)(T * 4));
+  auto slot_rsrc = [&](int f) {
+    return make_rsrc(gslot(a, h, f < T ? f % a.RG : 0, Sh::slot_bytes), (uint32_t)Sh::slot_bytes);
+  };
 
-  u32x4 Gr[LPG];
-  u32x2 Bn[NB];
-  float gan = 0.f, ben = 0.f;
-  // G, B, gamma and beta of frame f into the next-frame registers
-  auto load_frame = [&](int f) {
+  // Register buffers (the frame loop is unrolled by two, so every buffer
+  // index is a constant): Gr[f & 1] holds this wave's G pieces of frame f from
+  // their load (during frame f - 3) to their staging (during frame f - 2);
+  // Bn[f & 1], ga[f & 1], be[f & 1] frame f's B blocks, gamma and beta from
+  // their load (during frame f - 1) to their use.
+  u32x4 Gr[2][LPG];
+  u32x2 Bn[2][NB];
+  float ga[2] = {0.f, 0.f}, be[2] = {0.f, 0.f};
+  auto load_g = [&](int f, auto bc_) {
+    constexpr int r = decltype(bc_)::value;
     const bool ok = f < T;
-    const unsigned char* sl = gslot(a, h, ok ? f % a.RG : 0, Sh::slot_bytes);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sl, (uint32_t)Sh::slot_bytes);
-    gan = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gars, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
-    ben = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bers, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(f);
 #pragma unroll
     for (int i = 0; i < LPG; ++i) {
       const int q = J + kFW * i;
-      Gr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, (ok && q < NGL) ? (uint32_t)(q * 1024 + l * 16) : kOOB, 0,
-                                            kCoherent));
+      Gr[r][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rs, (ok && q < NGL) ? (uint32_t)(q * 1024 + l * 16) : kOOB, 0,
+                                               kCoherent));
     }
+  };
+  auto load_b = [&](int f, auto bc_) {
+    constexpr int r = decltype(bc_)::value;
+    const bool ok = f < T;                           // issued in any case (out of range: no access)
+    const __amdgpu_buffer_rsrc_t rs = slot_rsrc(f);
+    ga[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gars, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
+    be[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bers, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
 #pragma unroll
     for (int I = 0; I < NB; ++I)
-      Bn[I] = __builtin_bit_cast(
+      Bn[r][I] = __builtin_bit_cast(
           u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                      rs, (ok && own) ? (uint32_t)(Sh::g_bytes + ((j * NB + I) * 512 + l * 8)) : kOOB, 0, kCoherent));
   };
-  auto stage_g = [&](int slot) {
+  auto stage_g = [&](int f, auto bc_) {             // buffer r's G (frame f) into LDS slot f mod 3
+    constexpr int r = decltype(bc_)::value;
+    unsigned char* dst = gsl + (size_t)(f % 3) * Sh::g_bytes;
+    asm volatile("" ::"v"(Gr[r][LPG - 1]));
 #pragma unroll
     for (int i = 0; i < LPG; ++i) {
       const int q = J + kFW * i;
-      if (q < NGL) *(u32x4*)(gsl + (size_t)slot * Sh::g_bytes + q * 1024 + l * 16) = Gr[i];
+      if (q < NGL) *(u32x4*)(dst + q * 1024 + l * 16) = Gr[r][i];
     }
   };
   // A operand half for key block I, k-block L: row n of block (I, L), columns 4g..4g+3
@@ -534,42 +573,52 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
     }
   };
 
-  // Per frame t the G_t, B_t, gamma_t and beta_t are already in LDS and
-  // registers (loaded during frame t-1), and the polls of gready(t+1) and of
-  // this frame's state slot were issued during frame t-1.  The loads of frame
-  // t+1 are issued before the frame's MFMAs, so their latency overlaps the
-  // arithmetic.  cdone = t (M_0..M_{t-1} stored) is published during frame t,
-  // once the loads of frame t+1 are back: they were issued after the state
-  // stores of frame t-1, and a wave's vector memory operations complete in
-  // order.
+  // Frame f, per wave: the MFMAs and the update (G from LDS slot f mod 3, B
+  // and the gates from registers); the check that frame f - RM's readout has
+  // copied its state slot; the polls for frame f + 1; frame f + 1's B and
+  // gates into registers; the bf16 M_f into the state ring; the check that
+  // gram slot f + 3 is filled and its G into registers; frame f + 2's G
+  // (loaded during frame f - 1) into LDS slot (f + 2) mod 3; then the one
+  // barrier of the frame, after which cdone = f.  Each wave checks the flags
+  // its own loads and stores depend on, so no barrier waits on a broadcast.
+  // A wave's vector memory operations complete in order: once every wave has
+  // its frame f + 2 G back, the M_{f-1} stores issued before those loads are
+  // in the L2 (cdone = f: M_0..M_{f-1} stored), and the loads of frames up to
+  // f are complete (their gram slots are free).  The same memory operations
+  // are issued on every path (out-of-range offsets where there is nothing to
+  // do), so the waits the compiler places for a value cover exactly the
+  // operations issued up to that value's load: each wait is on loads issued
+  // at least a frame earlier.  A wave whose wait gave up (abort word set)
+  // stops waiting and runs to the end, so the barriers still match.
   auto gready_of = [&](int f) { return gready_flag(a, h, f % a.RG); };
   auto rdone_of = [&](int f) { return rdone_flag(a, h, f % a.RM); };
   uint32_t* const cdone = cdone_flag(a, h, c);
-  bool ok = true;
-  if (J == 0) ok = wait_geq(a, gready_of(0), 1u);
-  if (!barrier_ok(bcast, ok)) return;
-  load_frame(0);
-  uint32_t pg = (J == 0 && T > 1) ? poll(gready_of(1)) : 0u;          // gready(t + 1), in flight
-  uint32_t pr = 0u;                                                   // rdone of frame t's state slot
-  wait_memory();
-  stage_g(0);
+  bool live = true;
+  auto check = [&](uint32_t polled, const uint32_t* flag, uint32_t target) {
+    if (live && __builtin_amdgcn_readfirstlane(polled) < target) live = wait_geq(a, flag, target);
+  };
+  auto store_flag = [&](uint32_t v) {
+    if constexpr (REMOTE) flag_store_dev(cdone, v);
+    else flag_store(cdone, v);
+  };
+  const __amdgpu_buffer_rsrc_t mring_rs = make_rsrc(mslot(a, h, 0, D), (uint32_t)(a.RM * D * D * 2));
+  for (int f = 0; f < 3 && f < T; ++f) check(0u, gready_of(f), (uint32_t)(f + 1));
+  load_g(0, Int<0>{});
+  load_g(1, Int<1>{});
+  stage_g(0, Int<0>{});
+  stage_g(1, Int<1>{});
+  uint32_t pr[2], pg[2];              // polled rdone of frame f's state slot, gready of frame f + 3
+  pr[0] = poll(rdone_of(0));
+  pg[0] = poll(gready_of(3));
+  load_b(0, Int<0>{});
+  load_g(2, Int<0>{});
   __syncthreads();
 
-  for (int t = 0; t < T; ++t) {
-    const unsigned char* gs = gsl + (size_t)(t & 1) * Sh::g_bytes;
-    const float gm = gan, bt = ben, bg = bt * gm;
-    u32x2 Bc[NB];
-#pragma unroll
-    for (int I = 0; I < NB; ++I) Bc[I] = Bn[I];
-    // frame t+1 must be in its gram slot before its loads
-    ok = true;
-    if (J == 0 && t + 1 < T && __builtin_amdgcn_readfirstlane(pg) < (uint32_t)(t + 2))
-      ok = wait_geq(a, gready_of(t + 1), (uint32_t)(t + 2));
-    if (!barrier_ok(bcast, ok)) return;
-    load_frame(t + 1);
-    pg = (J == 0 && t + 2 < T) ? poll(gready_of(t + 2)) : 0u;
-    pr = (J == 0 && t >= a.RM) ? poll(rdone_of(t)) : 0u;
+  auto frame = [&](auto rc, int f) {
+    constexpr int r = decltype(rc)::value;
     if (own) {
+      const unsigned char* gs = gsl + (size_t)(f % 3) * Sh::g_bytes;
+      const float gm = ga[r], bt = be[r], bg = bt * gm;
       // B operand: bf16 of the state column tile in k-slot order
       u32x4 bop[NKC];
 #pragma unroll
@@ -594,35 +643,40 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb) acc = mfma_bf16(aop[kb], bop[kb], acc);
-        const u32x2 bw = Bc[I];
+        const u32x2 bw = Bn[r][I];
         const f32x4 bin = {bf16_lo_f32(bw[0]), bf16_hi_f32(bw[0]), bf16_lo_f32(bw[1]), bf16_hi_f32(bw[1])};
 #pragma unroll
         for (int e = 0; e < 4; ++e) m[I][e] = state_update(gm, m[I][e], bg, acc[e], ERASE ? bin[e] : bt * bin[e]);
       });
+      // the state slot of frame f must have been read (frame f - RM done)
+      if (f >= a.RM) check(pr[r], rdone_of(f), (uint32_t)(f - a.RM + 1));
     }
-    // the state slot of frame t must have been read (frame t - RM done)
-    ok = true;
-    if (J == 0 && t >= a.RM && __builtin_amdgcn_readfirstlane(pr) < (uint32_t)(t - a.RM + 1))
-      ok = wait_geq(a, rdone_of(t), (uint32_t)(t - a.RM + 1));
-    if (!barrier_ok(bcast, ok)) return;
-    if (own) {
-      unsigned char* ms = mslot(a, h, t % a.RM, D);
+    pr[r ^ 1] = poll(rdone_of(f + 1));
+    pg[r ^ 1] = poll(gready_of(f + 4));
+    load_b(f + 1, Int<r ^ 1>{});
+    {
+      const uint32_t base = (uint32_t)((f % a.RM) * D * D * 2);
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         const u32x2 pub = {pack_bf16(m[I][0], m[I][1]), pack_bf16(m[I][2], m[I][3])};
-        *(u32x2*)(ms + ((size_t)(j * NB + I) * 64 + l) * 8) = pub;
+        const uint32_t off = own ? base + (uint32_t)(((j * NB + I) * 64 + l) * 8) : kOOB;
+        // a state read on another XCD is written through the L2
+        __builtin_amdgcn_raw_buffer_store_b64(pub, mring_rs, off, 0, REMOTE ? kCoherent : 0);
       }
     }
-    // G of frame t+1 into the other LDS slot; the loads of frame t+1 (and
-    // everything issued before them: the state stores of frame t-1) are done
-    asm volatile("" ::"v"(Gr[LPG - 1]), "v"(Bn[NB - 1]));
-    stage_g((t + 1) & 1);
+    if (f + 3 < T) check(pg[r], gready_of(f + 3), (uint32_t)(f + 4));
+    load_g(f + 3, Int<r ^ 1>{});
+    stage_g(f + 2, Int<r>{});
     __syncthreads();
-    if (J == 0 && l == 0 && t > 0) flag_store(cdone, (uint32_t)t);
+    if (J == 0 && l == 0 && f >= 1 && live) store_flag((uint32_t)f);
+  };
+  for (int t = 0; t < T; t += 2) {
+    frame(Int<0>{}, t);
+    if (t + 1 < T) frame(Int<1>{}, t + 1);
   }
   wait_memory();
   __syncthreads();
-  if (J == 0 && l == 0) flag_store(cdone, (uint32_t)T);
+  if (J == 0 && l == 0 && live) store_flag((uint32_t)T);
   if (own && a.state_out) {
     float* dst = a.state_out + (size_t)h * D * D;
 #pragma unroll
@@ -636,48 +690,79 @@ template <int D, bool FP8, bool ERASE>
 __global__ __launch_bounds__(kFusedWaves * 64, 2) void gdn_fused_kernel(FusedArgs a) {
   using Sh = FShape<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint32_t* bcast = (uint32_t*)(smem + Sh::lds_bytes - 64);
+  Bcast bc{(uint32_t*)(smem + Sh::lds_bytes - 64), 0u};
+  uint32_t* bcast = bc.w + 2;                                          // the ticket's broadcast word
   const int NX = a.NX;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // The XCD this workgroup runs on, from the hardware, and its rank among the
-  // workgroups of that XCD (a ticket): the dispatcher deals workgroups to the
-  // XCDs round-robin, grid/NX to each, but the XCD of workgroup 0 depends on
-  // earlier launches, so the workgroup id does not tell.
-  uint32_t xcc;
+  // The XCD this workgroup runs on and its CU, from the hardware.  The
+  // dispatcher deals workgroups to the XCDs round-robin, grid/NX to each, but
+  // the XCD of workgroup 0 depends on earlier launches, so the workgroup id
+  // does not tell; and every CU holds exactly two workgroups (the launch
+  // size and its LDS request).  The first of a CU's two takes the CU's rank
+  // among the CUs of its XCD (a ticket) and posts it; the second reads it.
+  // p = 2 rank + (0 or 1) numbers the XCD's workgroups so that p and p ^ 1
+  // share a CU: the chain workgroups, p < nh CW, then sit in pairs on CUs of
+  // their own, away from the streaming workgroups' memory traffic.
+  uint32_t xcc, hwid;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hwid));
   const int x = (int)(xcc & 0xFu);
   const int nwg = (int)gridDim.x / NX;                                 // workgroups on each XCD
   if (threadIdx.x == 0) {
-    const uint32_t r = x < NX ? __hip_atomic_fetch_add((uint32_t*)(a.ctl + kFusedCtlTicket + 64 * x), 1u,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : 0xffffffffu;
-    *bcast = r;
+    uint32_t pos = 0xffffffffu;
+    if (x < NX) {
+      uint32_t* cu = (uint32_t*)(a.ctl + kFusedCtlCu + ((size_t)x * 256 + ((hwid >> 8) & 0xFFu)) * 8);
+      const uint32_t slot = __hip_atomic_fetch_add(cu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (slot == 0) {
+        const uint32_t rank = __hip_atomic_fetch_add((uint32_t*)(a.ctl + kFusedCtlTicket + 64 * x), 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flag_store(cu + 1, rank + 1u);
+        pos = 2 * rank;
+      } else if (slot == 1 && wait_geq(a, cu + 1, 1u)) {
+        pos = 2 * (poll(cu + 1) - 1u) + 1u;
+      }
+    }
+    *bcast = pos;
   }
   __syncthreads();
   const int rank = (int)__builtin_amdgcn_readfirstlane(*(volatile uint32_t*)bcast);
   __syncthreads();
-  if (x >= NX || rank >= nwg) {
-    // an XCD with more workgroups than its share: the item split would not hold
-    if (threadIdx.x == 0) flag_store((uint32_t*)a.ctl, 2u);
+  if (x >= NX || rank < 0 || rank >= nwg) {
+    // an XCD with more workgroups than its share, or a CU with more than two
+    if (threadIdx.x == 0) flag_store_dev((uint32_t*)a.ctl, 2u);
     return;
   }
   constexpr int CW = chain_wgs<D>();
-  const int nh = x < a.BH ? (a.BH - x + NX - 1) / NX : 0;              // heads on this XCD
+  // Heads: head h's gram items and chain on XCD h mod NX.  With BH = q NX +
+  // rem and a.balance set, the XCDs x < rem hold one head more than the
+  // others; the readouts of that last head go to XCD x + rem (when it
+  // exists), so that every XCD then streams about the same bytes.  Such a
+  // head's state copies and flags are written through the L2 (device-scope
+  // stores), read with device-scope loads on the other XCD.
+  const int q = a.BH / NX, rem = a.BH % NX;
+  const int nh = x < a.BH ? (a.BH - x + NX - 1) / NX : 0;              // heads of this XCD
+  const bool moved = a.balance && x < rem && x + rem < NX;             // last head's readouts elsewhere
+  const bool incoming = a.balance && x >= rem && x < 2 * rem;          // readouts of head x - rem + q NX here
+  const int nr = nh - (moved ? 1 : 0) + (incoming ? 1 : 0);            // readout heads
   if (rank < nh * CW) {
-    const int h = x + NX * (rank / CW), c = rank % CW;
+    const int hi = rank / CW, h = x + NX * hi, c = rank % CW;
+    const bool remote = moved && hi == nh - 1;
     static_for<kFW>([&](auto wc) {
       constexpr int W = decltype(wc)::value;
-      if (w == W) chain_wave<D, ERASE, W>(a, smem, bcast, h, c);
+      if (w == W) {
+        if (remote) chain_wave<D, ERASE, W, true>(a, smem, h, c);
+        else chain_wave<D, ERASE, W, false>(a, smem, h, c);
+      }
     });
     return;
   }
   const int ns = nwg - nh * CW, k = rank - nh * CW;                    // stream workgroups of this XCD
-  if (nh == 0) return;
+  if (nh + nr == 0) return;
   if (ns <= 0) {
-    if (threadIdx.x == 0) flag_store((uint32_t*)a.ctl, 3u);             // no stream workgroup: give up
+    if (threadIdx.x == 0) flag_store_dev((uint32_t*)a.ctl, 3u);         // no stream workgroup: give up
     return;
   }
-  const long long per_block = 2LL * nh;
+  const long long per_block = (long long)nh + nr;
   const long long nitems = per_block * (long long)(a.T + a.L);
   for (long long it = k; it < nitems; it += ns) {
     const int u = (int)(it / per_block), r = (int)(it % per_block);
@@ -687,12 +772,14 @@ __global__ __launch_bounds__(kFusedWaves * 64, 2) void gdn_fused_kernel(FusedArg
       const int h = x + NX * r;
       static_for<kFW>([&](auto wc) {
         constexpr int W = decltype(wc)::value;
-        if (w == W) ok = gram_item_wave<D, FP8, W>(a, smem, bcast, h, u);
+        if (w == W) ok = gram_item_wave<D, FP8, W>(a, smem, bc, h, u);
       });
     } else {
       const int t = u - a.L;
       if (t < 0 || t >= a.T) continue;
-      ok = readout_item<D, FP8>(a, smem, bcast, x + NX * (r - nh), t);
+      const int ri = r - nh;
+      const bool remote = incoming && ri == nr - 1;
+      ok = readout_item<D, FP8>(a, smem, bc, remote ? x - rem + NX * q : x + NX * ri, t, remote);
     }
     if (!ok) return;
     __syncthreads();                                                   // LDS reuse by the next item
@@ -709,7 +796,7 @@ hipError_t launch_fused_t3(const FusedArgs& fa, int grid, hipStream_t stream) {
   FusedArgs arg = fa;
   void* params[] = {&arg};
   return hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(kFusedWaves * 64), params,
-                                    (unsigned)FShape<D>::lds_bytes, stream);
+                                    (unsigned)FShape<D>::launch_lds, stream);
 }
 
 template <int D>
@@ -722,14 +809,14 @@ hipError_t launch_fused_t(const FusedArgs& fa, int fp8, int erase, hipStream_t s
     hipError_t e = hipSuccess;
     int per_cu = 1 << 30;
     for (int i = 0; i < 4 && e == hipSuccess; ++i) {
-      e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)FShape<D>::lds_bytes);
+      e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)FShape<D>::launch_lds);
       int occ = 0;
       if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fns[i], kFusedWaves * 64, FShape<D>::lds_bytes);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fns[i], kFusedWaves * 64, FShape<D>::launch_lds);
       per_cu = occ < per_cu ? occ : per_cu;
     }
     if (e == hipSuccess) e = hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
-    info.slots = per_cu >= 2 ? 2 * info.cus : 0;                   // two workgroups per CU
+    info.slots = per_cu == 2 ? 2 * info.cus : 0;                   // two workgroups per CU, exactly
     return e;
   }, &li);
   if (ie != hipSuccess) return ie;

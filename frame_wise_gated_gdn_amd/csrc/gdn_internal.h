@@ -183,7 +183,8 @@ constexpr int kFusedMaxRG = 48;           // gram ring slots per head (at most)
 constexpr int kFusedMaxRM = 16;           // state ring slots per head (at most)
 constexpr int kFusedMaxCW = 2;            // chain workgroups per head (one per 4 value tiles)
 constexpr size_t kFusedCtlTicket = 64;    // control block: abort word at 0, per-XCD tickets from here
-constexpr size_t kFusedCtlHead = 2048;    // (64 bytes apart, up to 16 XCDs), then per-head flags
+constexpr size_t kFusedCtlCu = 2048;      // (64 bytes apart, up to 16 XCDs), then per-CU words (two
+constexpr size_t kFusedCtlHead = kFusedCtlCu + 16 * 256 * 8;   // per CU id and XCD), then per-head flags
 constexpr size_t kFusedCtlPerHead = 8192;
 inline size_t fused_ctl_bytes(int BH) { return kFusedCtlHead + (size_t)BH * kFusedCtlPerHead; }
 // per head: the chain workgroups' progress words, then gready per gram slot,
@@ -206,7 +207,8 @@ struct FusedArgs {
   unsigned char* mring;     // [BH][RM] x D*D*2 (bf16 state, snapshot block layout)
   int BH, T, S;
   int NX;                   // XCDs; head h lives on XCD h % NX
-  int RG, RM, L;            // ring slots per head; readout lag in frames (L < RG + RM)
+  int RG, RM, L;            // ring slots per head; readout lag in frames (4 <= L <= RG + RM - 2, 5 <= RG)
+  int balance;              // 1: the readouts of an XCD's extra head run on a less loaded XCD
   int grid;                 // workgroups (two per CU, a multiple of NX)
   float kscale, kscale2;    // 1/sqrt(D*S) and 1/(D*S), each rounded once to fp32
 };

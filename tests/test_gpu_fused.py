@@ -102,10 +102,12 @@ def test_token_counts_modes_and_state(env, S, mode):
     compare(env, inp, mode=mode, state=m0, oracle_heads=[(1, 4)])
 
 
-@pytest.mark.parametrize("BH", [1, 8, 9, 20, 40])
+@pytest.mark.parametrize("BH", [1, 5, 8, 9, 13, 20, 40])
 def test_head_counts(env, BH):
-    """Heads dealt to the XCDs: fewer heads than XCDs, one per XCD, one more,
-    the 720p head count (three or two per XCD) and five per XCD."""
+    """Heads dealt to the XCDs: fewer heads than XCDs (all extra heads' readouts
+    moved to another XCD, or only some of them), one per XCD, one more, the
+    720p head count (three or two per XCD, four readouts moved) and five per
+    XCD."""
     torch, gdn, wl, go = env
     inp = {k: v.cuda() for k, v in wl.generate(wl.Workload("f", 1, BH, 40, 96, 112, gamma=(0.9, 1.0),
                                                               beta=(0.1, 1.0))).items()}
