@@ -548,6 +548,29 @@ def main():
         "kernels_ms_per_step": kms,
         "ms_per_step_with_kernel_events": dt_ev * 1e3 / args.steps,
     }
+    # context for the HBM fraction: one elementwise kernel with the same
+    # bytes as the step (three bf16 reads of the input size, one write),
+    # torch.addcmul on the same tensors
+    sink = torch.empty_like(out)
+    for _ in range(2):
+        torch.addcmul(inp["q"], inp["k"], inp["v"], out=sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(5):
+        e0.record()
+        torch.addcmul(inp["q"], inp["k"], inp["v"], out=sink)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del sink
+    ems = min(ts)
+    rec["streaming_reference"] = {
+        "what": "torch.addcmul(q, k, v) on the step's tensors: one elementwise kernel, 3 reads + 1 write of "
+                "the step's bf16 size (no recurrence)",
+        "ms": ems, "GB_per_s": path_bytes / (ems * 1e-3) / 1e9,
+        "frac_of_peak": path_bytes / (ems * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_over_reference": ms_step / ems}
     if args.path == "auto":
         # the same step as three launches (same bits), for context
         ws3 = torch.empty(gdn.workspace_size(gdn.make_desc(w.B, w.H, w.T, w.S, w.D, w.dtype, w.beta_mode,

@@ -399,17 +399,21 @@ struct FusedPlan {
 // (a cooperative launch of every workgroup, the clear of the control block,
 // the serial chain filling and draining the pipeline, about 35-45 us) only
 // pays off on long sequences; on a 4-frame streaming chunk or a tiny call the
-// three launches finish first, and with e4m3 I/O the gram items of the
-// one-launch form are compute-bound (measured on MI355X: 720p bf16 3.01 vs
-// 3.39 ms; short clip 161 vs 165 us; 4-frame chunk 47 vs 22 us; e4m3 720p 2.34
-// vs 2.28 ms).  GDN_FLAG_ONE_LAUNCH asks for it whatever the size.
-constexpr double kOneLaunchMinElems = 67108864.0;   // B*H*T*S*D
+// three launches finish first.  With e4m3 I/O the frames are half the bytes
+// and the serial chain, not the memory traffic, sets the pace, so the one
+// launch needs longer calls to win (measured on MI355X, one launch vs three:
+// 720p bf16 2.88 vs 3.39 ms; short clip bf16 146 vs 166 us, e4m3 134 vs
+// 124 us; 720p e4m3 2.07 vs 2.30 ms; 4-frame chunk 50 vs 22 us).
+// GDN_FLAG_ONE_LAUNCH asks for it whatever the size.
+constexpr double kOneLaunchMinElems = 67108864.0;      // B*H*T*S*D, bf16 I/O
+constexpr double kOneLaunchMinElemsFp8 = 268435456.0;  // e4m3 I/O
 
 FusedPlan make_fused_plan(const gdn_desc* d) {
   FusedPlan f;
   if (d->io_dtype == GDN_F32 || (d->flags & (GDN_FLAG_DIRECT | GDN_FLAG_THREE_PASS))) return f;
   if (!(d->flags & GDN_FLAG_ONE_LAUNCH) &&
-      (d->io_dtype != GDN_BF16 || (double)d->B * d->H * d->T * d->S * d->D < kOneLaunchMinElems))
+      (double)d->B * d->H * d->T * d->S * d->D <
+          (d->io_dtype == GDN_BF16 ? kOneLaunchMinElems : kOneLaunchMinElemsFp8))
     return f;
   static gdn::DeviceOnce once;
   gdn::LaunchInfo li;

@@ -608,9 +608,23 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
   stage_g(0, Int<0>{});
   stage_g(1, Int<1>{});
   uint32_t pr[2], pg[2];              // polled rdone of frame f's state slot, gready of frame f + 3
+  // the state stores of a frame (none here: out of range); the prologue
+  // issues what a frame issues, in the same order, so that the loop entry
+  // and the loop back edge agree on the operations in flight
+  auto store_m = [&](int f) {
+    const uint32_t base = (uint32_t)((f % a.RM) * D * D * 2);
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      const u32x2 pub = {pack_bf16(m[I][0], m[I][1]), pack_bf16(m[I][2], m[I][3])};
+      const uint32_t off = (own && f >= 0) ? base + (uint32_t)(((j * NB + I) * 64 + l) * 8) : kOOB;
+      // a state read on another XCD is written through the L2
+      __builtin_amdgcn_raw_buffer_store_b64(pub, mring_rs, off, 0, REMOTE ? kCoherent : 0);
+    }
+  };
   pr[0] = poll(rdone_of(0));
   pg[0] = poll(gready_of(3));
   load_b(0, Int<0>{});
+  store_m(-1);
   load_g(2, Int<0>{});
   __syncthreads();
 
@@ -654,26 +668,19 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
     pr[r ^ 1] = poll(rdone_of(f + 1));
     pg[r ^ 1] = poll(gready_of(f + 4));
     load_b(f + 1, Int<r ^ 1>{});
-    {
-      const uint32_t base = (uint32_t)((f % a.RM) * D * D * 2);
-#pragma unroll
-      for (int I = 0; I < NB; ++I) {
-        const u32x2 pub = {pack_bf16(m[I][0], m[I][1]), pack_bf16(m[I][2], m[I][3])};
-        const uint32_t off = own ? base + (uint32_t)(((j * NB + I) * 64 + l) * 8) : kOOB;
-        // a state read on another XCD is written through the L2
-        __builtin_amdgcn_raw_buffer_store_b64(pub, mring_rs, off, 0, REMOTE ? kCoherent : 0);
-      }
-    }
+    store_m(f);
     if (f + 3 < T) check(pg[r], gready_of(f + 3), (uint32_t)(f + 4));
     load_g(f + 3, Int<r ^ 1>{});
     stage_g(f + 2, Int<r>{});
     __syncthreads();
     if (J == 0 && l == 0 && f >= 1 && live) store_flag((uint32_t)f);
   };
-  for (int t = 0; t < T; t += 2) {
+  int t = 0;
+  for (; t + 1 < T; t += 2) {
     frame(Int<0>{}, t);
-    if (t + 1 < T) frame(Int<1>{}, t + 1);
+    frame(Int<1>{}, t + 1);
   }
+  if (t < T) frame(Int<0>{}, t);
   wait_memory();
   __syncthreads();
   if (J == 0 && l == 0 && live) store_flag((uint32_t)T);

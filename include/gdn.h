@@ -117,10 +117,11 @@ typedef enum gdn_status {
  * workspace in HBM.  One launch: the three roles in one persistent kernel,
  * every head on one XCD, those per-frame terms handed over in that XCD's L2.
  * Both compute the same operations in the same order: the results are
- * bitwise equal.  By default bf16 calls with B*H*T*S*D >= 2^26 take the one
- * launch (it needs a cooperative launch, at most 16 XCDs, every XCD's
- * workgroups at least twice its heads' chain workgroups, and the workspace
- * gdn_workspace_size gives), the rest the three.  GDN_FLAG_THREE_PASS forces
+ * bitwise equal.  By default calls with B*H*T*S*D >= 2^26 (bf16) or
+ * >= 2^28 (e4m3) take the one launch (it needs a cooperative launch, at most
+ * 16 XCDs, every XCD's workgroups at least twice its heads' chain
+ * workgroups, and the workspace gdn_workspace_size gives), the rest the
+ * three.  GDN_FLAG_THREE_PASS forces
  * the three launches; GDN_FLAG_ONE_LAUNCH asks for the one launch whatever
  * the size or dtype (it still falls back where the device or the workspace
  * does not allow it).  The two flags exclude each other.
