@@ -862,6 +862,54 @@ gdn_status run_backward(const gdn_desc* d, const void* q, const void* k, const v
   return GDN_OK;
 }
 
+// The checks of gdn_check_args; with_workspace = false leaves the workspace
+// out (a caller that has none yet checks the tensors first).
+gdn_status check_io(const gdn_desc* d, const void* q, const void* k, const void* v, const float* gamma,
+                    const float* beta, const float* state_in, const void* o, const float* state_out,
+                    const float* state_norms, const void* workspace, size_t workspace_bytes, int state_in_required,
+                    bool with_workspace) {
+  g_last_error.clear();
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v) return fail(GDN_ERR_NULL, "q, k and v are required");
+  if (!gamma || !beta) return fail(GDN_ERR_NULL, "gamma and beta are required");
+  if (!o) return fail(GDN_ERR_NULL, "o is required");
+  if (state_in_required && !state_in) return fail(GDN_ERR_NULL, "gdn_frame_step requires state_in");
+  if (!with_workspace) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+  } else if (!workspace) {
+    return fail(GDN_ERR_WORKSPACE, "workspace is required (gdn_workspace_size)");
+  }
+  const Plan p = make_plan(d);
+  if (with_workspace && workspace_bytes < ws_bytes_for(p, 1))
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, ws_bytes_for(p, 1));
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+  if (misaligned(gamma, 4) || misaligned(beta, 4) || misaligned(state_in, 4) || misaligned(state_out, 4) ||
+      misaligned(state_norms, 4))
+    return fail(GDN_ERR_ALIGN, "gamma, beta, states and norms must be 4-byte aligned");
+  if (misaligned(workspace, kAlign)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  struct Buf { const void* p; size_t n; const char* name; };
+  const Buf ins[] = {{q, p.io_bytes, "q"}, {k, p.io_bytes, "k"}, {v, p.io_bytes, "v"},
+                     {gamma, p.gb_bytes, "gamma"}, {beta, p.gb_bytes, "beta"},
+                     {state_in, p.state_bytes, "state_in"}};
+  const Buf outs[] = {{o, p.io_bytes, "o"}, {state_out, p.state_bytes, "state_out"},
+                      {state_norms, p.gb_bytes, "state_norms"}, {workspace, workspace_bytes, "workspace"}};
+  for (const Buf& x : outs) {
+    if (!x.p) continue;
+    for (const Buf& y : ins) {
+      if (x.p == state_out && y.p == state_in && state_out == state_in) continue;  // in place
+      if (overlap(x.p, x.n, y.p, y.n)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
+    }
+    for (const Buf& y : outs)
+      if (&y != &x && y.p && overlap(x.p, x.n, y.p, y.n))
+        return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
+  }
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -869,7 +917,11 @@ extern "C" {
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
 const char* gdn_status_string(gdn_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the bits, not the enum (a value outside
+  // the enumerators' range is not a valid C++ value of the type).
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case GDN_OK: return "GDN_OK";
     case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
     case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: a size is out of range";
@@ -904,41 +956,8 @@ gdn_status gdn_check_args(const gdn_desc* d, const void* q, const void* k, const
                           const float* gamma, const float* beta, const float* state_in,
                           const void* o, const float* state_out, const float* state_norms,
                           const void* workspace, size_t workspace_bytes, int state_in_required) {
-  g_last_error.clear();
-  gdn_status st = check_desc(d);
-  if (st != GDN_OK) return st;
-  if (!q || !k || !v) return fail(GDN_ERR_NULL, "q, k and v are required");
-  if (!gamma || !beta) return fail(GDN_ERR_NULL, "gamma and beta are required");
-  if (!o) return fail(GDN_ERR_NULL, "o is required");
-  if (state_in_required && !state_in) return fail(GDN_ERR_NULL, "gdn_frame_step requires state_in");
-  if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is required (gdn_workspace_size)");
-  const Plan p = make_plan(d);
-  if (workspace_bytes < ws_bytes_for(p, 1))
-    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes < minimum %zu", workspace_bytes, ws_bytes_for(p, 1));
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
-    return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
-  if (misaligned(gamma, 4) || misaligned(beta, 4) || misaligned(state_in, 4) || misaligned(state_out, 4) ||
-      misaligned(state_norms, 4))
-    return fail(GDN_ERR_ALIGN, "gamma, beta, states and norms must be 4-byte aligned");
-  if (misaligned(workspace, kAlign)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
-
-  struct Buf { const void* p; size_t n; const char* name; };
-  const Buf ins[] = {{q, p.io_bytes, "q"}, {k, p.io_bytes, "k"}, {v, p.io_bytes, "v"},
-                     {gamma, p.gb_bytes, "gamma"}, {beta, p.gb_bytes, "beta"},
-                     {state_in, p.state_bytes, "state_in"}};
-  const Buf outs[] = {{o, p.io_bytes, "o"}, {state_out, p.state_bytes, "state_out"},
-                      {state_norms, p.gb_bytes, "state_norms"}, {workspace, workspace_bytes, "workspace"}};
-  for (const Buf& x : outs) {
-    if (!x.p) continue;
-    for (const Buf& y : ins) {
-      if (x.p == state_out && y.p == state_in && state_out == state_in) continue;  // in place
-      if (overlap(x.p, x.n, y.p, y.n)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
-    }
-    for (const Buf& y : outs)
-      if (&y != &x && y.p && overlap(x.p, x.n, y.p, y.n))
-        return fail(GDN_ERR_ALIAS, "%s overlaps %s", x.name, y.name);
-  }
-  return GDN_OK;
+  return check_io(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, workspace, workspace_bytes,
+                  state_in_required, true);
 }
 
 gdn_status gdn_frame_forward(const gdn_desc* d, const void* q, const void* k, const void* v,
@@ -966,6 +985,8 @@ gdn_status gdn_frame_forward_noalloc(const gdn_desc* d, const void* q, const voi
   if (d->flags & GDN_FLAG_TIME_KERNELS)
     return fail(GDN_ERR_UNSUPPORTED, "gdn_frame_forward_noalloc records no kernel times (their events are created "
                                      "on demand)");
+  st = check_io(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, nullptr, 0, 0, false);
+  if (st != GDN_OK) return st;
   const Plan p = make_plan(d);
   const FusedPlan f = p.gram ? make_fused_plan(d) : FusedPlan();
   const size_t need = f.ok ? f.total : ws_bytes_for(p, 1);
