@@ -985,14 +985,15 @@ gdn_status gdn_frame_forward_noalloc(const gdn_desc* d, const void* q, const voi
   if (d->flags & GDN_FLAG_TIME_KERNELS)
     return fail(GDN_ERR_UNSUPPORTED, "gdn_frame_forward_noalloc records no kernel times (their events are created "
                                      "on demand)");
-  st = check_io(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, nullptr, 0, 0, false);
-  if (st != GDN_OK) return st;
   const Plan p = make_plan(d);
   const FusedPlan f = p.gram ? make_fused_plan(d) : FusedPlan();
   const size_t need = f.ok ? f.total : ws_bytes_for(p, 1);
   if (need > gdn::kNoAllocScratchBytes)
     return fail(GDN_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", need,
                 gdn::kNoAllocScratchBytes);
+  // the tensors, before the scratch address is asked for (that touches the device)
+  st = check_io(d, q, k, v, gamma, beta, state_in, o, state_out, state_norms, nullptr, 0, 0, false);
+  if (st != GDN_OK) return st;
   void* scratch = nullptr;
   const hipError_t e = gdn::noalloc_scratch(&scratch);
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
