@@ -11,31 +11,37 @@
 // roles share one launch and hand those per-frame terms over through small
 // rings that stay in the L2 of one XCD:
 //
-//   - every head lives on one XCD (head h on XCD h mod NX); two workgroups
-//     of 4 waves run on every CU; the XCD's first workgroups are the heads'
-//     chain workgroups, the rest are stream workgroups;
+//   - head h's gram items and chain live on XCD h mod NX; two workgroups of
+//     4 waves run on every CU (the launch's LDS request allows no third); the
+//     chain workgroups of the XCD's heads sit in pairs on CUs of their own,
+//     the rest are stream workgroups;
+//   - with BH = q NX + rem, the readouts of the extra head of XCD x < rem run
+//     on XCD x + rem, so that every XCD streams about the same bytes;
 //   - a stream workgroup takes items of its XCD in a fixed order -- per
 //     frame block u: the gram items G(h, u) of the XCD's heads, then the
-//     readout items R(h, u - L) -- item k, k + Ns, k + 2 Ns, ... for the k-th
-//     of Ns stream workgroups;
+//     readout items R(h, u - L) of its readout heads -- item k, k + Ns,
+//     k + 2 Ns, ... for the k-th of Ns stream workgroups;
 //   - G(h, t) reads K_t and V_t once (coalesced, non-temporal), and writes
 //     G_t, B_t into slot t mod RG of the head's gram ring;
-//   - the chain workgroup of h runs the frames in order: G_t, B_t from the
-//     ring, the state in fp32 registers (wave j owns the value-column tiles
-//     j, j + 4, ... of every key block), the bf16 copy of M_t into slot
-//     t mod RM of the head's state ring;
+//   - the chain workgroups of h run the frames in order: G_t, B_t from the
+//     ring, the state in fp32 registers (wave j of chain workgroup c owns
+//     value tile 4c + j, every key block of it), the bf16 copy of M_t into
+//     slot t mod RM of the head's state ring;
 //   - R(h, t) reads the bf16 M_t from the ring and streams Q_t to O_t.
 //
 // Hand-over within an XCD: the producer's plain stores stay in that XCD's L2
 // (write-back); it waits for them to complete, then stores a sequence number
 // in a flag word.  The consumer polls the flag with device-scope loads, which
 // miss the CU's L1 and read the L2, and then reads the data the same way.
-// Every producer and consumer of a ring sit on the same XCD (each workgroup
-// takes its role from its hardware XCC id), so the L2 is the point of
-// coherence and no L2 write-back or invalidation is needed.  Flags: per head, `cdone` (frames of
-// the chain done: M_0..M_{cdone-1} are in the state ring, and the gram slots
-// of those frames are free), `gready[s]` (1 + frame of the G_t, B_t in gram
-// slot s) and `rdone[s]` (1 + frame whose state slot s has been read).
+// Gram items and chain of a head sit on the same XCD (each workgroup takes
+// its role from its hardware XCC id), so there the L2 is the point of
+// coherence and no L2 write-back or invalidation is needed.  The state copies
+// and flags of a head whose readouts run on another XCD are written with
+// device-scope stores, which write through the L2, and read there with
+// device-scope loads.  Flags: per head, `cdone` (frames of the chain done:
+// M_0..M_{cdone-1} are in the state ring, and the gram slots of those frames
+// are free), `gready[s]` (1 + frame of the G_t, B_t in gram slot s) and
+// `rdone[s]` (1 + frame whose state slot s has been read).
 //
 // Progress.  All workgroups are resident (cooperative launch).  The chain
 // reads a frame's G three frames ahead and publishes `cdone` a frame late:
