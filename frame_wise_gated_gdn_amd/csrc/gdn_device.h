@@ -59,6 +59,17 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// e4m3 x e4m3 -> fp32, 16x16x32.  Operand lane layout (checked on the GPU
+// against a host product of small exact values): lane l holds row (column
+// for B) l % 16, k = 8 (l / 16) + j in its byte j; the result as for bf16:
+// lane l holds rows 4 (l / 16) + r, column l % 16.  Numerics (measured on
+// random finite codes, subnormals included, against exact sums): every
+// product is exact, subnormal codes are honoured, but the 32-term sum is not
+// fp32-exact: |result - exact| stayed within 2.2e-4 of the sum of |products|.
+__device__ __forceinline__ f32x4 mfma_fp8(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a), __builtin_bit_cast(long, b), c, 0,
+                                                     0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -68,6 +79,22 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
   return __builtin_bit_cast(u32x2, r);
+}
+
+// Transposing 8-byte LDS read of 8-bit elements.  Within each 16-lane group
+// the lanes' addresses name 16 rows of 8 bytes, D[i][c] (row i from lane i
+// of the group); lane l of the group receives D[l / 8 + 2k][l % 8] in byte k
+// (checked on the GPU with a pattern of known bytes).
+__device__ __forceinline__ u32x2 lds_tr8(const unsigned char* p) {
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+// ReLU of 8 OCP E4M3 codes: a code with the sign bit set (negative values,
+// -0 and the negative NaN) becomes +0, as the bf16 ReLU of its exact value.
+__device__ __forceinline__ u32x2 relu_e4m3x8(u32x2 x) {
+  const uint32_t s0 = (x[0] >> 7) & 0x01010101u, s1 = (x[1] >> 7) & 0x01010101u;
+  return u32x2{x[0] & ~(s0 * 0xFFu), x[1] & ~(s1 * 0xFFu)};
 }
 
 // Wave-local LDS ordering: LDS operations of one wave complete in order; the

@@ -87,6 +87,8 @@ struct FShape {
   static constexpr int UPR = D / 8;                   // 16-byte units per token row (bf16)
   static constexpr int NLD = D / 16;                  // 1 KB pieces per 32-token chunk of one tensor
   static constexpr int RS = D + 8;                    // LDS row stride (elements)
+  static constexpr int RS8 = D + 8;                   // row stride of an e4m3 tile (bytes; rows 8 bytes
+                                                      // off a 16-byte grid keep the transposing reads apart)
   static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
   static constexpr int NBLK = NB * (NB + 1) / 2;      // stored G blocks (I >= L)
   static constexpr int NBB = NB * NB;                 // B blocks
@@ -254,17 +256,35 @@ __device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char
       X[i] = IO::load_nt(p < NLD ? krs : vrs, off);
     }
   };
+  // bf16 I/O: the chunk is staged as bf16 (K through ReLU) and the blocks
+  // are bf16 MFMAs; e4m3 I/O: staged as e4m3 codes, fp8 MFMAs (exact
+  // products, sums within about 2^-12 of the sum of |products|), the gram
+  // kernel's e4m3 form, so both give the same bits
   auto stage = [&](int buf, const raw (&X)[LPW]) {
-    uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
-    uint16_t* vt = kt + 32 * RS;
+    if constexpr (FP8) {
+      unsigned char* kt = smem + (size_t)buf * 2 * Sh::tile_bytes;
+      unsigned char* vt = kt + 32 * Sh::RS8;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int p = W + NW * i;
-      if (p < 2 * NLD) {
-        const int u = 64 * (p % NLD) + l;
-        uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
-        const u32x4 x = IO::to_bf16(X[i]);
-        *(u32x4*)dst = p < NLD ? relu8(x) : x;
+      for (int i = 0; i < LPW; ++i) {
+        const int p = W + NW * i;
+        if (p < 2 * NLD) {
+          const int u = 64 * (p % NLD) + l;
+          unsigned char* dst = (p < NLD ? kt : vt) + (u / UPR) * Sh::RS8 + 8 * (u % UPR);
+          *(u32x2*)dst = p < NLD ? relu_e4m3x8(X[i]) : X[i];
+        }
+      }
+    } else {
+      uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
+      uint16_t* vt = kt + 32 * RS;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int p = W + NW * i;
+        if (p < 2 * NLD) {
+          const int u = 64 * (p % NLD) + l;
+          uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
+          const u32x4 x = IO::to_bf16(X[i]);
+          *(u32x4*)dst = p < NLD ? relu8(x) : x;
+        }
       }
     }
   };
@@ -272,6 +292,10 @@ __device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char
     const uint16_t* p0 = tile + (4 * g + (n >> 2)) * RS + 16 * blk + 4 * (n & 3);
     const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
     return u32x4{x[0], x[1], y[0], y[1]};
+  };
+  // e4m3 operand of block blk: dim 16 blk + l % 16, tokens 8 (l / 16) .. + 7
+  auto frag8 = [&](const unsigned char* tile, int blk) -> u32x2 {
+    return lds_tr8(tile + (8 * g + (n >> 1)) * Sh::RS8 + 16 * blk + 8 * (n & 1));
   };
 
   f32x4 acc[NMB > 0 ? NMB : 1];
@@ -291,7 +315,25 @@ __device__ __forceinline__ bool gram_item_wave(const FusedArgs& a, unsigned char
       stage(r & 1, R[r]);
       load_chunk(c + kRingChunks, R[r]);
       lds_barrier();
-      if (c < nch) {
+      if (c < nch && FP8) {
+        const unsigned char* kt = smem + (size_t)(r & 1) * 2 * Sh::tile_bytes;
+        const unsigned char* vt = kt + 32 * Sh::RS8;
+        u32x2 X[NB], Y[NB];
+        static_for<NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr ((XM >> j) & 1u) X[j] = frag8(kt, j);
+          if constexpr ((YM >> j) & 1u) Y[j] = frag8(vt, j);
+        });
+        static_for<NMB>([&](auto ic) {
+          constexpr int i = decltype(ic)::value, b = B0 + i;
+          if constexpr (b < NBB) {
+            acc[i] = mfma_fp8(X[b % NB], Y[b / NB], acc[i]);
+          } else {
+            constexpr int k = b - NBB;
+            acc[i] = mfma_fp8(X[fblk_col(k)], X[fblk_row(k)], acc[i]);
+          }
+        });
+      } else if (c < nch) {
         const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
         const uint16_t* vt = kt + 32 * RS;
         u32x4 X[NB], Y[NB];

@@ -58,7 +58,11 @@ namespace gdn {
 // (coalesced 1 KB loads spread over the waves, kept kGramRing chunks ahead in
 // registers), passed through ReLU (keys) and staged in a double-buffered LDS
 // tile, from which every wave takes the operands its blocks need with
-// transposed reads, one MFMA per block and chunk.
+// transposed reads, one MFMA per block and chunk.  With e4m3 I/O the tile
+// holds the codes themselves (keys through a sign-bit ReLU) and the blocks
+// are 16x16x32 fp8 MFMAs: the products are those of the decoded values, the
+// 32-term sum inside the instruction is not rounded once to fp32 (on gfx950
+// it lands within about 2^-12 of the sum of |products| of the exact value).
 // ----------------------------------------------------------------------------
 constexpr int kGramRing = 4;   // chunks in flight per workgroup (even: LDS buffer = slot % 2)
 
@@ -71,6 +75,7 @@ struct GramShape {
   static constexpr int NLD = D / 16;                  // 1 KB pieces per 32-token chunk of one tensor
   static constexpr int LPW = (2 * NLD + NW - 1) / NW; // pieces loaded per wave per chunk
   static constexpr int RS = D + 8;                    // LDS row stride (elements)
+  static constexpr int RS8 = D + 8;                   // row stride of an e4m3 tile (bytes)
   static constexpr size_t tile_bytes = (size_t)32 * RS * 2;
   static constexpr size_t lds_bytes = 2 * 2 * tile_bytes;   // (K, V) x 2 buffers
   static constexpr int NBLK = NB * (NB + 1) / 2;       // stored G blocks (I >= L)
@@ -148,17 +153,33 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
       X[i] = IO::load_nt(p < NLD ? krs : vrs, off);
     }
   };
+  // bf16 I/O: staged as bf16 (K through ReLU), bf16 MFMAs; e4m3 I/O:
+  // staged as e4m3 codes, e4m3 MFMAs on the exact codes
   auto stage = [&](int buf, const raw (&X)[LPW]) {
-    uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
-    uint16_t* vt = kt + 32 * RS;
+    if constexpr (FP8) {
+      unsigned char* kt = smem + (size_t)buf * 2 * Sh::tile_bytes;
+      unsigned char* vt = kt + 32 * Sh::RS8;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int p = W + NW * i;
-      if (p < 2 * NLD) {
-        const int u = 64 * (p % NLD) + l;
-        uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
-        const u32x4 x = IO::to_bf16(X[i]);
-        *(u32x4*)dst = p < NLD ? relu8(x) : x;
+      for (int i = 0; i < LPW; ++i) {
+        const int p = W + NW * i;
+        if (p < 2 * NLD) {
+          const int u = 64 * (p % NLD) + l;
+          unsigned char* dst = (p < NLD ? kt : vt) + (u / UPR) * Sh::RS8 + 8 * (u % UPR);
+          *(u32x2*)dst = p < NLD ? relu_e4m3x8(X[i]) : X[i];
+        }
+      }
+    } else {
+      uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
+      uint16_t* vt = kt + 32 * RS;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int p = W + NW * i;
+        if (p < 2 * NLD) {
+          const int u = 64 * (p % NLD) + l;
+          uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
+          const u32x4 x = IO::to_bf16(X[i]);
+          *(u32x4*)dst = p < NLD ? relu8(x) : x;
+        }
       }
     }
   };
@@ -168,6 +189,12 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
     const uint16_t* p0 = tile + (4 * g + (n >> 2)) * RS + 16 * blk + 4 * (n & 3);
     const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
     return u32x4{x[0], x[1], y[0], y[1]};
+  };
+  // e4m3 operand of block blk: lane l gets dim 16 blk + l % 16 of tokens
+  // 8 (l / 16) .. + 7, the 16 lanes of a group naming rows (token, 8-byte
+  // half) for the transposing read
+  auto frag8 = [&](const unsigned char* tile, int blk) -> u32x2 {
+    return lds_tr8(tile + (8 * g + (n >> 1)) * Sh::RS8 + 16 * blk + 8 * (n & 1));
   };
 
   f32x4 acc[NMB];
@@ -186,23 +213,43 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
       load_chunk(c + kGramRing, R[r]);
       lds_barrier();
       if (c < nch) {
-        const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
-        const uint16_t* vt = kt + 32 * RS;
-        u32x4 X[NB], Y[NB];
-        static_for<NB>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
-          if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
-        });
-        static_for<NMB>([&](auto ic) {
-          constexpr int i = decltype(ic)::value, b = B0 + i;
-          if constexpr (b < NBB) {
-            acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
-          } else {
-            constexpr int k = b - NBB;
-            acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
-          }
-        });
+        if constexpr (FP8) {
+          const unsigned char* kt = smem + (size_t)(r & 1) * 2 * Sh::tile_bytes;
+          const unsigned char* vt = kt + 32 * Sh::RS8;
+          u32x2 X[NB], Y[NB];
+          static_for<NB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr ((XM >> j) & 1u) X[j] = frag8(kt, j);
+            if constexpr ((YM >> j) & 1u) Y[j] = frag8(vt, j);
+          });
+          static_for<NMB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, b = B0 + i;
+            if constexpr (b < NBB) {
+              acc[i] = mfma_fp8(X[b % NB], Y[b / NB], acc[i]);
+            } else {
+              constexpr int k = b - NBB;
+              acc[i] = mfma_fp8(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+            }
+          });
+        } else {
+          const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
+          const uint16_t* vt = kt + 32 * RS;
+          u32x4 X[NB], Y[NB];
+          static_for<NB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
+            if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
+          });
+          static_for<NMB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, b = B0 + i;
+            if constexpr (b < NBB) {
+              acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
+            } else {
+              constexpr int k = b - NBB;
+              acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+            }
+          });
+        }
       }
     }
   }
@@ -330,17 +377,33 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
     lch = wrap ? 0 : lch + 1;
     lk += wrap ? 1 : 0;
   };
+  // bf16 I/O: staged as bf16 (K through ReLU), bf16 MFMAs; e4m3 I/O:
+  // staged as e4m3 codes, e4m3 MFMAs on the exact codes
   auto stage = [&](int buf, const raw (&X)[LPW]) {
-    uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
-    uint16_t* vt = kt + 32 * RS;
+    if constexpr (FP8) {
+      unsigned char* kt = smem + (size_t)buf * 2 * Sh::tile_bytes;
+      unsigned char* vt = kt + 32 * Sh::RS8;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int p = W + NW * i;
-      if (p < 2 * NLD) {
-        const int u = 64 * (p % NLD) + l;
-        uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
-        const u32x4 x = IO::to_bf16(X[i]);
-        *(u32x4*)dst = p < NLD ? relu8(x) : x;
+      for (int i = 0; i < LPW; ++i) {
+        const int p = W + NW * i;
+        if (p < 2 * NLD) {
+          const int u = 64 * (p % NLD) + l;
+          unsigned char* dst = (p < NLD ? kt : vt) + (u / UPR) * Sh::RS8 + 8 * (u % UPR);
+          *(u32x2*)dst = p < NLD ? relu_e4m3x8(X[i]) : X[i];
+        }
+      }
+    } else {
+      uint16_t* kt = (uint16_t*)(smem + (size_t)buf * 2 * Sh::tile_bytes);
+      uint16_t* vt = kt + 32 * RS;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int p = W + NW * i;
+        if (p < 2 * NLD) {
+          const int u = 64 * (p % NLD) + l;
+          uint16_t* dst = (p < NLD ? kt : vt) + (u / UPR) * RS + 8 * (u % UPR);
+          const u32x4 x = IO::to_bf16(X[i]);
+          *(u32x4*)dst = p < NLD ? relu8(x) : x;
+        }
       }
     }
   };
@@ -348,6 +411,12 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
     const uint16_t* p0 = tile + (4 * g + (n >> 2)) * RS + 16 * blk + 4 * (n & 3);
     const u32x2 x = lds_tr16(p0), y = lds_tr16(p0 + 16 * RS);
     return u32x4{x[0], x[1], y[0], y[1]};
+  };
+  // e4m3 operand of block blk: lane l gets dim 16 blk + l % 16 of tokens
+  // 8 (l / 16) .. + 7, the 16 lanes of a group naming rows (token, 8-byte
+  // half) for the transposing read
+  auto frag8 = [&](const unsigned char* tile, int blk) -> u32x2 {
+    return lds_tr8(tile + (8 * g + (n >> 1)) * Sh::RS8 + 16 * blk + 8 * (n & 1));
   };
   // copy piece p of the staged frame k to its place in HBM (out-of-range
   // lanes, pieces and frames go to an offset past the buffer: no branch)
@@ -386,23 +455,43 @@ __device__ __forceinline__ void gram_stream_wave(const GramArgs& a, unsigned cha
       // the previous frame's output, one piece per wave and chunk
       store_piece(ck - 1, cch * NW + W);
       if (q < total) {
-        const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
-        const uint16_t* vt = kt + 32 * RS;
-        u32x4 X[NB], Y[NB];
-        static_for<NB>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
-          if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
-        });
-        static_for<NMB>([&](auto ic) {
-          constexpr int i = decltype(ic)::value, b = B0 + i;
-          if constexpr (b < NBB) {
-            acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
-          } else {
-            constexpr int k = b - NBB;
-            acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
-          }
-        });
+        if constexpr (FP8) {
+          const unsigned char* kt = smem + (size_t)(r & 1) * 2 * Sh::tile_bytes;
+          const unsigned char* vt = kt + 32 * Sh::RS8;
+          u32x2 X[NB], Y[NB];
+          static_for<NB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr ((XM >> j) & 1u) X[j] = frag8(kt, j);
+            if constexpr ((YM >> j) & 1u) Y[j] = frag8(vt, j);
+          });
+          static_for<NMB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, b = B0 + i;
+            if constexpr (b < NBB) {
+              acc[i] = mfma_fp8(X[b % NB], Y[b / NB], acc[i]);
+            } else {
+              constexpr int k = b - NBB;
+              acc[i] = mfma_fp8(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+            }
+          });
+        } else {
+          const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
+          const uint16_t* vt = kt + 32 * RS;
+          u32x4 X[NB], Y[NB];
+          static_for<NB>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
+            if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
+          });
+          static_for<NMB>([&](auto ic) {
+            constexpr int i = decltype(ic)::value, b = B0 + i;
+            if constexpr (b < NBB) {
+              acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
+            } else {
+              constexpr int k = b - NBB;
+              acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+            }
+          });
+        }
         if (cch == nch - 1) {
           // frame complete: stage its blocks (B scaled by c, G by c^2, as in
           // the per-frame kernel) and start the next frame

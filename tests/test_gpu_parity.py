@@ -507,11 +507,15 @@ def test_fp8_chunked_rollout_equals_one_shot_bitwise(env):
 
 
 @pytest.mark.parametrize("S,D", [(96, 64), (880, 112)])
-def test_fp8_inputs_run_the_bf16_pipeline_bitwise(env, S, D):
-    """Every E4M3 value is exact in bf16, so E4M3 inputs and the same values as
-    bf16 must give bitwise the same final state and state norms (the decode
-    feeds the identical bf16 tiles); the outputs differ only in their last
-    rounding (e4m3 against bf16 of the same fp32 value)."""
+def test_fp8_inputs_match_the_bf16_pipeline(env, S, D):
+    """Every E4M3 value is exact in bf16 and every product of two E4M3 values
+    is exact in fp32, so E4M3 inputs and the same values as bf16 form the same
+    gram products.  The bf16 gram sums them on 16x16x16 bf16 MFMAs; the E4M3
+    gram feeds the codes to 16x16x32 fp8 MFMAs, whose 32-term sum is not
+    rounded once to fp32: on gfx950 it lands within about 2^-12 of the sum of
+    the |products| of the exact value (subnormal codes included).  So the
+    final states differ by about 2e-4 relative, far below the output's own
+    E4M3 rounding (2^-4), and a wrong operand layout (O(1) errors) fails."""
     torch, gdn, wl, go = env
     inp = gen(env, wl.Workload("fp8eq", 1, 3, 6, S, D, dtype="fp8", gamma=(0.8, 1.0), beta=(0.2, 1.0)))
     as_bf16 = {n: (inp[n].to(torch.bfloat16) if n in ("q", "k", "v") else inp[n]) for n in inp}
@@ -522,10 +526,16 @@ def test_fp8_inputs_run_the_bf16_pipeline_bitwise(env, S, D):
         ob, sb, nb = gdn.frame_forward(as_bf16["q"], as_bf16["k"], as_bf16["v"], as_bf16["gamma"],
                                        as_bf16["beta"], state=m0, beta_mode=mode, want_norms=True)
         torch.cuda.synchronize()
-        assert torch.equal(s8, sb) and torch.equal(n8, nb)
-        # both outputs are one rounding of the same fp32 values
+        es = float((s8.double() - sb.double()).norm() / sb.double().norm())
+        en = float(((n8.double() - nb.double()).abs() / nb.double().abs()).max())
+        assert es < 1e-3 and en < 1e-3, (mode, es, en)
+        # both outputs are one rounding of nearly the same fp32 values: one
+        # e4m3 step apart (2^-3 relative for normals), plus an absolute term
+        # for values near zero, where the readout's cancellation turns the
+        # states' 2e-4 relative difference into a few 2^-9 subnormal steps
         d = (o8.float() - ob.float()).abs()
-        assert bool((d <= ob.float().abs() * 2.0 ** -4 + 2.0 ** -10).all())
+        slack = d - ob.float().abs() * 2.0 ** -3
+        assert float(slack.max()) <= 2.0 ** -7, (mode, float(slack.max()), float(ob.float().abs().max()))
 
 
 def test_fp8_initial_state_norms_and_peek(env):
