@@ -538,8 +538,10 @@ __device__ __forceinline__ bool readout_item(const FusedArgs& a, unsigned char* 
 // (I, j).  Value tiles evolve independently, so the chain workgroups of a
 // head only share their inputs.
 // ---------------------------------------------------------------------------
-template <int D, bool ERASE, int J, bool REMOTE>
-__device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* smem, int h, int c) {
+// J is a run-time value on purpose: the four waves then run one copy of the
+// frame loop, which stays in the instruction cache.
+template <int D, bool ERASE, bool REMOTE>
+__device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* smem, int h, int c, const int J) {
   using Sh = FShape<D>;
   constexpr int NB = Sh::NB, NKC = Sh::NKC, NGL = Sh::NGL;
   constexpr int LPG = (NGL + kFW - 1) / kFW;         // G pieces loaded per wave
@@ -570,7 +572,9 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
   // index is a constant): Gr[f & 1] holds this wave's G pieces of frame f from
   // their load (during frame f - 3) to their staging (during frame f - 2);
   // Bn[f & 1], ga[f & 1], be[f & 1] frame f's B blocks, gamma and beta from
-  // their load (during frame f - 1) to their use.
+  // their load (during frame f - 2, after frame f - 2's update has read the
+  // buffer) to their use: two frames of memory latency, which a saturated
+  // HBM needs.
   u32x4 Gr[2][LPG];
   u32x2 Bn[2][NB];
   float ga[2] = {0.f, 0.f}, be[2] = {0.f, 0.f};
@@ -623,7 +627,7 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
 
   // Frame f, per wave: the MFMAs and the update (G from LDS slot f mod 3, B
   // and the gates from registers); the check that frame f - RM's readout has
-  // copied its state slot; the polls for frame f + 1; frame f + 1's B and
+  // copied its state slot; the polls for frame f + 1; frame f + 2's B and
   // gates into registers; the bf16 M_f into the state ring; the check that
   // gram slot f + 3 is filled and its G into registers; frame f + 2's G
   // (loaded during frame f - 1) into LDS slot (f + 2) mod 3; then the one
@@ -669,9 +673,10 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
       __builtin_amdgcn_raw_buffer_store_b64(pub, mring_rs, off, 0, REMOTE ? kCoherent : 0);
     }
   };
+  load_b(0, Int<0>{});
   pr[0] = poll(rdone_of(0));
   pg[0] = poll(gready_of(3));
-  load_b(0, Int<0>{});
+  load_b(1, Int<1>{});
   store_m(-1);
   load_g(2, Int<0>{});
   __syncthreads();
@@ -715,7 +720,7 @@ __device__ __forceinline__ void chain_wave(const FusedArgs& a, unsigned char* sm
     }
     pr[r ^ 1] = poll(rdone_of(f + 1));
     pg[r ^ 1] = poll(gready_of(f + 4));
-    load_b(f + 1, Int<r ^ 1>{});
+    load_b(f + 2, Int<r>{});
     store_m(f);
     if (f + 3 < T) check(pg[r], gready_of(f + 3), (uint32_t)(f + 4));
     load_g(f + 3, Int<r ^ 1>{});
@@ -802,13 +807,8 @@ __global__ __launch_bounds__(kFusedWaves * 64, 2) void gdn_fused_kernel(FusedArg
   if (rank < nh * CW) {
     const int hi = rank / CW, h = x + NX * hi, c = rank % CW;
     const bool remote = moved && hi == nh - 1;
-    static_for<kFW>([&](auto wc) {
-      constexpr int W = decltype(wc)::value;
-      if (w == W) {
-        if (remote) chain_wave<D, ERASE, W, true>(a, smem, h, c);
-        else chain_wave<D, ERASE, W, false>(a, smem, h, c);
-      }
-    });
+    if (remote) chain_wave<D, ERASE, true>(a, smem, h, c, w);
+    else chain_wave<D, ERASE, false>(a, smem, h, c, w);
     return;
   }
   const int ns = nwg - nh * CW, k = rank - nh * CW;                    // stream workgroups of this XCD
