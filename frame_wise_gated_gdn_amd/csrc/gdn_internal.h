@@ -72,6 +72,7 @@ struct ReadoutArgs {
   int BH, T, S, t0, Tc;
   int Fs, f0;               // snapshots (and norm partials) hold [BH][Fs] frames from f0
   int fp8;                  // 1: Q and O are OCP e4m3 bytes (bf16 snapshots only)
+  int nsplit;               // workgroups per frame, each a share of its chunks (set by the launcher)
 };
 
 // C_t = ReLU(Q_t)^T dO_t and dQ_t of the backward in one pass over Q_t and dO_t.

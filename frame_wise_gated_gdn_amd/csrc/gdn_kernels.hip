@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -571,8 +573,11 @@ struct ReadShape {
 };
 
 // RW waves per workgroup split the frame's chunks: kReadWaves, or twice that
-// for launches with fewer frames than CUs.  Every output element is computed
-// the same way whatever RW is.
+// for launches with fewer frames than CUs, which also give each frame
+// a.nsplit workgroups (a short streaming chunk: a few frames per head, too
+// few workgroups to keep the chip's loads in flight).  The chunks go round
+// the frame's RW * nsplit waves.  Every output element is computed the same
+// way whatever RW and nsplit are.
 template <int D, bool FP8, int RW>
 __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_kernel(ReadoutArgs a) {
   using Sh = ReadShape<D>;
@@ -581,10 +586,12 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
   constexpr int NB = Sh::NB, NKC = Sh::NKC, UPR = Sh::UPR, NLD = Sh::NLD, RS = Sh::RS;
   constexpr int RS8 = D + 8;                       // row stride (bytes) of the e4m3 O tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int frame = blockIdx.x;                    // over BH * Tc
+  const int nsp = a.nsplit;
+  const int frame = blockIdx.x / nsp, sp = blockIdx.x % nsp;   // over BH * Tc, then the frame's shares
   const int bh = frame / a.Tc, tl = frame % a.Tc, t = a.t0 + tl;
   const int tid = threadIdx.x, l = lane_id(), g = l >> 4, n = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int RWT = RW * nsp, wt = RW * sp + w;      // the frame's waves; this wave's place among them
   uint16_t* const qs = (uint16_t*)(smem + (size_t)w * 2 * Sh::tile_bytes);
   uint16_t* const os = qs + 32 * RS;
   const int S = a.S, T = a.T;
@@ -594,10 +601,10 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
   const __amdgpu_buffer_rsrc_t ors = make_rsrc((unsigned char*)a.o + head0, head_bytes);
   const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * IO::ebytes;   // frame's first byte in the head
   const int nchunk = (S + 31) / 32;
-  const int NC = (nchunk + RW - 1) / RW;                     // chunk slots per wave
+  const int NC = (nchunk + RWT - 1) / RWT;                   // chunk slots per wave
   const size_t sf = (size_t)bh * a.Fs + a.f0 + tl;           // staging frame of (head, frame)
 
-  if (a.norms && a.norm_part && tid == 0) {
+  if (a.norms && a.norm_part && sp == 0 && tid == 0) {
     float sq = 0.f;
     for (int j = 0; j < NB; ++j) sq += a.norm_part[sf * NB + j];
     a.norms[(size_t)bh * T + t] = sqrtf(sq);
@@ -609,7 +616,7 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
     return (ch < nchunk && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * IO::unit_bytes : kOOB;
   };
   auto load_chunk = [&](int i, raw (&X)[NLD]) {
-    const int ch = w + RW * i;
+    const int ch = wt + RWT * i;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) X[j] = IO::load_nt(qrs, i < NC ? unit_off(ch, 64 * j + l) : kOOB);
   };
@@ -635,7 +642,7 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
   // The snapshot loads were issued first: one use of the last of them makes
   // the compiler wait for all of them here, once, instead of inside the loop.
   asm volatile("" ::"v"(A[NB - 1][NKC - 1]));
-  if (a.norms && !a.norm_part && w == 0) {
+  if (a.norms && !a.norm_part && sp == 0 && w == 0) {
     // state norm from the bf16 snapshot: each element of M_t sits in exactly
     // one lane of one fragment of every wave
     float sq = 0.f;
@@ -654,7 +661,7 @@ __global__ __launch_bounds__(RW * 64, RW > kReadWaves ? 1 : 2) void gdn_readout_
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       const int i = base + r;
-      const int ch = w + RW * i;
+      const int ch = wt + RWT * i;
       // the loop is unrolled by RING: slots past NC only keep the loads going
       const bool live = i < NC;
       // stage ReLU(Q) of the chunk (row-major, padded rows)
@@ -770,23 +777,32 @@ static hipError_t launch_readout_t(const ReadoutArgs& ro, hipStream_t stream) {
   }, &li);
   if (ie != hipSuccess) return ie;
   const int cus = li.cus;
-  const unsigned grid = (unsigned)(ro.BH * ro.Tc);
+  const unsigned frames = (unsigned)(ro.BH * ro.Tc);
+  ReadoutArgs ra = ro;
+  ra.nsplit = 1;
   if constexpr (BF16) {
     // bf16 snapshots: bf16 or e4m3 Q and O; a launch with fewer frames than
-    // CUs (a short streaming chunk) takes twice the waves per frame
-    const bool wide = (int)grid < cus;
+    // CUs (a short streaming chunk) takes twice the waves per frame and
+    // splits each frame's chunks over up to 2 cus / frames workgroups, at
+    // least a chunk per wave
+    const bool wide = (int)frames < cus;
+    if (wide) {
+      const int nchunk = (ro.S + 31) / 32, rw = 2 * RW;
+      ra.nsplit = std::max(1, std::min((2 * cus + (int)frames - 1) / (int)frames, (nchunk + rw - 1) / rw));
+    }
+    const unsigned grid = frames * (unsigned)ra.nsplit;
     const size_t lds = ReadShape<D>::lds_bytes(wide ? 2 * RW : RW);
     const dim3 block(wide ? 2 * RW * 64 : RW * 64);
-    if (ro.fp8) {
-      if (wide) hipLaunchKernelGGL((gdn_readout_kernel<D, true, 2 * RW>), dim3(grid), block, lds, stream, ro);
-      else hipLaunchKernelGGL((gdn_readout_kernel<D, true, RW>), dim3(grid), block, lds, stream, ro);
+    if (ra.fp8) {
+      if (wide) hipLaunchKernelGGL((gdn_readout_kernel<D, true, 2 * RW>), dim3(grid), block, lds, stream, ra);
+      else hipLaunchKernelGGL((gdn_readout_kernel<D, true, RW>), dim3(grid), block, lds, stream, ra);
     } else {
-      if (wide) hipLaunchKernelGGL((gdn_readout_kernel<D, false, 2 * RW>), dim3(grid), block, lds, stream, ro);
-      else hipLaunchKernelGGL((gdn_readout_kernel<D, false, RW>), dim3(grid), block, lds, stream, ro);
+      if (wide) hipLaunchKernelGGL((gdn_readout_kernel<D, false, 2 * RW>), dim3(grid), block, lds, stream, ra);
+      else hipLaunchKernelGGL((gdn_readout_kernel<D, false, RW>), dim3(grid), block, lds, stream, ra);
     }
   } else {
-    hipLaunchKernelGGL((gdn_readout_f32_kernel<D>), dim3(grid), dim3(kReadWaves * 64),
-                       (size_t)D * (D + 1) * 4, stream, ro);
+    hipLaunchKernelGGL((gdn_readout_f32_kernel<D>), dim3(frames), dim3(kReadWaves * 64),
+                       (size_t)D * (D + 1) * 4, stream, ra);
   }
   return hipGetLastError();
 }

@@ -310,6 +310,30 @@ def test_streaming_long_chunks_bitwise(env):
     check(env, inp, o1, st1, run_oracle(env, inp, state=s0, want_norms=True), TOL["bf16"], norms=n1)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("S,D", [(300, 64), (880, 112), (40, 16)])
+def test_small_launch_readout_split_is_bitwise(env, dtype, S, D):
+    """A launch with fewer frames than CUs splits each frame's token chunks
+    over several readout workgroups (a 4-frame chunk of a few heads).  Heads
+    0..3 of a 64-head call, run on their own (16 frames: split), give bitwise
+    the outputs, states and norms of the same heads in the whole call (256
+    frames: one workgroup per frame), ragged chunk counts included."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.Workload("split", 1, 64, 4, S, D, dtype=dtype, gamma=(0.8, 1.0), beta=(0.2, 1.0)))
+    full = gdn.frame_forward(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], want_norms=True,
+                             path="three_pass")
+    part = gdn.frame_forward(*(inp[n][:, :4].contiguous() for n in ("q", "k", "v", "gamma", "beta")),
+                             want_norms=True, path="three_pass")
+    torch.cuda.synchronize()
+    raw = (lambda x: x.view(torch.uint8)) if dtype == "fp8" else (lambda x: x)
+    assert torch.equal(raw(part[0]), raw(full[0][:, :4].contiguous()))
+    assert torch.equal(part[1], full[1][:, :4]) and torch.equal(part[2], full[2][:, :4])
+    if dtype == "bf16":
+        sub = {n: inp[n][:, :4] for n in inp}
+        check(env, sub, part[0], part[1], run_oracle(env, sub, heads=[(0, 0), (0, 3)], want_norms=True),
+              TOL["bf16"], norms=part[2])
+
+
 @pytest.mark.parametrize("B,H,T,S,D", [(1, 3, 7, 400, 112), (2, 2, 5, 352, 96), (1, 5, 33, 290, 64),
                                         (1, 2, 9, 1000, 48)])
 def test_streaming_gram_kernel_shapes(env, B, H, T, S, D):
