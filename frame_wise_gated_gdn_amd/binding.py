@@ -170,8 +170,13 @@ def _nbytes(t) -> int:
 def _check(device, name, t, shape=None, dtype=None):
     """An optional tensor argument (None passes) must be contiguous, on
     `device`, and of the given shape and dtype: the library takes raw device
-    addresses and cannot tell a host tensor or a short buffer from a good one."""
+    addresses and cannot tell a host tensor or a short buffer from a good one.
+    The passing case costs a few attribute reads (a streaming chunk makes one
+    call per few frames); the message is built only on failure."""
     if t is None:
+        return
+    if (t.get_device() == (device.index if device.index is not None else -1) and t.is_contiguous()
+            and (shape is None or t.shape == shape) and (dtype is None or t.dtype == dtype)):
         return
     if t.device != device:
         raise ValueError(f"{name} must be on {device}, not {t.device}")
@@ -181,6 +186,7 @@ def _check(device, name, t, shape=None, dtype=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    raise ValueError(f"{name}: unsupported tensor")
 
 
 def _check_gdn_inputs(entry, q, k, v, gamma, beta, state, extra=()):
@@ -193,11 +199,12 @@ def _check_gdn_inputs(entry, q, k, v, gamma, beta, state, extra=()):
     if not q.is_cuda:
         raise ValueError(f"{entry}: q must be a device tensor")
     B, H, T, S, D = q.shape
+    dev, shp, dt = q.device, q.shape, q.dtype
     for name, t in (("q", q), ("k", k), ("v", v)) + tuple(extra):
-        _check(q.device, name, t, q.shape, q.dtype)
-    _check(q.device, "gamma", gamma, (B, H, T), torch.float32)
-    _check(q.device, "beta", beta, (B, H, T), torch.float32)
-    _check(q.device, "state", state, (B, H, D, D), torch.float32)
+        _check(dev, name, t, shp, dt)
+    _check(dev, "gamma", gamma, (B, H, T), torch.float32)
+    _check(dev, "beta", beta, (B, H, T), torch.float32)
+    _check(dev, "state", state, (B, H, D, D), torch.float32)
 
 
 def _stream_and_alloc(stream, device):
@@ -212,9 +219,19 @@ def _stream_and_alloc(stream, device):
     import contextlib
     import torch
     if stream is None:
-        return torch.cuda.current_stream(device).cuda_stream, contextlib.nullcontext()
+        return _current_stream(device), contextlib.nullcontext()
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     return handle, torch.cuda.stream(torch.cuda.ExternalStream(handle, device=device))
+
+
+def _current_stream(device) -> int:
+    """Handle of torch's current stream on `device` (the raw query when this
+    torch has it: building a Stream object costs microseconds per call)."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _flags(path: str, time_kernels: bool) -> int:

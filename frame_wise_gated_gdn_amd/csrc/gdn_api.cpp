@@ -260,6 +260,57 @@ hipError_t side_stream(SideStream** out) {
 // pass is latency-bound and light on resources, so the state of sub-range
 // i+1 runs on the CUs next to the HBM-bound readout of sub-range i.  The state
 // crosses sub-ranges and ranges in fp32, so any split gives the same bits.
+// Compute units of the current device (0 when the query fails).
+int device_cus() {
+  static gdn::DeviceOnce once;
+  gdn::LaunchInfo li;
+  const hipError_t e = once.get([](int dev, gdn::LaunchInfo& info) {
+    return hipDeviceGetAttribute(&info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  }, &li);
+  return e == hipSuccess ? li.cus : 0;
+}
+
+// Short chunk (at most kTailMaxFrames frames, D <= 112, fewer frames than
+// CUs, no norms asked for): the gram pass, then the chain and the readout in one
+// launch (gdn_step_tail_kernel), two launches instead of three with the same
+// bits.  When state_in and state_out overlap, the gram pass first copies
+// state_in to the workspace carrier, which the chain then reads.
+bool tail_ok(const gdn_desc* d, const Plan& p, const Ptrs& x, size_t F, int cus) {
+  return !(d->flags & GDN_FLAG_THREE_PASS) && !x.norms && F >= (size_t)d->T && d->T <= gdn::kTailMaxFrames &&
+         d->D <= 112 && cus > 0 && (long long)p.bh * d->T <= cus;
+}
+
+gdn_status run_tail(const gdn_desc* d, const Plan& p, const Ptrs& x, float* carrier, void* gfr, void* bfr,
+                    int cus, hipStream_t s) {
+  const double c = 1.0 / std::sqrt((double)d->D * (double)d->S);
+  const bool timed = (d->flags & GDN_FLAG_TIME_KERNELS) != 0;
+  const size_t sb = p.state_bytes;
+  const bool alias = overlap(x.state_in, sb, x.state_out, sb);
+  gdn::GramArgs ga;
+  ga.k = x.k; ga.v = x.v; ga.gfr = gfr; ga.bfr = bfr;
+  ga.BH = (int)p.bh; ga.T = d->T; ga.S = d->S; ga.t0 = 0; ga.Tc = d->T;
+  ga.kscale = (float)c; ga.kscale2 = (float)(c * c);
+  ga.fp8 = d->io_dtype == GDN_FP8_E4M3;
+  if (alias) { ga.copy_src = x.state_in; ga.copy_dst = carrier; }
+  hipError_t e = launch_timed(timed, GDN_KERNEL_GRAM, s, [&] { return gdn::launch_gram(d->D, ga, s); });
+  if (e == hipSuccess) {
+    gdn::TailArgs ta;
+    ta.q = x.q; ta.o = x.o; ta.gfr = gfr; ta.bfr = bfr; ta.gamma = x.gamma; ta.beta = x.beta;
+    ta.state_src = alias ? carrier : x.state_in;
+    ta.state_dst = x.state_out;
+    ta.BH = (int)p.bh; ta.T = d->T; ta.S = d->S; ta.t0 = 0; ta.Tc = d->T;
+    // shares of a frame's chunks: about two workgroups per CU, at least two
+    // chunks per wave (each share repeats the chain)
+    const long long frames = (long long)p.bh * d->T;
+    const int nchunk = (d->S + 31) / 32;
+    ta.nsplit = (int)std::max<long long>(1, std::min<long long>(2 * cus / frames, nchunk / (2 * (long long)p.nb)));
+    ta.beta_mode = d->beta_mode; ta.fp8 = d->io_dtype == GDN_FP8_E4M3;
+    e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_step_tail(d->D, ta, cus, s); });
+  }
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "kernel launch (short chunk): %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
 gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* workspace, size_t wb,
                     hipStream_t s, bool side_ok = true) {
   const size_t F = frames_per_launch(p, d->T, wb);
@@ -271,6 +322,8 @@ gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* works
   carve(0);
   void* gfr = carve(F * p.gfr_frame);
   void* bfr = carve(F * p.bfr_frame);
+  const int cus = device_cus();
+  if (tail_ok(d, p, x, F, cus)) return run_tail(d, p, x, carrier, gfr, bfr, cus, s);
 
   // The state travels between launches through state_out when the caller gave
   // one (in-place per workgroup tile), else through the workspace carrier.

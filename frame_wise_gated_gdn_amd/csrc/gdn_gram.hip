@@ -280,6 +280,28 @@ __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gr
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int fh = blockIdx.x;   // over BH * Tc
   const int bh = fh / a.Tc, tl = fh % a.Tc;
+  // Workgroups past the last frame copy one head's state each (only the
+  // short launches, with more waves than the default shape, are given a
+  // copy): they run on CUs that the frames leave idle.
+  constexpr bool kCanCopy = NW > GramShape<D>::NW;
+  if (kCanCopy && fh >= a.BH * a.Tc) {
+    constexpr int TH = NW * 64, PER = (D * D + TH - 1) / TH;
+    const int h = fh - a.BH * a.Tc;
+    const float* src = a.copy_src + (size_t)h * D * D;
+    float* dst = a.copy_dst + (size_t)h * D * D;
+    float x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = (int)threadIdx.x + i * TH;
+      x[i] = u < D * D ? src[u] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = (int)threadIdx.x + i * TH;
+      if (u < D * D) dst[u] = x[i];
+    }
+    return;
+  }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   static_for<NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
@@ -704,6 +726,280 @@ __global__ __launch_bounds__(D / 16 * 64, 1) void gdn_state_bf16_kernel(StateArg
 
 
 // ----------------------------------------------------------------------------
+// Chunk tail: the state chain and the readout of a short launch (a streaming
+// chunk of at most kTailMaxFrames frames per head) in one kernel.  There the
+// serial state pass and a readout launch behind it cost far more than the
+// chain itself.  One workgroup per (head, frame t, share of the frame's
+// token chunks), NB waves.  Wave I owns key-block row I of the state for
+// every value tile j and first runs the chain over the launch's frames
+// 0..t: per element the same instructions as gdn_state_bf16_kernel (the
+// product over the G row and the bf16 state column of tile j, then the
+// gate, input and erase), hence the same bits.  That leaves bf16(M_t) in
+// LDS exactly as the readout's A operands.  Then the waves read out
+// O_t = ReLU(Q_t) M_t for their chunks with the readout kernel's MFMA order
+// (the same bits as gdn_readout_kernel), each lane storing its 4
+// consecutive output columns of every value tile.  A workgroup recomputes
+// the frames before its own instead of waiting for another workgroup, so no
+// workgroup ever waits on another, and Q is read once.  All frames' G and B
+// are loaded first, then the first Q chunks, which stay in flight during
+// the chain.  The workgroup of the last frame (share 0) writes the fp32
+// state; state_src is read by every workgroup and so must not alias
+// state_dst (the caller passes a copy).
+// ----------------------------------------------------------------------------
+template <int D>
+struct TailShape {
+  using St = StateShape<D>;
+  static constexpr int NB = D / 16, NKC = St::NKC;
+  static constexpr int UPR = D / 8, NLD = D / 16, RS = D + 8;
+  static constexpr int QRING = D >= 80 ? 2 : 3;       // Q chunks in flight per wave
+  static constexpr int FRING = kTailMaxFrames;        // frames of G, B, gamma, beta (all of them)
+  // exchange buffer: per value tile j the state kernel's slots (kb, lane)
+  static constexpr size_t xtile = (size_t)NKC * 64 * 16;
+  static constexpr size_t xbuf = NB * xtile;
+  static constexpr size_t xch_off = 2 * St::g_slot;
+  static constexpr size_t qtile_off = xch_off + 2 * xbuf;
+  static constexpr size_t qtile_bytes = (size_t)32 * RS * 2;
+  static constexpr size_t lds_bytes = qtile_off + (size_t)NB * qtile_bytes;
+};
+constexpr bool tail_fits(int D) { return D <= 112; }   // LDS (D = 128 would need 170 KB)
+
+template <int D, bool FP8, bool ERASE, int I>
+__device__ __forceinline__ void tail_wave(const TailArgs& a, unsigned char* smem, int bh, int tl, int sp) {
+  using Sh = StateShape<D>;
+  using Tl = TailShape<D>;
+  using IO = IoFmt<FP8>;
+  using raw = typename IO::raw;
+  constexpr int NB = Sh::NB, NKC = Sh::NKC, NGL = Sh::NGL, LPG = Sh::LPG;
+  constexpr int UPR = Tl::UPR, NLD = Tl::NLD, RS = Tl::RS, FR = Tl::FRING;
+  // e4m3 at D >= 96 keeps one chunk in flight (the conversions' registers)
+  constexpr int QR = FP8 && D >= 96 ? 1 : Tl::QRING;
+  const int l = lane_id(), g = l >> 4, n = l & 15;
+  unsigned char* gsl = smem;                                  // 2 G slots
+  unsigned char* xch = smem + Tl::xch_off;                    // 2 exchange buffers
+  uint16_t* qs = (uint16_t*)(smem + Tl::qtile_off + (size_t)I * Tl::qtile_bytes);
+  const int S = a.S, T = a.T, t = a.t0 + tl;
+
+  // ---- Q chunks of this wave: chunk wt + RWT i of the frame ----
+  const uint32_t head_bytes = (uint32_t)T * (uint32_t)S * D * IO::ebytes;
+  const size_t head0 = (size_t)bh * T * S * D * IO::ebytes;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const unsigned char*)a.q + head0, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc((unsigned char*)a.o + head0, head_bytes);
+  const uint32_t fbyte = (uint32_t)t * (uint32_t)S * D * IO::ebytes;
+  const int nchunk = (S + 31) / 32;
+  const int RWT = NB * a.nsplit, wt = NB * sp + I;
+  const int NC = (nchunk + RWT - 1) / RWT;
+  auto unit_off = [&](int ch, int u) -> uint32_t {
+    const int tok = ch * 32 + u / UPR;
+    return (ch < nchunk && tok < S) ? fbyte + (uint32_t)(ch * 32 * UPR + u) * IO::unit_bytes : kOOB;
+  };
+  auto load_chunk = [&](int i, raw (&X)[NLD]) {
+    const int ch = wt + RWT * i;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) X[u] = IO::load_nt(qrs, i < NC ? unit_off(ch, 64 * u + l) : kOOB);
+  };
+  raw X[QR][NLD];
+
+  // ---- the chain over frames 0..tl: block (I, j) of every tile j ----
+  if ((NB & 1) && I == 0) {
+    // block NB of an odd block count is a zero pad of the last k-step
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      *(u32x2*)(xch + j * Tl::xtile + ((size_t)(NKC - 1) * 64 + l) * 16 + 8) = u32x2{0u, 0u};
+      *(u32x2*)(xch + Tl::xbuf + j * Tl::xtile + ((size_t)(NKC - 1) * 64 + l) * 16 + 8) = u32x2{0u, 0u};
+    }
+  }
+  const int row0 = 16 * I + 4 * g;
+  f32x4 m[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) m[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.state_src) {
+    const float* src = a.state_src + (size_t)bh * D * D;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[j][r] = src[(size_t)(row0 + r) * D + 16 * j + n];
+  }
+  auto publish = [&](int buf, int j, f32x4 x) {
+    const u32x2 v = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    *(u32x2*)(xch + (size_t)buf * Tl::xbuf + j * Tl::xtile + ((size_t)(I >> 1) * 64 + l) * 16 + 8 * (I & 1)) = v;
+  };
+#pragma unroll
+  for (int j = 0; j < NB; ++j) publish(0, j, m[j]);
+
+  const int Tc = a.Tc;
+  const size_t gfb = GramShape<D>::g_frame_bytes, bfb = GramShape<D>::b_frame_bytes;
+  const size_t fb = (size_t)bh * Tc;
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc((const unsigned char*)a.gfr + fb * gfb, (uint32_t)(Tc * gfb));
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc((const unsigned char*)a.bfr + fb * bfb, (uint32_t)(Tc * bfb));
+  const __amdgpu_buffer_rsrc_t gars = make_rsrc(a.gamma + (size_t)bh * T + a.t0, (uint32_t)(Tc * 4));
+  const __amdgpu_buffer_rsrc_t bers = make_rsrc(a.beta + (size_t)bh * T + a.t0, (uint32_t)(Tc * 4));
+
+  u32x4 Gr[FR][LPG];
+  u32x2 Bf[FR][NB];                        // B blocks (j, I), lane-linear as the state pass reads them
+  float Ga[FR], Be[FR];
+  auto load_frame = [&](int f) {
+    const bool ok = f <= tl;
+    Ga[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gars, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
+    Be[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bers, ok ? (uint32_t)f * 4u : kOOB, 0, 0));
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int q = I + NB * i;
+      Gr[f][i] = buf_load16(grs, (ok && q < NGL) ? (uint32_t)f * (uint32_t)gfb + q * 1024 + l * 16 : kOOB);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      Bf[f][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               brs, ok ? (uint32_t)((j * NB + I) * 512 + l * 8) + (uint32_t)f * (uint32_t)bfb
+                                                       : kOOB, 0, 0));
+  };
+  auto stage_g = [&](int slot, int f) {
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int q = I + NB * i;
+      if (q < NGL) *(u32x4*)(gsl + (size_t)slot * Sh::g_slot + q * 1024 + l * 16) = Gr[f][i];
+    }
+  };
+  auto g_half = [&](const unsigned char* gs, auto Lc) -> u32x2 {
+    constexpr int L = decltype(Lc)::value;
+    if constexpr (L >= NB) {
+      return u32x2{0u, 0u};
+    } else if constexpr (L <= I) {
+      return *(const u32x2*)(gs + (size_t)(I * (I + 1) / 2 + L) * 512 + l * 8);
+    } else {
+      const unsigned char* blk = gs + (size_t)(L * (L + 1) / 2 + I) * 512;
+      return lds_tr16((const uint16_t*)(blk + ((n & 3) * 16 + 4 * g + (n >> 2)) * 8));
+    }
+  };
+
+  // Every frame's G, B, gamma and beta, then the first Q chunks: the chain
+  // below issues no load, so each of its waits is for exactly the frame
+  // loads it needs (loads complete in issue order).
+#pragma unroll
+  for (int f = 0; f < FR; ++f) load_frame(f);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < QR; ++r) load_chunk(r, X[r]);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_g(0, 0);
+  lds_barrier();
+  // All FR frames, unrolled; those past tl are computed on zeros and not
+  // committed, so no branch splits the waits.
+#pragma unroll
+  for (int f = 0; f < FR; ++f) {
+    __builtin_amdgcn_sched_barrier(0);       // no work of a later frame moves up (its waits would follow)
+    const bool ok = f <= tl;
+    const unsigned char* xr = xch + (size_t)(f & 1) * Tl::xbuf;
+    const unsigned char* gs = gsl + (size_t)(f & 1) * Sh::g_slot;
+    u32x4 aop[NKC];
+    static_for<NKC>([&](auto kbc) {
+      constexpr int kb = decltype(kbc)::value;
+      const u32x2 lo = g_half(gs, Int<2 * kb>{}), hi = g_half(gs, Int<2 * kb + 1>{});
+      aop[kb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    });
+    const float gm = Ga[f], bt = Be[f], bg = bt * gm;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      u32x4 bop[NKC];
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) bop[kb] = *(const u32x4*)(xr + j * Tl::xtile + ((size_t)kb * 64 + l) * 16);
+      f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKC; ++kb) p = mfma_bf16(aop[kb], bop[kb], p);
+      const u32x2 bw = Bf[f][j];
+      const f32x4 bin = {bf16_lo_f32(bw[0]), bf16_hi_f32(bw[0]), bf16_lo_f32(bw[1]), bf16_hi_f32(bw[1])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float nv = state_update(gm, m[j][e], bg, p[e], ERASE ? bin[e] : bt * bin[e]);
+        m[j][e] = ok ? nv : m[j][e];
+      }
+    }
+    if (f + 1 < FR) stage_g((f + 1) & 1, f + 1);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) publish((f & 1) ^ 1, j, m[j]);
+    lds_barrier();
+  }
+  if (tl == Tc - 1 && sp == 0 && a.state_dst) {
+    float* dst = a.state_dst + (size_t)bh * D * D;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(row0 + r) * D + 16 * j + n] = m[j][r];
+  }
+
+  // ---- readout: A operand (jb, kc) = exchange slot (jb, kc) of bf16(M_t) ----
+  const unsigned char* xf = xch + (size_t)(FR & 1) * Tl::xbuf;   // published after frame FR - 1
+  u32x4 A[NB][NKC];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) A[jb][kc] = *(const u32x4*)(xf + jb * Tl::xtile + ((size_t)kc * 64 + l) * 16);
+  for (int base = 0; base < NC; base += QR) {
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+      const int i = base + r;
+      const int ch = wt + RWT * i;
+      // Nothing of a later slot moves up: the compiler would hoist the ReLU
+      // of the next chunks and with it the waits for their loads.
+      __builtin_amdgcn_sched_barrier(0);
+      // branch-free like the chain: a slot past the wave's last chunk reads
+      // zeros and its stores are dropped (chunk index past the frame)
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const int uu = 64 * u + l;
+        *(u32x4*)(qs + (uu / UPR) * RS + 8 * (uu % UPR)) = relu8(IO::to_bf16(X[r][u]));
+      }
+      load_chunk(i + QR, X[r]);
+      wave_lds_sync();
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 B[NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+          const uint16_t* rp = qs + (16 * half + n) * RS + 32 * kc + 4 * g;
+          const u32x2 lo = *(const u32x2*)rp;
+          const u32x2 hi = (32 * kc + 32 <= D) ? *(const u32x2*)(rp + 16) : u32x2{0u, 0u};
+          B[kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        const int tok = ch * 32 + 16 * half + n;
+        const bool in = ch < nchunk && tok < S;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) acc = mfma_bf16(A[jb][kc], B[kc], acc);
+          const uint32_t off = in ? fbyte + ((uint32_t)tok * D + 16 * jb + 4 * g) * IO::ebytes : kOOB;
+          if constexpr (FP8) {
+            __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_fp8x4(acc), ors, off, 0, 0);
+          } else {
+            const u32x2 pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(pk, ors, off, 0, 0);
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+template <int D, bool FP8, bool ERASE>
+__global__ __launch_bounds__(D / 16 * 64) void gdn_step_tail_kernel(TailArgs a) {
+  constexpr int NB = D / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if constexpr (tail_fits(D)) {
+    const int nsp = a.nsplit;
+    const int unit = xcd_unit(a.BH * a.Tc * nsp);
+    if (unit < 0) return;                     // whole workgroup: no work on this slot
+    const int sp = unit % nsp, fr = unit / nsp;
+    const int bh = fr / a.Tc, tl = fr % a.Tc;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    static_for<NB>([&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      if (w == I) tail_wave<D, FP8, ERASE, I>(a, smem, bh, tl, sp);
+    });
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Backward: C_t = ReLU(Q_t)^T dO_t and dQ_t = (dO_t M_t^T) * [Q_t > 0] in one
 // pass over Q_t and dO_t.  One workgroup per (head, frame) with the gram
 // pass's waves and chunk pipeline (Q in the key's place, dO in the value's):
@@ -1108,10 +1404,13 @@ static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
   const int cus = li.cus, slots = li.slots;
   const long long nfh = (long long)ga.BH * ga.Tc;
   const int nch = (ga.S + 31) / 32;
+  if (ga.copy_src && nfh > 2 * cus) return hipErrorInvalidValue;   // only the short-launch kernels copy
+  const unsigned grid = (unsigned)(nfh + (ga.copy_src ? ga.BH : 0));   // + one copy workgroup per head
   if (nfh <= 2 * cus) {
     // at most two frames per CU (a short streaming chunk): one workgroup per
-    // frame with twice the waves, so that the launch takes half as long
-    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, 2 * NW>), dim3((unsigned)nfh), dim3(2 * NW * 64),
+    // frame with twice the waves, so that the launch takes half as long (four
+    // times the waves measured slower again)
+    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, 2 * NW>), dim3(grid), dim3(2 * NW * 64),
                        GramShape<D>::lds_bytes, stream, ga);
   } else if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {
     // persistent: one workgroup per resident slot
@@ -1151,6 +1450,38 @@ static hipError_t launch_state_t(const StateArgs& sa, hipStream_t stream) {
   else
     hipLaunchKernelGGL((gdn_state_bf16_kernel<D, false>), dim3(grid), dim3(D / 16 * 64), StateShape<D>::lds_bytes,
                        stream, sa);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_step_tail_t(const TailArgs& ta, int cus, hipStream_t stream) {
+  static DeviceOnce once;
+  LaunchInfo li;
+  const hipError_t ie = once.get([](int, LaunchInfo&) {
+    const void* fns[4] = {(const void*)gdn_step_tail_kernel<D, false, true>,
+                          (const void*)gdn_step_tail_kernel<D, false, false>,
+                          (const void*)gdn_step_tail_kernel<D, true, true>,
+                          (const void*)gdn_step_tail_kernel<D, true, false>};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 4 && e == hipSuccess && tail_fits(D); ++i)
+      e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)TailShape<D>::lds_bytes);
+    return e;
+  }, &li);
+  if (ie != hipSuccess) return ie;
+  if (!tail_fits(D) || ta.Tc < 1 || ta.Tc > kTailMaxFrames || ta.nsplit < 1) return hipErrorInvalidValue;
+  const long long units = (long long)ta.BH * ta.Tc * ta.nsplit;
+  if (units > (1ll << 30)) return hipErrorInvalidValue;
+  (void)cus;
+  const dim3 grid((unsigned)(8 * ((units + 7) / 8))), block(D / 16 * 64);
+  const size_t lds = tail_fits(D) ? TailShape<D>::lds_bytes : 0;
+  const bool erase = ta.beta_mode == 0;
+  if (ta.fp8) {
+    if (erase) hipLaunchKernelGGL((gdn_step_tail_kernel<D, true, true>), grid, block, lds, stream, ta);
+    else hipLaunchKernelGGL((gdn_step_tail_kernel<D, true, false>), grid, block, lds, stream, ta);
+  } else {
+    if (erase) hipLaunchKernelGGL((gdn_step_tail_kernel<D, false, true>), grid, block, lds, stream, ta);
+    else hipLaunchKernelGGL((gdn_step_tail_kernel<D, false, false>), grid, block, lds, stream, ta);
+  }
   return hipGetLastError();
 }
 
@@ -1211,6 +1542,9 @@ hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream) {
 }
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream) {
   GDN_DISPATCH(launch_state_t, (sa, stream))
+}
+hipError_t launch_step_tail(int D, const TailArgs& ta, int cus, hipStream_t stream) {
+  GDN_DISPATCH(launch_step_tail_t, (ta, cus, stream))
 }
 hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream) {
   GDN_DISPATCH(launch_adjoint_t, (aa, stream))

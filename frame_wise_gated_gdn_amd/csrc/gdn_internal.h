@@ -140,7 +140,31 @@ struct GramArgs {
   int BH, T, S, t0, Tc;
   float kscale, kscale2;    // 1/sqrt(D*S) and 1/(D*S), each rounded once to fp32
   int fp8;                  // 1: K and V are OCP e4m3 bytes
+  // optional (launches of at most 2 frames per CU only): BH extra
+  // workgroups copy each head's [D][D] fp32 state from copy_src to copy_dst
+  const float* copy_src = nullptr;
+  float* copy_dst = nullptr;
 };
+
+// Chain and readout of a short chunk in one launch (see gdn_step_tail_kernel).
+struct TailArgs {
+  const void* q;            // [BH][T][S][D] bf16, or OCP e4m3 when fp8
+  void* o;                  // as q
+  const void* gfr;          // this launch's G_t: [BH][Tc] frames, as in GramArgs
+  const void* bfr;          // this launch's B_t: [BH][Tc] frames
+  const float* gamma;       // [BH][T]
+  const float* beta;        // [BH][T]
+  const float* state_src;   // [BH][D][D] fp32 or nullptr (zero state); must not alias state_dst
+  float* state_dst;         // [BH][D][D] fp32 or nullptr
+  int BH, T, S, t0, Tc;
+  int nsplit;               // workgroups per (head, frame, value tile): shares of the frame's chunks
+  int beta_mode;            // 0 ERASE, 1 WRITE
+  int fp8;
+};
+// Longest launch (frames per head) that takes the chunk tail; each workgroup
+// recomputes the chain of the frames before its own (all kTailMaxFrames of
+// them, those past its own frame on zeros).
+constexpr int kTailMaxFrames = 4;
 
 // State pass (bf16 I/O): the serial frame loop over G and B.
 struct StateArgs {
@@ -227,6 +251,7 @@ hipError_t launch_recurrence(int D, bool bf16, const RecurArgs& ra, hipStream_t 
 hipError_t launch_readout(int D, bool bf16, const ReadoutArgs& ro, hipStream_t stream);
 hipError_t launch_gram(int D, const GramArgs& ga, hipStream_t stream);
 hipError_t launch_state(int D, const StateArgs& sa, hipStream_t stream);
+hipError_t launch_step_tail(int D, const TailArgs& ta, int cus, hipStream_t stream);
 hipError_t launch_adjoint(int D, const AdjointArgs& aa, hipStream_t stream);
 hipError_t launch_dvdk(int D, const DvkArgs& da, hipStream_t stream);
 hipError_t launch_tconv(const TconvArgs& ta, hipStream_t stream);

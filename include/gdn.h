@@ -121,8 +121,13 @@ typedef enum gdn_status {
  * >= 2^28 (e4m3) take the one launch (it needs a cooperative launch, at most
  * 16 XCDs, every XCD's workgroups at least twice its heads' chain
  * workgroups, and the workspace gdn_workspace_size gives), the rest the
- * three.  GDN_FLAG_THREE_PASS forces
- * the three launches; GDN_FLAG_ONE_LAUNCH asks for the one launch whatever
+ * three.  Of the rest, a short call -- at most 4 frames per head, D <= 112,
+ * B*H*T no more than the device's compute units, state_norms NULL, the
+ * whole call in one range of the workspace (a streaming chunk) -- runs the
+ * state pass and the readout as one kernel, each of its workgroups
+ * recomputing the state chain of the frames before its own: two launches,
+ * the same bits.
+ * GDN_FLAG_THREE_PASS forces the three launches; GDN_FLAG_ONE_LAUNCH asks for the one launch whatever
  * the size or dtype (it still falls back where the device or the workspace
  * does not allow it).  The two flags exclude each other.
  */
@@ -131,7 +136,7 @@ typedef enum gdn_status {
 
 /* Kernel kinds booked by gdn_kernel_times. */
 #define GDN_KERNEL_RECURRENCE 0 /* single-pass recurrence */
-#define GDN_KERNEL_READOUT 1    /* O_t = Qf M_t from the per-frame state snapshots */
+#define GDN_KERNEL_READOUT 1    /* O_t = Qf M_t (for a short call: with the state chain) */
 #define GDN_KERNEL_GRAM 2       /* Gram pass: G_t, B_t per (head, frame) */
 #define GDN_KERNEL_STATE 3      /* serial state pass over G_t, B_t */
 #define GDN_KERNEL_BACKWARD 4   /* the backward's own kernels (its forward replay books as GRAM/STATE) */

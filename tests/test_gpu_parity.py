@@ -334,6 +334,42 @@ def test_small_launch_readout_split_is_bitwise(env, dtype, S, D):
               TOL["bf16"], norms=part[2])
 
 
+@pytest.mark.parametrize("dtype,mode", [("bf16", "erase"), ("bf16", "write"), ("fp8", "erase")])
+@pytest.mark.parametrize("B,H,T,S,D", [(1, 16, 4, 880, 64), (1, 1, 4, 880, 64), (1, 20, 4, 880, 112),
+                                        (1, 1, 3, 880, 112), (2, 3, 2, 300, 96), (1, 2, 4, 300, 48),
+                                        (1, 4, 3, 40, 16), (1, 1, 2, 1, 32), (1, 2, 4, 100, 80),
+                                        (2, 3, 1, 77, 128), (1, 1, 8, 300, 64)])
+def test_short_chunk_tail_equals_three_launches(env, dtype, mode, B, H, T, S, D):
+    """A short call without norms (at most 4 frames, D <= 112) runs the state
+    chain and the readout as one launch, every workgroup recomputing the chain
+    of the frames before its own.  It must give bitwise the outputs and states
+    of the three launches: with the state updated in place (the gram pass
+    copies it first), into a new tensor, peeked (no state out) and from the
+    zero state; ragged token counts, one token, one frame and the token-share
+    split included.  D = 128 and 8 frames take the three launches (same
+    check)."""
+    torch, gdn, wl, go = env
+    inp = gen(env, wl.Workload("tail", B, H, T, S, D, dtype=dtype, gamma=(0.5, 1.0), beta=(0.0, 1.0)))
+    args = [inp[n] for n in ("q", "k", "v", "gamma", "beta")]
+    s0 = torch.randn((B, H, D, D), generator=torch.Generator().manual_seed(3)).cuda() * 0.1
+    ref_o, ref_s, _ = gdn.frame_forward(*args, state=s0, beta_mode=mode, path="three_pass")
+    ref_o0, ref_s0, _ = gdn.frame_forward(*args, beta_mode=mode, path="three_pass")
+    inplace = s0.clone()
+    o_in, _, _ = gdn.frame_step(*args, inplace, beta_mode=mode, commit="inplace")
+    o_new, s_new, _ = gdn.frame_step(*args, s0, beta_mode=mode, commit="new")
+    o_peek, none, _ = gdn.frame_step(*args, s0, beta_mode=mode, commit="peek")
+    o_zero, s_zero, _ = gdn.frame_forward(*args, beta_mode=mode)
+    torch.cuda.synchronize()
+    raw = (lambda x: x.view(torch.uint8)) if dtype == "fp8" else (lambda x: x)
+    for o in (o_in, o_new, o_peek):
+        assert torch.equal(raw(o), raw(ref_o))
+    assert torch.equal(inplace, ref_s) and torch.equal(s_new, ref_s) and none is None
+    assert torch.equal(raw(o_zero), raw(ref_o0)) and torch.equal(s_zero, ref_s0)
+    if dtype == "bf16":
+        check(env, inp, o_new, s_new, run_oracle(env, inp, heads=[(0, 0), (B - 1, H - 1)], mode=mode, state=s0),
+              TOL["bf16"])
+
+
 @pytest.mark.parametrize("B,H,T,S,D", [(1, 3, 7, 400, 112), (2, 2, 5, 352, 96), (1, 5, 33, 290, 64),
                                         (1, 2, 9, 1000, 48)])
 def test_streaming_gram_kernel_shapes(env, B, H, T, S, D):
