@@ -120,7 +120,7 @@ constexpr uint32_t gram_ymask(int NB, int b0, int b1) {
 // twice that for launches too small to fill the GPU, where the time of one
 // workgroup is the latency of the whole launch).  Every block is accumulated
 // over the chunks in the same order whatever NW is, so the bits do not change.
-template <int D, bool FP8, int NW, int W>
+template <int D, bool FP8, int NW, int W, int CPI>
 __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem, int bh, int tl) {
   using Sh = GramShape<D>;
   using IO = IoFmt<FP8>;
@@ -205,50 +205,59 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
 #pragma unroll
   for (int r = 0; r < kGramRing; ++r) load_chunk(r, R[r]);
 
+  // CPI chunks are staged per barrier, into buffer set (slot / CPI) % 2
+  static_assert(kGramRing % (2 * CPI) == 0, "the LDS buffer sets alternate within the ring");
   for (int base = 0; base < nit; base += kGramRing) {
 #pragma unroll
-    for (int r = 0; r < kGramRing; ++r) {
-      const int c = base + r;
-      stage(r & 1, R[r]);
-      load_chunk(c + kGramRing, R[r]);
+    for (int r0 = 0; r0 < kGramRing; r0 += CPI) {
+#pragma unroll
+      for (int q = 0; q < CPI; ++q) {
+        stage(((r0 / CPI) & 1) * CPI + q, R[r0 + q]);
+        load_chunk(base + r0 + q + kGramRing, R[r0 + q]);
+      }
       lds_barrier();
-      if (c < nch) {
-        if constexpr (FP8) {
-          const unsigned char* kt = smem + (size_t)(r & 1) * 2 * Sh::tile_bytes;
-          const unsigned char* vt = kt + 32 * Sh::RS8;
-          u32x2 X[NB], Y[NB];
-          static_for<NB>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            if constexpr ((XM >> j) & 1u) X[j] = frag8(kt, j);
-            if constexpr ((YM >> j) & 1u) Y[j] = frag8(vt, j);
-          });
-          static_for<NMB>([&](auto ic) {
-            constexpr int i = decltype(ic)::value, b = B0 + i;
-            if constexpr (b < NBB) {
-              acc[i] = mfma_fp8(X[b % NB], Y[b / NB], acc[i]);
-            } else {
-              constexpr int k = b - NBB;
-              acc[i] = mfma_fp8(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
-            }
-          });
-        } else {
-          const uint16_t* kt = (const uint16_t*)(smem + (size_t)(r & 1) * 2 * Sh::tile_bytes);
-          const uint16_t* vt = kt + 32 * RS;
-          u32x4 X[NB], Y[NB];
-          static_for<NB>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
-            if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
-          });
-          static_for<NMB>([&](auto ic) {
-            constexpr int i = decltype(ic)::value, b = B0 + i;
-            if constexpr (b < NBB) {
-              acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
-            } else {
-              constexpr int k = b - NBB;
-              acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
-            }
-          });
+#pragma unroll
+      for (int q = 0; q < CPI; ++q) {
+        const int r = ((r0 / CPI) & 1) * CPI + q;   // LDS buffer of this chunk
+        const int c = base + r0 + q;
+        if (c < nch) {
+          if constexpr (FP8) {
+            const unsigned char* kt = smem + (size_t)r * 2 * Sh::tile_bytes;
+            const unsigned char* vt = kt + 32 * Sh::RS8;
+            u32x2 X[NB], Y[NB];
+            static_for<NB>([&](auto jc) {
+              constexpr int j = decltype(jc)::value;
+              if constexpr ((XM >> j) & 1u) X[j] = frag8(kt, j);
+              if constexpr ((YM >> j) & 1u) Y[j] = frag8(vt, j);
+            });
+            static_for<NMB>([&](auto ic) {
+              constexpr int i = decltype(ic)::value, b = B0 + i;
+              if constexpr (b < NBB) {
+                acc[i] = mfma_fp8(X[b % NB], Y[b / NB], acc[i]);
+              } else {
+                constexpr int k = b - NBB;
+                acc[i] = mfma_fp8(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+              }
+            });
+          } else {
+            const uint16_t* kt = (const uint16_t*)(smem + (size_t)r * 2 * Sh::tile_bytes);
+            const uint16_t* vt = kt + 32 * RS;
+            u32x4 X[NB], Y[NB];
+            static_for<NB>([&](auto jc) {
+              constexpr int j = decltype(jc)::value;
+              if constexpr ((XM >> j) & 1u) X[j] = frag(kt, j);
+              if constexpr ((YM >> j) & 1u) Y[j] = frag(vt, j);
+            });
+            static_for<NMB>([&](auto ic) {
+              constexpr int i = decltype(ic)::value, b = B0 + i;
+              if constexpr (b < NBB) {
+                acc[i] = mfma_bf16(X[b % NB], Y[b / NB], acc[i]);
+              } else {
+                constexpr int k = b - NBB;
+                acc[i] = mfma_bf16(X[gblk_col(k)], X[gblk_row(k)], acc[i]);
+              }
+            });
+          }
         }
       }
     }
@@ -275,7 +284,7 @@ __device__ __forceinline__ void gram_wave(const GramArgs& a, unsigned char* smem
   });
 }
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, int CPI = 1>
 __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gram_kernel(GramArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int fh = blockIdx.x;   // over BH * Tc
@@ -305,7 +314,7 @@ __global__ __launch_bounds__(NW * 64, NW > GramShape<D>::NW ? 1 : 2) void gdn_gr
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   static_for<NW>([&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    if (w == W) gram_wave<D, FP8, NW, W>(a, smem, bh, tl);
+    if (w == W) gram_wave<D, FP8, NW, W, CPI>(a, smem, bh, tl);
   });
 }
 
@@ -1387,8 +1396,8 @@ static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8, 2 * NW>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramShape<D>::lds_bytes);
+      e = hipFuncSetAttribute((const void*)gdn_gram_kernel<D, FP8, 2 * NW, 2>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * GramShape<D>::lds_bytes));
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)gdn_gram_stream_kernel<D, FP8>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)GramStream<D>::lds_bytes);
@@ -1409,9 +1418,10 @@ static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
   if (nfh <= 2 * cus) {
     // at most two frames per CU (a short streaming chunk): one workgroup per
     // frame with twice the waves, so that the launch takes half as long (four
-    // times the waves measured slower again)
-    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, 2 * NW>), dim3(grid), dim3(2 * NW * 64),
-                       GramShape<D>::lds_bytes, stream, ga);
+    // times the waves measured slower again), and two chunks staged per
+    // barrier (the time of a chunk is one barrier-to-MFMA round trip)
+    hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, 2 * NW, 2>), dim3(grid), dim3(2 * NW * 64),
+                       2 * GramShape<D>::lds_bytes, stream, ga);
   } else if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {
     // persistent: one workgroup per resident slot
     const int grid = (int)std::min<long long>(nfh, slots);
