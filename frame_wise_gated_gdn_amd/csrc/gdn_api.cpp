@@ -299,11 +299,12 @@ gdn_status run_tail(const gdn_desc* d, const Plan& p, const Ptrs& x, float* carr
     ta.state_src = alias ? carrier : x.state_in;
     ta.state_dst = x.state_out;
     ta.BH = (int)p.bh; ta.T = d->T; ta.S = d->S; ta.t0 = 0; ta.Tc = d->T;
-    // shares of a frame's chunks: about two workgroups per CU, at least two
-    // chunks per wave (each share repeats the chain)
+    // shares of a frame's chunks: about one workgroup per CU, at least one
+    // chunk per wave (each share repeats the chain; on the 4-frame short-clip
+    // chunk 4 shares measured best, against 1-3 and 7)
     const long long frames = (long long)p.bh * d->T;
     const int nchunk = (d->S + 31) / 32;
-    ta.nsplit = (int)std::max<long long>(1, std::min<long long>(2 * cus / frames, nchunk / (2 * (long long)p.nb)));
+    ta.nsplit = (int)std::max<long long>(1, std::min<long long>(cus / frames, nchunk / (long long)p.nb));
     ta.beta_mode = d->beta_mode; ta.fp8 = d->io_dtype == GDN_FP8_E4M3;
     e = launch_timed(timed, GDN_KERNEL_READOUT, s, [&] { return gdn::launch_step_tail(d->D, ta, cus, s); });
   }
