@@ -253,13 +253,6 @@ hipError_t side_stream(SideStream** out) {
   return hipSuccess;
 }
 
-// Gram path.  Per range of up to kMaxFramesPerLaunch frames: the gram pass
-// (all frames in parallel) on the caller's stream; then the serial state pass
-// in kStateSplit sub-ranges on the side stream, and the readout of each
-// sub-range on the caller's stream as soon as its states exist.  The state
-// pass is latency-bound and light on resources, so the state of sub-range
-// i+1 runs on the CUs next to the HBM-bound readout of sub-range i.  The state
-// crosses sub-ranges and ranges in fp32, so any split gives the same bits.
 // Compute units of the current device (0 when the query fails).
 int device_cus() {
   static gdn::DeviceOnce once;
@@ -271,9 +264,9 @@ int device_cus() {
 }
 
 // Short chunk (at most kTailMaxFrames frames, D <= 112, fewer frames than
-// CUs, no norms asked for): the gram pass, then the chain and the readout in one
-// launch (gdn_step_tail_kernel), two launches instead of three with the same
-// bits.  When state_in and state_out overlap, the gram pass first copies
+// CUs, no norms asked for): the gram pass, then the chain and the readout in
+// one launch (gdn_step_tail_kernel), two launches instead of three with the
+// same bits.  When state_in and state_out overlap, the gram pass first copies
 // state_in to the workspace carrier, which the chain then reads.
 bool tail_ok(const gdn_desc* d, const Plan& p, const Ptrs& x, size_t F, int cus) {
   return !(d->flags & GDN_FLAG_THREE_PASS) && !x.norms && F >= (size_t)d->T && d->T <= gdn::kTailMaxFrames &&
@@ -312,6 +305,13 @@ gdn_status run_tail(const gdn_desc* d, const Plan& p, const Ptrs& x, float* carr
   return GDN_OK;
 }
 
+// Gram path.  Per range of up to kMaxFramesPerLaunch frames: the gram pass
+// (all frames in parallel) on the caller's stream; then the serial state pass
+// in kStateSplit sub-ranges on the side stream, and the readout of each
+// sub-range on the caller's stream as soon as its states exist.  The state
+// pass is latency-bound and light on resources, so the state of sub-range
+// i+1 runs on the CUs next to the HBM-bound readout of sub-range i.  The state
+// crosses sub-ranges and ranges in fp32, so any split gives the same bits.
 gdn_status run_gram(const gdn_desc* d, const Plan& p, const Ptrs& x, void* workspace, size_t wb,
                     hipStream_t s, bool side_ok = true) {
   const size_t F = frames_per_launch(p, d->T, wb);

@@ -1419,7 +1419,7 @@ static hipError_t launch_gram_io(const GramArgs& ga, hipStream_t stream) {
     // at most two frames per CU (a short streaming chunk): one workgroup per
     // frame with twice the waves, so that the launch takes half as long (four
     // times the waves measured slower again), and two chunks staged per
-    // barrier (the time of a chunk is one barrier-to-MFMA round trip)
+    // barrier (3 % faster than one)
     hipLaunchKernelGGL((gdn_gram_kernel<D, FP8, 2 * NW, 2>), dim3(grid), dim3(2 * NW * 64),
                        2 * GramShape<D>::lds_bytes, stream, ga);
   } else if (gram_stream_fits<D>() && nch >= gram_stream_min_chunks<D>()) {

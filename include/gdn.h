@@ -126,10 +126,10 @@ typedef enum gdn_status {
  * whole call in one range of the workspace (a streaming chunk) -- runs the
  * state pass and the readout as one kernel, each of its workgroups
  * recomputing the state chain of the frames before its own: two launches,
- * the same bits.
- * GDN_FLAG_THREE_PASS forces the three launches; GDN_FLAG_ONE_LAUNCH asks for the one launch whatever
- * the size or dtype (it still falls back where the device or the workspace
- * does not allow it).  The two flags exclude each other.
+ * the same bits.  GDN_FLAG_THREE_PASS forces the three launches;
+ * GDN_FLAG_ONE_LAUNCH asks for the one launch whatever the size or dtype (it
+ * still falls back where the device or the workspace does not allow it).  The
+ * two flags exclude each other.
  */
 #define GDN_FLAG_THREE_PASS 0x4u
 #define GDN_FLAG_ONE_LAUNCH 0x8u
